@@ -1,0 +1,246 @@
+"""CPU oracle for KVpop's per-KV-head fixed-budget sparse KV cache.
+
+TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
+reference that the GPU path is checked against.  Only the test suite, the
+package's smoke check and the benchmark's CPU-baseline leg may import it; the
+product path never does.  It shares no code with the GPU path: it imports
+NumPy and nothing else.
+
+What it computes, and where that is stated:
+
+* The cache of each KV head is bounded: some initial sink tokens, a protected
+  window of the most recent tokens, and a scored top-k of older tokens
+  ("Qwen3-8B-KVpop-4x" model card, intro: "a bounded sink + scored top-k +
+  recent-window cache", 4 sink + 3,772 scored + 256 recent = 4,032 entries;
+  aiweekly French article, second paragraph: each head keeps initial sink
+  tokens, a protected recent window, and a learned top-k over older tokens).
+* Delayed scoring: a token gets its long-range score only when it leaves the
+  protected recent window (model card, "Paper highlights / Delayed scoring";
+  KVpop abstract on the HF papers page: the scorer defers scoring by a fixed
+  number of steps).  The score itself comes from a learned scorer; here it is
+  an input.
+* The eviction policy makes an online keep-or-drop decision under a fixed
+  budget (KVpop abstract: "fixed-budget KV eviction policy", "keep-or-drop
+  decision"); an evicted token is gone for good.
+* Decode attention is ordinary softmax attention of each query head over the
+  rows its KV head keeps (grouped-query attention).
+
+Readings taken where the pages say nothing (each also listed in the design
+notes of the repository):
+
+1. The window holds the W newest positions including the token being
+   decoded, so token t leaves the window when token t + W arrives.
+2. Sinks are positions 0 .. s-1; they are never scored and never in the window.
+3. Order of importance is the key (score, position), compared
+   lexicographically: on an equal score the newer token counts as more
+   important, so the lower score, then the older token, is evicted first.
+4. While fewer than k tokens hold scored slots, a leaving token is admitted
+   without a comparison.
+5. Softmax scale defaults to 1/sqrt(D).
+6. Query head h reads KV head floor(h * Hkv / Hq) (contiguous groups).
+7. A NaN score is a caller error (the oracle raises).
+8. At prefill the scores of positions [s, P - W) are used; the scores of
+   window positions arrive later, one per decode step.
+
+All arithmetic is float64 on exactly decoded bfloat16 values.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact float64 value of bfloat16 bit patterns.
+
+    A bfloat16 is the upper half of an IEEE binary32, so widening the pattern
+    to 32 bits with sixteen zero bits below gives the same number.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """KV head read by query head h (reading 6: contiguous query groups)."""
+    return (h * n_kv_heads) // n_q_heads
+
+
+def _check_score(x: float) -> float:
+    x = float(x)
+    if math.isnan(x):
+        raise ValueError("NaN score: scores must be ordered numbers")
+    return x
+
+
+# ---------------------------------------------------------------------------
+# The kept set by its definition (used to pin the streaming oracle)
+# ---------------------------------------------------------------------------
+
+def kept_by_definition(scores_g, n: int, n_sink: int, n_scored: int, n_recent: int):
+    """Kept set of one KV head after position n, written from its definition.
+
+    Kept(n) = Sink(n) | Win(n) | TopK(Cand(n)) where
+      Sink(n) = {0 .. min(s, n+1) - 1}
+      Win(n)  = {max(s, n - W + 1) .. n}      (reading 1)
+      Cand(n) = {s .. n - W}                   (tokens that left the window)
+      TopK    = the k members of Cand(n) with the largest (score, position).
+    Scores only matter for positions in Cand(n).  Returns a sorted list.
+    """
+    s, k, W = n_sink, n_scored, n_recent
+    if n < 0:
+        return []
+    sink = set(range(0, min(s, n + 1)))
+    win = set(range(max(s, n - W + 1), n + 1))
+    cand = range(s, n - W + 1)
+    ranked = sorted(cand, key=lambda t: (_check_score(scores_g[t]), t), reverse=True)
+    return sorted(sink | win | set(ranked[:k]))
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def softmax_attention(q, K, V, scale: float) -> np.ndarray:
+    """out = sum_j softmax_j(scale * <q, K_j>) V_j, float64, rows in any order."""
+    logits = scale * (K @ q)
+    logits = logits - logits.max()
+    w = np.exp(logits)
+    w = w / w.sum()
+    return w @ V
+
+
+def masked_dense_attention(q, K_all, V_all, kept, scale: float) -> np.ndarray:
+    """Attention of q over all positions 0..n, with -inf outside ``kept``.
+
+    A second, independent route to the same number: the full logit row is
+    formed and every position outside the kept set is masked out.
+    """
+    n1 = K_all.shape[0]
+    mask = np.zeros(n1, dtype=bool)
+    mask[np.asarray(list(kept), dtype=np.int64)] = True
+    logits = np.full(n1, -np.inf)
+    logits[mask] = scale * (K_all[mask] @ q)
+    m = logits[mask].max()
+    w = np.where(mask, np.exp(logits - m), 0.0)
+    return (w / w.sum()) @ V_all
+
+
+# ---------------------------------------------------------------------------
+# Streaming oracle: one (layer, sequence) with all its KV heads
+# ---------------------------------------------------------------------------
+
+class KVpopOracle:
+    """The cache of one (layer, sequence), followed step by step.
+
+    prefill(k, v, scores)          fill from a P-token prompt
+    decode(q, k_new, v_new, sl)    process one new token; returns the
+                                   attention output of every query head
+    kept(g)                        sorted kept positions of KV head g
+    """
+
+    def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 n_sink: int, n_scored: int, n_recent: int,
+                 softmax_scale: float | None = None):
+        if n_q_heads % n_kv_heads:
+            raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+        if n_recent < 1 or n_sink < 0 or n_scored < 0:
+            raise ValueError("bad cache geometry")
+        self.Hq, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
+        self.s, self.k, self.W = n_sink, n_scored, n_recent
+        self.scale = (1.0 / math.sqrt(head_dim)) if not softmax_scale or softmax_scale <= 0 \
+            else float(softmax_scale)
+        self.n = -1                       # newest processed position
+        self._cap = 0
+        self._K = np.zeros((self.Hkv, 0, self.D))
+        self._V = np.zeros((self.Hkv, 0, self.D))
+        # Scored region per KV head: position -> score (reading 3 orders them).
+        self.S = [dict() for _ in range(self.Hkv)]
+
+    # -- storage of every row ever seen (the oracle never forgets a row) -----
+    def _reserve(self, n_rows: int):
+        if n_rows <= self._cap:
+            return
+        cap = max(n_rows, 2 * self._cap, 64)
+        K = np.zeros((self.Hkv, cap, self.D))
+        V = np.zeros((self.Hkv, cap, self.D))
+        K[:, :self._cap] = self._K[:, :self._cap]
+        V[:, :self._cap] = self._V[:, :self._cap]
+        self._K, self._V, self._cap = K, V, cap
+
+    # -- prefill -------------------------------------------------------------
+    def prefill(self, k_bits, v_bits, scores):
+        """Fill an empty cache from a P-token prompt.
+
+        k_bits, v_bits: uint16 [Hkv][P][D]; scores: float32 [Hkv][P] (only
+        positions s .. P-W-1 are read, reading 8).  After the call n = P-1 and
+        each head's scored region is the top-k of Cand(P-1).
+        """
+        if self.n != -1:
+            raise RuntimeError("prefill needs an empty cache")
+        P = int(np.asarray(k_bits).shape[1])
+        if P == 0:
+            return
+        self._reserve(P)
+        self._K[:, :P] = bf16_to_f64(k_bits)
+        self._V[:, :P] = bf16_to_f64(v_bits)
+        self.n = P - 1
+        cand = range(self.s, P - self.W)
+        for g in range(self.Hkv):
+            ranked = sorted(cand, key=lambda t: (_check_score(scores[g][t]), t), reverse=True)
+            self.S[g] = {t: float(scores[g][t]) for t in ranked[:self.k]}
+
+    # -- one decode step -----------------------------------------------------
+    def _admit_leaving(self, g: int, t: int, score: float):
+        """Token t has just left the window with ``score`` (delayed scoring)."""
+        S = self.S[g]
+        if len(S) < self.k:                       # reading 4
+            S[t] = score
+            return
+        if self.k == 0:
+            return
+        m = min(S, key=lambda p: (S[p], p))       # least important member
+        if (score, t) > (S[m], m):                # keep-or-drop decision
+            del S[m]                              # evicted for good
+            S[t] = score
+        # else: t is dropped for good
+
+    def decode(self, q_bits, k_new_bits, v_new_bits, score_leaving):
+        """Process token n = self.n + 1 and return out [Hq][D] (float64).
+
+        q_bits: uint16 [Hq][D]; k_new_bits, v_new_bits: uint16 [Hkv][D];
+        score_leaving: float [Hkv], the score of token n - W for each KV head
+        (ignored when n - W < s).
+        """
+        n = self.n + 1
+        self._reserve(n + 1)
+        self._K[:, n] = bf16_to_f64(k_new_bits)
+        self._V[:, n] = bf16_to_f64(v_new_bits)
+        t = n - self.W
+        if t >= self.s:
+            for g in range(self.Hkv):
+                self._admit_leaving(g, t, _check_score(score_leaving[g]))
+        self.n = n
+        q = bf16_to_f64(q_bits)
+        out = np.zeros((self.Hq, self.D))
+        for g in range(self.Hkv):
+            rows = np.asarray(self.kept(g), dtype=np.int64)
+            Kg, Vg = self._K[g, rows], self._V[g, rows]
+            for h in range(self.Hq):
+                if kv_head_of(h, self.Hq, self.Hkv) == g:
+                    out[h] = softmax_attention(q[h], Kg, Vg, self.scale)
+        return out
+
+    # -- state ---------------------------------------------------------------
+    def kept(self, g: int):
+        """Sorted kept positions of KV head g after position self.n."""
+        n = self.n
+        if n < 0:
+            return []
+        sink = set(range(0, min(self.s, n + 1)))
+        win = set(range(max(self.s, n - self.W + 1), n + 1))
+        return sorted(sink | win | set(self.S[g]))
+
+    def rows(self, g: int):
+        """All rows stored so far for KV head g (float64 K and V, [n+1][D])."""
+        return self._K[g, :self.n + 1], self._V[g, :self.n + 1]

@@ -1,0 +1,369 @@
+// C-ABI host side of the fixed-budget cache: argument validation, the device
+// memory layout, a host mirror of every sequence's position, and kernel
+// launches.  No call throws; every failure maps to a KVPOP_E* code.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kvpop.h"
+#include "kvpop_internal.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  size_t kc, vc, keys, pos, ring, ctl, sel, part_acc, part_ml, part_min, tickets, total;
+  int32_t nsplit, rows_per_split;
+};
+
+bool mul_ok(size_t a, size_t b, size_t* r) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+bool config_valid(const kvpop_config* c) {
+  if (c == nullptr) return false;
+  if (c->n_layers < 1 || c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1) return false;
+  if (c->n_q_heads % c->n_kv_heads != 0) return false;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->n_sink < 0 || c->n_scored < 0 || c->n_recent < 1) return false;
+  const int64_t budget = int64_t(c->n_sink) + c->n_scored + c->n_recent;
+  if (budget > (1 << 20)) return false;
+  if (c->max_positions < 1 || c->max_positions > (1 << 30)) return false;
+  if (c->decode_splits < 0 || c->decode_splits > kvpop::decode_max_splits()) return false;
+  if (std::isnan(c->softmax_scale) || std::isinf(c->softmax_scale)) return false;
+  return true;
+}
+
+// Split count for decode: about four workgroups per compute unit in total,
+// at least 4 passes of rows per split.
+void choose_splits(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split) {
+  const int64_t budget = int64_t(c.n_sink) + c.n_scored + c.n_recent;
+  const int64_t rpp = kvpop::decode_rows_per_pass(c.head_dim);
+  const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
+  int64_t ns = c.decode_splits;
+  if (ns == 0) {
+    const int64_t target = 1024;
+    ns = (target + heads - 1) / heads;
+    const int64_t cap = std::max<int64_t>(1, (budget + 4 * rpp - 1) / (4 * rpp));
+    ns = std::min<int64_t>(std::max<int64_t>(ns, 1), cap);
+    ns = std::min<int64_t>(ns, kvpop::decode_max_splits());
+  }
+  int64_t rows = (budget + ns - 1) / ns;
+  rows = (rows + rpp - 1) / rpp * rpp;
+  *nsplit = int32_t(ns);
+  *rows_per_split = int32_t(rows);
+}
+
+bool compute_layout(const kvpop_config& c, Layout* L) {
+  const size_t budget = size_t(c.n_sink) + c.n_scored + c.n_recent;
+  const size_t heads_all = size_t(c.n_layers) * c.batch * c.n_kv_heads;
+  const size_t heads = size_t(c.batch) * c.n_kv_heads;
+  const size_t G = size_t(c.n_q_heads / c.n_kv_heads);
+  choose_splits(c, &L->nsplit, &L->rows_per_split);
+  size_t rows, kvb, tmp;
+  if (!mul_ok(heads_all, budget, &rows)) return false;
+  if (!mul_ok(rows, size_t(c.head_dim) * 2, &kvb)) return false;
+  size_t off = 0;
+  auto take = [&](size_t bytes, size_t* at) -> bool {
+    *at = off;
+    const size_t a = align_up(bytes);
+    if (a < bytes || off > SIZE_MAX - a) return false;
+    off += a;
+    return true;
+  };
+  bool ok = take(kvb, &L->kc) && take(kvb, &L->vc);
+  ok = ok && mul_ok(rows, 8, &tmp) && take(tmp, &L->keys);
+  ok = ok && mul_ok(rows, 4, &tmp) && take(tmp, &L->pos);
+  ok = ok && mul_ok(heads_all, size_t(c.n_recent) * 4, &tmp) && take(tmp, &L->ring);
+  ok = ok && mul_ok(heads_all, sizeof(kvpop::HeadCtl), &tmp) && take(tmp, &L->ctl);
+  ok = ok && take(size_t(c.n_kv_heads) * size_t(std::max(c.n_scored, 1)) * 4, &L->sel);
+  const size_t parts = heads * size_t(L->nsplit);
+  ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
+  ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
+  ok = ok && mul_ok(parts, sizeof(kvpop::MinPart), &tmp) && take(tmp, &L->part_min);
+  ok = ok && take(heads * 4, &L->tickets);
+  L->total = off;
+  return ok;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct kvpop_cache {
+  kvpop_config cfg;
+  Layout lay;
+  int device = -1;
+  bool owns = false;
+  bool poisoned = false;
+  char* base = nullptr;
+  float scale_log2e = 0.f;
+  std::vector<int32_t> n_host;  // [L][B], newest processed position
+
+  kvpop::Geometry geo() const {
+    kvpop::Geometry g;
+    g.batch = cfg.batch;
+    g.n_q_heads = cfg.n_q_heads;
+    g.n_kv_heads = cfg.n_kv_heads;
+    g.head_dim = cfg.head_dim;
+    g.n_sink = cfg.n_sink;
+    g.n_scored = cfg.n_scored;
+    g.n_recent = cfg.n_recent;
+    g.budget = cfg.n_sink + cfg.n_scored + cfg.n_recent;
+    return g;
+  }
+  kvpop::LayerView layer(int32_t l) const {
+    const size_t heads = size_t(cfg.batch) * cfg.n_kv_heads;
+    const size_t budget = size_t(cfg.n_sink) + cfg.n_scored + cfg.n_recent;
+    const size_t h0 = size_t(l) * heads;
+    kvpop::LayerView v;
+    v.kc = reinterpret_cast<uint16_t*>(base + lay.kc) + h0 * budget * cfg.head_dim;
+    v.vc = reinterpret_cast<uint16_t*>(base + lay.vc) + h0 * budget * cfg.head_dim;
+    v.keys = reinterpret_cast<uint64_t*>(base + lay.keys) + h0 * budget;
+    v.pos = reinterpret_cast<int32_t*>(base + lay.pos) + h0 * budget;
+    v.ring = reinterpret_cast<int32_t*>(base + lay.ring) + h0 * cfg.n_recent;
+    v.ctl = reinterpret_cast<kvpop::HeadCtl*>(base + lay.ctl) + h0;
+    return v;
+  }
+  kvpop::DecodeWork work() const {
+    kvpop::DecodeWork w;
+    w.part_acc = reinterpret_cast<float*>(base + lay.part_acc);
+    w.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
+    w.part_min = reinterpret_cast<kvpop::MinPart*>(base + lay.part_min);
+    w.tickets = reinterpret_cast<uint32_t*>(base + lay.tickets);
+    w.nsplit = lay.nsplit;
+    w.rows_per_split = lay.rows_per_split;
+    return w;
+  }
+};
+
+extern "C" {
+
+size_t kvpop_cache_required_bytes(const kvpop_config* cfg) {
+  if (!config_valid(cfg)) return 0;
+  Layout L;
+  if (!compute_layout(*cfg, &L)) return 0;
+  return L.total;
+}
+
+int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena_bytes,
+                       kvpop_cache** out) {
+  if (out == nullptr) return KVPOP_EINVAL;
+  *out = nullptr;
+  if (!config_valid(cfg)) return KVPOP_EINVAL;
+  Layout L;
+  if (!compute_layout(*cfg, &L)) return KVPOP_EINVAL;
+  if (device_arena != nullptr) {
+    if (reinterpret_cast<uintptr_t>(device_arena) % ALIGN != 0) return KVPOP_EINVAL;
+    if (arena_bytes < L.total) return KVPOP_ENOMEM;
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return KVPOP_EHIP;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVPOP_EHIP;
+
+  kvpop_cache* c = new (std::nothrow) kvpop_cache();
+  if (c == nullptr) return KVPOP_ENOMEM;
+  try {
+    c->n_host.assign(size_t(cfg->n_layers) * cfg->batch, -1);
+  } catch (...) {
+    delete c;
+    return KVPOP_ENOMEM;
+  }
+  c->cfg = *cfg;
+  c->lay = L;
+  c->device = dev;
+  const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale
+                                                : 1.0f / std::sqrt(float(cfg->head_dim));
+  c->scale_log2e = scale * 1.4426950408889634f;
+  if (device_arena != nullptr) {
+    c->base = static_cast<char*>(device_arena);
+    c->owns = false;
+  } else {
+    void* p = nullptr;
+    if (hipMalloc(&p, L.total) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      delete c;
+      return KVPOP_ENOMEM;
+    }
+    c->base = static_cast<char*>(p);
+    c->owns = true;
+  }
+  const size_t heads_all = size_t(cfg->n_layers) * cfg->batch * cfg->n_kv_heads;
+  const size_t heads = size_t(cfg->batch) * cfg->n_kv_heads;
+  hipError_t e = kvpop::launch_init_ctl(reinterpret_cast<kvpop::HeadCtl*>(c->base + L.ctl),
+                                        int64_t(heads_all),
+                                        reinterpret_cast<uint32_t*>(c->base + L.tickets),
+                                        int64_t(heads), nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    if (c->owns) (void)hipFree(c->base);
+    delete c;
+    return KVPOP_EHIP;
+  }
+  *out = c;
+  return KVPOP_OK;
+}
+
+void kvpop_cache_destroy(kvpop_cache* cache) {
+  if (cache == nullptr) return;
+  if (cache->owns && cache->base != nullptr) {
+    DeviceGuard dg(cache->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(cache->base);
+  }
+  delete cache;
+}
+
+int kvpop_cache_reset(kvpop_cache* cache, int32_t layer, int32_t seq, void* stream) {
+  if (cache == nullptr) return KVPOP_EINVAL;
+  if (layer < 0 || layer >= cache->cfg.n_layers || seq < 0 || seq >= cache->cfg.batch)
+    return KVPOP_EINVAL;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  kvpop::LayerView lv = cache->layer(layer);
+  hipError_t e = kvpop::launch_init_ctl(lv.ctl + size_t(seq) * cache->cfg.n_kv_heads,
+                                        cache->cfg.n_kv_heads, nullptr, 0,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  cache->n_host[size_t(layer) * cache->cfg.batch + seq] = -1;
+  return KVPOP_OK;
+}
+
+int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_t n_tokens,
+                          const uint16_t* k, const uint16_t* v, const float* scores,
+                          void* stream) {
+  if (cache == nullptr) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (layer < 0 || layer >= c.n_layers || seq < 0 || seq >= c.batch || n_tokens < 0)
+    return KVPOP_EINVAL;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  int32_t& nh = cache->n_host[size_t(layer) * c.batch + seq];
+  if (nh != -1) return KVPOP_ESTATE;
+  if (n_tokens > c.max_positions) return KVPOP_ESTATE;
+  if (n_tokens == 0) return KVPOP_OK;
+  if (k == nullptr || v == nullptr || scores == nullptr) return KVPOP_EINVAL;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  hipError_t e = kvpop::launch_prefill(cache->geo(), cache->layer(layer), seq, n_tokens, k, v,
+                                       scores, reinterpret_cast<int32_t*>(cache->base + cache->lay.sel),
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  nh = n_tokens - 1;
+  return KVPOP_OK;
+}
+
+int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, const float* score_leaving, uint16_t* out,
+                      void* stream) {
+  if (cache == nullptr) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (layer < 0 || layer >= c.n_layers) return KVPOP_EINVAL;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || score_leaving == nullptr ||
+      out == nullptr)
+    return KVPOP_EINVAL;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  int32_t* nh = cache->n_host.data() + size_t(layer) * c.batch;
+  for (int32_t b = 0; b < c.batch; ++b)
+    if (int64_t(nh[b]) + 1 >= c.max_positions) return KVPOP_ESTATE;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  hipError_t e = kvpop::launch_decode(cache->geo(), cache->layer(layer), cache->work(), q, k_new,
+                                      v_new, score_leaving, out, cache->scale_log2e,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  for (int32_t b = 0; b < c.batch; ++b) nh[b] += 1;
+  return KVPOP_OK;
+}
+
+int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, kvpop_state* st,
+                      int32_t* counts, int32_t* kept_pos, void* stream) {
+  if (cache == nullptr || st == nullptr) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (layer < 0 || layer >= c.n_layers || seq < 0 || seq >= c.batch) return KVPOP_EINVAL;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  const int32_t Hkv = c.n_kv_heads;
+  const size_t budget = size_t(c.n_sink) + c.n_scored + c.n_recent;
+  std::vector<kvpop::HeadCtl> ctl;
+  std::vector<int32_t> pos;
+  try {
+    ctl.resize(Hkv);
+    pos.resize(size_t(Hkv) * budget);
+  } catch (...) {
+    return KVPOP_ENOMEM;
+  }
+  kvpop::LayerView lv = cache->layer(layer);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(ctl.data(), lv.ctl + size_t(seq) * Hkv,
+                                sizeof(kvpop::HeadCtl) * Hkv, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(pos.data(), lv.pos + size_t(seq) * Hkv * budget,
+                       sizeof(int32_t) * pos.size(), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  st->n = ctl[0].n;
+  st->flags = 0;
+  for (int32_t g = 0; g < Hkv; ++g) {
+    st->flags |= ctl[g].flags;
+    const int32_t cnt = std::max(0, std::min<int32_t>(ctl[g].count, int32_t(budget)));
+    if (counts != nullptr) counts[g] = cnt;
+    if (kept_pos != nullptr) {
+      int32_t* dst = kept_pos + size_t(g) * budget;
+      std::copy(pos.begin() + size_t(g) * budget, pos.begin() + size_t(g) * budget + cnt, dst);
+      std::sort(dst, dst + cnt);
+      std::fill(dst + cnt, dst + budget, -1);
+    }
+  }
+  return KVPOP_OK;
+}
+
+const char* kvpop_strerror(int code) {
+  switch (code) {
+    case KVPOP_OK: return "success";
+    case KVPOP_EINVAL: return "invalid argument";
+    case KVPOP_ENOMEM: return "out of device memory or arena too small";
+    case KVPOP_EHIP: return "HIP runtime error";
+    case KVPOP_ESTATE: return "call out of order, cache poisoned, or position limit reached";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

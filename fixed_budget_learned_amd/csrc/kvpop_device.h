@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels: score keys, bf16 packing,
+// wavefront (64-lane) and workgroup reductions/scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvpop_internal.h"
+
+namespace kvpop {
+
+constexpr int WAVE = 64;
+
+// Order-preserving code of a float32 score: flipping all bits of negatives
+// and setting the sign bit of non-negatives makes unsigned order equal float
+// order.  -0 is folded onto +0 first so the two compare equal.
+__device__ __forceinline__ uint32_t score_code(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bool score_is_nan(float s) {
+  return (__float_as_uint(s) & 0x7FFFFFFFu) > 0x7F800000u;
+}
+
+__device__ __forceinline__ uint64_t make_key(uint32_t code, int32_t pos) {
+  return (static_cast<uint64_t>(code) << 32) | static_cast<uint32_t>(pos);
+}
+
+// bf16 pair packed in a 32-bit word -> two floats (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---- wavefront reductions --------------------------------------------------
+
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t x) {
+  const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    uint32_t y = __shfl_up(x, d, WAVE);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Lexicographic minimum of (key, slot) over the wavefront.
+__device__ __forceinline__ void wave_min_key(uint64_t& key, int32_t& slot) {
+#pragma unroll
+  for (int d = WAVE / 2; d >= 1; d >>= 1) {
+    uint64_t k2 = __shfl_xor(key, d, WAVE);
+    int32_t s2 = __shfl_xor(slot, d, WAVE);
+    if (k2 < key || (k2 == key && s2 < slot)) {
+      key = k2;
+      slot = s2;
+    }
+  }
+}
+
+// Exclusive scan of one u32 per thread over a workgroup of NT threads.
+// `scratch` must hold NT/64 + 1 words of LDS.  Returns the exclusive prefix;
+// *total receives the sum over the workgroup.  Must be called by all threads.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan_u32(uint32_t x, uint32_t* scratch,
+                                                             uint32_t* total) {
+  constexpr int NW = NT / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wid = threadIdx.x / WAVE;
+  uint32_t inc = wave_inclusive_scan_u32(x);
+  if (lane == WAVE - 1) scratch[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t w = lane < NW ? scratch[lane] : 0u;
+    uint32_t wi = wave_inclusive_scan_u32(w);
+    if (lane < NW) scratch[lane] = wi - w;  // exclusive over waves
+    if (lane == NW - 1) scratch[NW] = wi;
+  }
+  __syncthreads();
+  uint32_t ex = scratch[wid] + inc - x;
+  *total = scratch[NW];
+  __syncthreads();  // scratch may be reused right after
+  return ex;
+}
+
+}  // namespace kvpop

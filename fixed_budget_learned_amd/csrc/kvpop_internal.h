@@ -1,0 +1,80 @@
+// Internal layout and launcher declarations shared by the C-ABI host code
+// (kvpop_abi.cpp) and the HIP kernels (kvpop_prefill.hip, kvpop_decode.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kvpop {
+
+// Importance key of a scored token: (score, position) compared
+// lexicographically, packed so that unsigned integer order equals key order.
+// The high word is the float32 score mapped to an order-preserving unsigned
+// code (-0 folded onto +0); the low word is the position.  KEY_NONE is larger
+// than every real key (positions stay below 2^31) and marks slots that are
+// not scored (sinks, window) so a minimum over a slot range skips them.
+constexpr uint64_t KEY_NONE = ~0ull;
+
+// Per (layer, sequence, KV head) control block, 32 bytes.
+struct HeadCtl {
+  int32_t n;        // newest processed position, -1 when empty
+  int32_t count;    // occupied slots are [0, count)
+  int32_t nscored;  // slots holding scored tokens
+  int32_t minslot;  // slot of the least important scored token (-1: none)
+  uint64_t minkey;  // its key, KEY_NONE when nscored == 0
+  int32_t flags;    // KVPOP_FLAG_* bits
+  int32_t pad;
+};
+static_assert(sizeof(HeadCtl) == 32, "HeadCtl layout");
+
+// Partial minimum of one split of a head's slot range.
+struct MinPart {
+  uint64_t key;
+  int32_t slot;
+  int32_t pad;
+};
+static_assert(sizeof(MinPart) == 16, "MinPart layout");
+
+// Device views of one layer of the cache.  Head index = seq * Hkv + g.
+struct LayerView {
+  uint16_t* kc;     // [B][Hkv][budget][D] bf16
+  uint16_t* vc;     // [B][Hkv][budget][D] bf16
+  uint64_t* keys;   // [B][Hkv][budget]
+  int32_t* pos;     // [B][Hkv][budget]
+  int32_t* ring;    // [B][Hkv][W]  slot of window position p at p % W
+  HeadCtl* ctl;     // [B][Hkv]
+};
+
+struct Geometry {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_sink, n_scored, n_recent, budget;
+};
+
+// Decode workspace, shared by every layer (calls are stream-ordered).
+struct DecodeWork {
+  float* part_acc;     // [B*Hkv][nsplit][G][D]
+  float* part_ml;      // [B*Hkv][nsplit][G][2]  (running max in log2 units, sum)
+  MinPart* part_min;   // [B*Hkv][nsplit]
+  uint32_t* tickets;   // [B*Hkv], zero between calls
+  int32_t nsplit;
+  int32_t rows_per_split;
+};
+
+// Launchers: return hipSuccess or the launch error.  All work is enqueued
+// on `stream`; nothing is synchronised.
+hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int64_t n_tickets,
+                           hipStream_t stream);
+hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
+                          const uint16_t* k, const uint16_t* v, const float* scores,
+                          int32_t* sel, hipStream_t stream);
+// Rows one decode pass covers (a multiple of which every split spans), and
+// the largest split count the decode kernel accepts.
+int decode_rows_per_pass(int head_dim);
+int decode_max_splits();
+
+hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeWork& work,
+                         const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         const float* score_leaving, uint16_t* out, float scale_log2e,
+                         hipStream_t stream);
+
+}  // namespace kvpop

@@ -1,0 +1,259 @@
+// Prefill compaction for gfx950: fill an empty (layer, sequence) of the
+// fixed-budget cache from a P-token prompt.
+//
+// The kept set after position P-1 is the sinks {0..s-1}, the window
+// {max(s, P-W)..P-1} and the k candidates of {s..P-W-1} with the largest
+// (score, position) keys ("Qwen3-8B-KVpop-4x" model card, intro: sink +
+// scored top-k + recent window; the window's scores arrive later, when each
+// token leaves it, per the card's "Delayed scoring").
+//
+// Two kernels per call:
+//   select  one 1024-thread workgroup per KV head.  A 4 x 8-bit radix select
+//           over the order-preserving score codes finds the threshold code
+//           and how many tokens carrying it survive; a tiled ordered scan
+//           then keeps every code above the threshold and the newest of the
+//           tied ones, and writes the kept positions in ascending order plus
+//           the head's control block (count, min key and its slot).
+//   gather  many 256-thread workgroups per head copy the kept K/V rows into
+//           slots [0, count) with 16-byte coalesced loads/stores and write
+//           per-slot position and key, and the window ring.
+// Slot layout after prefill: sinks, then selected candidates in ascending
+// position, then the window in ascending position.
+#include <hip/hip_runtime.h>
+
+#include "kvpop_device.h"
+#include "kvpop_internal.h"
+
+namespace kvpop {
+namespace {
+
+constexpr int SEL_THREADS = 1024;
+constexpr int GATHER_THREADS = 256;
+
+struct PrefillShape {
+  int32_t P;       // prompt length
+  int32_t s_eff;   // sinks present: min(s, P)
+  int32_t c0, c1;  // candidate positions [c0, c1)
+  int32_t kk;      // scored slots filled: min(k, c1 - c0)
+  int32_t w0;      // first window position
+  int32_t count;   // s_eff + kk + (P - w0)
+};
+
+__host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int32_t k, int32_t W) {
+  PrefillShape r;
+  r.P = P;
+  r.s_eff = P < s ? P : s;
+  r.c0 = s;
+  r.c1 = P - W;
+  if (r.c1 < r.c0) r.c1 = r.c0;
+  int32_t C = r.c1 - r.c0;
+  r.kk = k < C ? k : C;
+  r.w0 = (P - W) > s ? (P - W) : s;
+  if (r.w0 > P) r.w0 = P;
+  r.count = r.s_eff + r.kk + (P - r.w0);
+  return r;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
+    const float* __restrict__ scores, PrefillShape sh, int32_t k, int32_t* __restrict__ sel,
+    HeadCtl* __restrict__ ctl) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scan_buf[SEL_THREADS / WAVE + 1];
+  __shared__ uint32_t s_bin, s_above, s_nan;
+  __shared__ int32_t s_minslot;
+  __shared__ uint64_t s_minkey;
+
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* sc = scores + static_cast<int64_t>(g) * sh.P;
+  int32_t* out = sel + static_cast<int64_t>(g) * (k > 0 ? k : 1);
+
+  if (tid == 0) {
+    s_nan = 0;
+    s_minslot = -1;
+    s_minkey = KEY_NONE;
+  }
+  __syncthreads();
+
+  uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
+  uint32_t n_eq = 0;
+  if (sh.kk > 0) {
+    // ---- radix select of the kk-th largest code ---------------------------
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      bool saw_nan = false;
+      for (int32_t i = sh.c0 + tid; i < sh.c1; i += SEL_THREADS) {
+        float x = sc[i];
+        saw_nan |= score_is_nan(x);
+        uint32_t o = score_code(x);
+        if ((o & mask) == prefix) atomicAdd(&hist[(o >> shift) & 255u], 1u);
+      }
+      if (shift == 24 && saw_nan) s_nan = 1;
+      __syncthreads();
+      // Bins from the top: thread t holds bin 255 - t.
+      uint32_t h = tid < 256 ? hist[255 - tid] : 0u;
+      uint32_t tot;
+      uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>(h, scan_buf, &tot);
+      if (tid < 256 && ex < krem && krem <= ex + h) {
+        s_bin = 255u - tid;
+        s_above = ex;
+      }
+      __syncthreads();
+      const uint32_t bin = s_bin;
+      krem -= s_above;
+      prefix |= bin << shift;
+      mask |= 0xFFu << shift;
+      if (shift == 0) n_eq = hist[bin];
+      __syncthreads();
+    }
+    // ---- ordered compaction: codes > prefix, then the newest krem ties ----
+    const uint32_t thr = prefix;
+    const uint32_t drop = n_eq - krem;  // oldest ties that lose
+    uint32_t run_gt = 0, run_eq = 0;
+    for (int32_t base = sh.c0; base < sh.c1; base += SEL_THREADS) {
+      const int32_t i = base + tid;
+      uint32_t gt = 0, eq = 0;
+      if (i < sh.c1) {
+        uint32_t o = score_code(sc[i]);
+        gt = o > thr;
+        eq = o == thr;
+      }
+      uint32_t tot;
+      uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
+      const uint32_t eq_before = run_eq + (ex >> 16);
+      const uint32_t gt_before = run_gt + (ex & 0xFFFFu);
+      if (gt || (eq && eq_before >= drop)) {
+        const uint32_t kept_ties_before = eq_before > drop ? eq_before - drop : 0u;
+        const uint32_t idx = gt_before + kept_ties_before;
+        out[idx] = i;
+        if (eq && eq_before == drop) {  // the least important kept token
+          s_minslot = sh.s_eff + static_cast<int32_t>(idx);
+          s_minkey = make_key(thr, i);
+        }
+      }
+      run_eq += tot >> 16;
+      run_gt += tot & 0xFFFFu;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    HeadCtl c;
+    c.n = sh.P - 1;
+    c.count = sh.count;
+    c.nscored = sh.kk;
+    c.minslot = s_minslot;
+    c.minkey = s_minkey;
+    c.flags = s_nan ? 1 : 0;
+    c.pad = 0;
+    ctl[g] = c;
+  }
+}
+
+// Rows per gather workgroup: 256 threads move 16 bytes each per pass.
+template <int D>
+__global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ scores, PrefillShape sh, int32_t kcap, int32_t budget, int32_t W,
+    int32_t rows_per_block, const int32_t* __restrict__ sel, uint16_t* __restrict__ kc,
+    uint16_t* __restrict__ vc, uint64_t* __restrict__ keys, int32_t* __restrict__ pos,
+    int32_t* __restrict__ ring) {
+  constexpr int LPR = D / 8;                   // lanes per row (16 B each)
+  constexpr int RPP = GATHER_THREADS / LPR;    // rows per pass
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int rg = tid / LPR;
+  const int c = tid % LPR;
+  const int32_t r0 = blockIdx.x * rows_per_block;
+  const int32_t r1 = min(r0 + rows_per_block, sh.count);
+
+  const uint4* ksrc = reinterpret_cast<const uint4*>(k + static_cast<int64_t>(g) * sh.P * D);
+  const uint4* vsrc = reinterpret_cast<const uint4*>(v + static_cast<int64_t>(g) * sh.P * D);
+  uint4* kdst = reinterpret_cast<uint4*>(kc + static_cast<int64_t>(g) * budget * D);
+  uint4* vdst = reinterpret_cast<uint4*>(vc + static_cast<int64_t>(g) * budget * D);
+  const int32_t* selg = sel + static_cast<int64_t>(g) * kcap;
+  const float* scg = scores + static_cast<int64_t>(g) * sh.P;
+
+  for (int32_t r = r0 + rg; r < r1; r += RPP) {
+    int32_t p;
+    bool scored = false;
+    if (r < sh.s_eff) {
+      p = r;
+    } else if (r < sh.s_eff + sh.kk) {
+      p = selg[r - sh.s_eff];
+      scored = true;
+    } else {
+      p = sh.w0 + (r - sh.s_eff - sh.kk);
+    }
+    kdst[static_cast<int64_t>(r) * LPR + c] = ksrc[static_cast<int64_t>(p) * LPR + c];
+    vdst[static_cast<int64_t>(r) * LPR + c] = vsrc[static_cast<int64_t>(p) * LPR + c];
+    if (c == 0) {
+      const int64_t hs = static_cast<int64_t>(g) * budget + r;
+      pos[hs] = p;
+      keys[hs] = scored ? make_key(score_code(scg[p]), p) : KEY_NONE;
+      if (!scored && r >= sh.s_eff) ring[static_cast<int64_t>(g) * W + (p % W)] = r;
+    }
+  }
+}
+
+__global__ void init_ctl_kernel(HeadCtl* __restrict__ ctl, int64_t n_heads,
+                                uint32_t* __restrict__ tickets, int64_t n_tickets) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n_heads) {
+    HeadCtl c;
+    c.n = -1;
+    c.count = 0;
+    c.nscored = 0;
+    c.minslot = -1;
+    c.minkey = KEY_NONE;
+    c.flags = 0;
+    c.pad = 0;
+    ctl[i] = c;
+  }
+  if (tickets != nullptr && i < n_tickets) tickets[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int64_t n_tickets,
+                           hipStream_t stream) {
+  const int64_t n = n_heads > n_tickets ? n_heads : n_tickets;
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(init_ctl_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(threads), 0,
+                     stream, ctl, n_heads, tickets, n_tickets);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
+                          const uint16_t* k, const uint16_t* v, const float* scores,
+                          int32_t* sel, hipStream_t stream) {
+  const PrefillShape sh = prefill_shape(n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
+  const int64_t head0 = static_cast<int64_t>(seq) * geo.n_kv_heads;
+  const int32_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
+  hipLaunchKernelGGL(prefill_select_kernel, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0, stream,
+                     scores, sh, geo.n_scored, sel, lv.ctl + head0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (sh.count == 0) return hipSuccess;
+  const int32_t rows_per_block = 64;
+  const uint32_t nblk = static_cast<uint32_t>((sh.count + rows_per_block - 1) / rows_per_block);
+  const int64_t row0 = head0 * geo.budget;
+  const int64_t el0 = row0 * geo.head_dim;
+  const dim3 grid(nblk, geo.n_kv_heads);
+  if (geo.head_dim == 128) {
+    hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, dim3(GATHER_THREADS), 0, stream, k, v,
+                       scores, sh, kcap, geo.budget, geo.n_recent, rows_per_block, sel,
+                       lv.kc + el0, lv.vc + el0, lv.keys + row0, lv.pos + row0,
+                       lv.ring + head0 * geo.n_recent);
+  } else {
+    hipLaunchKernelGGL(prefill_gather_kernel<64>, grid, dim3(GATHER_THREADS), 0, stream, k, v,
+                       scores, sh, kcap, geo.budget, geo.n_recent, rows_per_block, sel,
+                       lv.kc + el0, lv.vc + el0, lv.keys + row0, lv.pos + row0,
+                       lv.ring + head0 * geo.n_recent);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvpop

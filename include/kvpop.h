@@ -1,0 +1,169 @@
+/*
+ * kvpop.h - C ABI of a per-KV-head fixed-budget sparse KV cache (KVpop) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the cache holds.  Every (layer, sequence, KV head) keeps at most
+ * budget = n_sink + n_scored + n_recent rows of K and V: the first n_sink
+ * positions (sinks), the n_recent newest positions (the protected recent
+ * window, which includes the token just decoded), and n_scored older tokens
+ * chosen by score ("Qwen3-8B-KVpop-4x" model card, intro: a bounded sink +
+ * scored top-k + recent-window cache of 4 + 3,772 + 256 = 4,032 entries per
+ * head; aiweekly French article, second paragraph: per-head sinks, protected
+ * recent window, learned top-k of older tokens).
+ *
+ * Delayed scoring.  A token's long-range score is supplied only when the
+ * token leaves the window, n_recent steps after it was decoded (model card,
+ * "Delayed scoring"; KVpop abstract: scoring deferred by a fixed number of
+ * steps).  The score is an input: the learned scorer is not part of this
+ * library.  The leaving token then either takes a scored slot or is dropped
+ * for good (KVpop abstract: a fixed-budget keep-or-drop eviction policy).
+ *
+ * Order of importance: key = (score, position) compared lexicographically,
+ * so on an equal score the newer token is kept; the lower score, then the
+ * older token, is evicted first.  The pages fix no tie order; this is the
+ * library's reading.  While fewer than n_scored tokens hold scored slots, a
+ * leaving token is admitted without comparison.  Scores are float32; -0 and
+ * +0 are equal, infinities order normally, NaN is a caller error (recorded
+ * in kvpop_state.flags; the kept set is then unspecified).
+ *
+ * Because scores never change once assigned and evicted tokens never
+ * return, after position n the kept set of a head equals
+ *   {0..min(s,n+1)-1}  U  {max(s,n-W+1)..n}  U  top-n_scored of {s..n-W} by key.
+ *
+ * Decode attention: query head h attends to KV head floor(h*Hkv/Hq) over the
+ * kept rows with softmax(scale * q.k) v, bf16 inputs, fp32 accumulation,
+ * bf16 output (round to nearest even).
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Device pointers are borrowed for the stream-ordered duration of the
+ *     call; the caller keeps them alive until the stream has passed it.  No
+ *     pointer is retained after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   - Return value: KVPOP_OK (0) or a negative KVPOP_E* code.  Arguments are
+ *     validated before anything is enqueued, so a call that fails validation
+ *     changes nothing.  A HIP error after enqueueing poisons the cache: every
+ *     later call returns KVPOP_ESTATE.
+ *   - A cache object is not thread-safe; drive it from one host thread and
+ *     one stream (calls on one cache share a device workspace).
+ */
+#ifndef KVPOP_H_
+#define KVPOP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define KVPOP_API __attribute__((visibility("default")))
+#else
+#define KVPOP_API
+#endif
+
+#define KVPOP_OK 0
+#define KVPOP_EINVAL (-1) /* bad argument, shape or NULL pointer           */
+#define KVPOP_ENOMEM (-2) /* device allocation failed or arena too small    */
+#define KVPOP_EHIP (-3)   /* HIP runtime or launch error (cache poisoned)   */
+#define KVPOP_ESTATE (-4) /* call out of order, cache poisoned, or position
+                             limit reached                                   */
+
+/* kvpop_state.flags bits */
+#define KVPOP_FLAG_NAN_SCORE 1 /* a NaN score reached the cache */
+
+typedef struct kvpop_cache kvpop_cache;
+
+typedef struct kvpop_config {
+  int32_t n_layers;      /* >= 1 */
+  int32_t batch;         /* sequences per layer, >= 1 */
+  int32_t n_q_heads;     /* Hq, a multiple of n_kv_heads; Hq/Hkv in {1,2,4,8} */
+  int32_t n_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t n_sink;        /* s >= 0 */
+  int32_t n_scored;      /* k >= 0 */
+  int32_t n_recent;      /* W >= 1 */
+  int32_t max_positions; /* positions 0 .. max_positions-1 per sequence;
+                            1 .. 2^30 */
+  int32_t decode_splits; /* slot ranges per head in decode attention;
+                            0 = chosen by the library, else 1 .. 256 */
+  float softmax_scale;   /* <= 0: 1/sqrt(head_dim) */
+} kvpop_config;
+
+typedef struct kvpop_state {
+  int32_t n;     /* newest processed position of the sequence; -1 when empty */
+  int32_t flags; /* KVPOP_FLAG_* bits, OR over the KV heads */
+} kvpop_state;
+
+/* Device bytes the cache needs for `cfg` (K/V rows, slot metadata and the
+ * decode workspace), or 0 if `cfg` is invalid.  Pure host arithmetic. */
+KVPOP_API size_t kvpop_cache_required_bytes(const kvpop_config* cfg);
+
+/* Create a cache on the current HIP device; every (layer, sequence) starts
+ * empty.  If `device_arena` is NULL the library allocates with hipMalloc and
+ * frees in kvpop_cache_destroy; otherwise it uses the caller's device memory
+ * (256-byte aligned, at least kvpop_cache_required_bytes(cfg) bytes), which
+ * must outlive the cache.  Initialisation runs on the legacy default stream
+ * and is complete when the call returns.  *out receives the handle.
+ * Errors: KVPOP_EINVAL (NULL pointer, invalid config, misaligned arena),
+ * KVPOP_ENOMEM (allocation failed or arena too small), KVPOP_EHIP (no usable
+ * device or a runtime error). */
+KVPOP_API int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena_bytes,
+                       kvpop_cache** out);
+
+/* Release the cache and the memory it allocated.  Waits for the device to
+ * finish using it.  NULL is a no-op. */
+KVPOP_API void kvpop_cache_destroy(kvpop_cache* cache);
+
+/* Mark (layer, seq) empty again (n = -1), stream-ordered.  The rows are not
+ * cleared; they are unreachable until refilled. */
+KVPOP_API int kvpop_cache_reset(kvpop_cache* cache, int32_t layer, int32_t seq, void* stream);
+
+/* Prefill compaction: fill the empty (layer, seq) from an n_tokens-long
+ * prompt.  k, v: device [Hkv][n_tokens][D] bf16.  scores: device
+ * [Hkv][n_tokens] float32, of which only positions n_sink .. n_tokens-n_recent-1
+ * are read (window positions are scored later, when they leave the window).
+ * Afterwards n = n_tokens-1 and each head keeps its sinks, its last n_recent
+ * positions, and the n_scored candidates with the largest keys.
+ * n_tokens == 0 is a no-op.  Errors: KVPOP_EINVAL (NULL pointers, bad
+ * indices, n_tokens < 0), KVPOP_ESTATE (not empty, poisoned, or n_tokens >
+ * max_positions). */
+KVPOP_API int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_t n_tokens,
+                          const uint16_t* k, const uint16_t* v, const float* scores,
+                          void* stream);
+
+/* One decode step of every sequence of `layer`: sequence b processes position
+ * n_b + 1 (position 0 if empty).
+ *   q            device [batch][Hq][D] bf16, the query of the new token
+ *   k_new, v_new device [batch][Hkv][D] bf16, K/V of the new token
+ *   score_leaving device [batch][Hkv] float32, the score of position
+ *                n_b + 1 - n_recent (the token leaving the window); read only
+ *                when that position is >= n_sink
+ *   out          device [batch][Hq][D] bf16, attention over the kept rows
+ *                (the new token included)
+ * The new token enters the window; the leaving token takes a scored slot
+ * (free, or the least important one's, which is evicted) or is dropped.
+ * Errors: KVPOP_EINVAL (NULL pointers, bad layer), KVPOP_ESTATE (poisoned or
+ * a sequence would reach max_positions), KVPOP_EHIP (launch failed). */
+KVPOP_API int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, const float* score_leaving, uint16_t* out,
+                      void* stream);
+
+/* Read back the state of (layer, seq).  Synchronises `stream` first.
+ *   st        host, receives n and flags
+ *   counts    host [Hkv] or NULL: kept rows per KV head
+ *   kept_pos  host [Hkv][budget] or NULL: kept positions of each head in
+ *             ascending order, padded with -1
+ * The caller owns the host buffers.  Errors: KVPOP_EINVAL, KVPOP_EHIP. */
+KVPOP_API int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, kvpop_state* st,
+                      int32_t* counts, int32_t* kept_pos, void* stream);
+
+/* Static description of a return code. */
+KVPOP_API const char* kvpop_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPOP_H_ */

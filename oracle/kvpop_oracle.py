@@ -205,12 +205,13 @@ class KVpopOracle:
             S[t] = score
         # else: t is dropped for good
 
-    def decode(self, q_bits, k_new_bits, v_new_bits, score_leaving):
+    def decode(self, q_bits, k_new_bits, v_new_bits, score_leaving, attend: bool = True):
         """Process token n = self.n + 1 and return out [Hq][D] (float64).
 
         q_bits: uint16 [Hq][D]; k_new_bits, v_new_bits: uint16 [Hkv][D];
         score_leaving: float [Hkv], the score of token n - W for each KV head
-        (ignored when n - W < s).
+        (ignored when n - W < s).  With attend=False only the cache is
+        updated and None is returned.
         """
         n = self.n + 1
         self._reserve(n + 1)
@@ -221,6 +222,12 @@ class KVpopOracle:
             for g in range(self.Hkv):
                 self._admit_leaving(g, t, _check_score(score_leaving[g]))
         self.n = n
+        if not attend:
+            return None
+        return self.attend(q_bits)
+
+    def attend(self, q_bits):
+        """Attention output [Hq][D] (float64) of q over the current kept rows."""
         q = bf16_to_f64(q_bits)
         out = np.zeros((self.Hq, self.D))
         for g in range(self.Hkv):

@@ -1,0 +1,374 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Kept sets must match bit-exactly; attention outputs within
+max|err| <= 2e-2 and relative L2 err <= 1e-2 (see gpu_harness).  The GPU
+side runs first and its results are copied to the host; the oracle then
+replays the same seeded inputs.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import (Geo, Stream, check_kept, check_output, log, make_cache, make_oracle,
+                         out_to_f64, to_dev_bf16, to_dev_f32)
+from fixed_budget_learned_amd import abi
+from fixed_budget_learned_amd.configs import (BATCH64_SERVING, LONG_131K_8X, QWEN3_8B_36L_4X,
+                                              QWEN3_8B_LAYER_4X, TINY)
+from fixed_budget_learned_amd.inputs import TokenStream, prompt_lengths
+from oracle import KVpopOracle, kept_by_definition
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    abi.load()
+    torch.cuda.init()
+
+
+def _geo(w):
+    return Geo(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sink, w.n_scored, w.n_recent)
+
+
+# ---------------------------------------------------------------------------
+# Generic driver: B sequences with ragged prompts, then `steps` decode steps
+# ---------------------------------------------------------------------------
+
+def run_case(geo: Geo, prompts, steps, score_kind="uniform", seed=0, splits=0,
+             check_every=1, out_every=1, layer=0, n_layers=1):
+    B = len(prompts)
+    streams = [Stream(geo, P + steps, seed * 1000 + b, score_kind) for b, P in enumerate(prompts)]
+    cache = make_cache(geo, n_layers=n_layers, batch=B, decode_splits=splits)
+    log(f"case geo={geo} prompts={prompts} steps={steps} scores={score_kind} splits={splits}")
+    for b, P in enumerate(prompts):
+        if P > 0:
+            cache.prefill_compact(layer, b, to_dev_bf16(streams[b].k[:, :P]),
+                                  to_dev_bf16(streams[b].v[:, :P]), to_dev_f32(streams[b].scores[:, :P]))
+    torch.cuda.synchronize()
+    gpu_kept = {}
+    gpu_out = {}
+
+    def snap_kept(i):
+        for b in range(B):
+            gpu_kept[(i, b)] = cache.state(layer, b)
+
+    snap_kept(-1)
+    H, Hq, D = geo.n_kv_heads, geo.n_q_heads, geo.head_dim
+    q = np.stack([np.stack([s.q[P + i] for s, P in zip(streams, prompts)]) for i in range(steps)])
+    kn = np.stack([np.stack([s.k[:, P + i] for s, P in zip(streams, prompts)]) for i in range(steps)])
+    vn = np.stack([np.stack([s.v[:, P + i] for s, P in zip(streams, prompts)]) for i in range(steps)])
+    sl = np.stack([np.stack([s.leaving(P + i) for s, P in zip(streams, prompts)]) for i in range(steps)])
+    qd, kd, vd, sd = to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn), to_dev_f32(sl)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    for i in range(steps):
+        cache.decode_step(layer, qd[i], kd[i], vd[i], sd[i], out)
+        if i % out_every == 0 or i == steps - 1:
+            gpu_out[i] = out_to_f64(out)
+        if i % check_every == 0 or i == steps - 1:
+            snap_kept(i)
+    torch.cuda.synchronize()
+    cache.close()
+
+    for b, P in enumerate(prompts):
+        s = streams[b]
+        orc = make_oracle(geo)
+        if P > 0:
+            orc.prefill(s.k[:, :P], s.v[:, :P], s.scores[:, :P])
+        _cmp_kept(gpu_kept[(-1, b)], orc, f"b={b} after prefill")
+        worst = 0.0
+        for i in range(steps):
+            n = P + i
+            assert np.array_equal(sl[i, b], s.scores[:, n - geo.n_recent]) if n - geo.n_recent >= 0 else True
+            ref = orc.decode(s.q[n], s.k[:, n], s.v[:, n], sl[i, b], attend=(i in gpu_out))
+            if i in gpu_out:
+                mx, _ = check_output(gpu_out[i][b], ref, f"b={b} step {i}")
+                worst = max(worst, mx)
+            if (i, b) in gpu_kept:
+                _cmp_kept(gpu_kept[(i, b)], orc, f"b={b} step {i}")
+        log(f"  seq {b}: P={P} ok, worst max|err| {worst:.2e}")
+
+
+def _cmp_kept(st, orc, what):
+    assert st.n == orc.n, f"{what}: n {st.n} != {orc.n}"
+    assert st.flags == 0, f"{what}: flags {st.flags}"
+    for g in range(orc.Hkv):
+        want = orc.kept(g)
+        got = st.kept[g].tolist()
+        if got != want:
+            raise AssertionError(f"{what}: head {g}: |got|={len(got)} |want|={len(want)} "
+                                 f"missing {sorted(set(want) - set(got))[:8]} "
+                                 f"extra {sorted(set(got) - set(want))[:8]}")
+
+
+# ---------------------------------------------------------------------------
+# Small and ragged cases, every step
+# ---------------------------------------------------------------------------
+
+CASES = [
+    ("g1_d64_from_empty", Geo(1, 1, 64, 4, 44, 16), [0], 150, "uniform", 0),
+    ("g4_d128_ragged_batch", Geo(8, 2, 128, 4, 100, 32), [0, 37, 500], 120, "uniform", 0),
+    ("g8_d64_ties", Geo(16, 2, 64, 2, 50, 8), [300, 3], 100, "ties", 0),
+    ("g2_d128_no_sink_signed_zero", Geo(4, 2, 128, 0, 20, 5), [100, 1], 60, "signed_zero_ties", 0),
+    ("k0_sink_plus_window", Geo(4, 1, 128, 4, 0, 16), [64], 40, "uniform", 0),
+    ("short_prompts", Geo(4, 1, 64, 4, 30, 16), [1, 2, 4, 5, 19, 20, 21, 50], 50, "normal", 0),
+    ("increasing_scores", Geo(4, 2, 128, 4, 40, 16), [200], 60, "increasing", 0),
+    ("decreasing_scores", Geo(4, 2, 128, 4, 40, 16), [200], 60, "decreasing", 0),
+    ("infinite_scores", Geo(8, 1, 128, 3, 60, 12), [400], 60, "inf", 0),
+    ("one_split", Geo(8, 2, 128, 4, 500, 64), [3000, 700], 40, "normal", 1),
+    ("max_splits", Geo(8, 2, 128, 4, 500, 64), [3000, 700], 40, "normal", 256),
+    ("odd_splits", Geo(8, 2, 128, 4, 500, 64), [3000, 700], 40, "ties", 7),
+    ("big_budget_multi_chunk", Geo(32, 8, 128, 4, 6000, 256), [9000], 30, "normal", 0),
+    ("gqa8_d128", Geo(64, 8, 128, 4, 200, 32), [1000], 30, "normal", 0),
+]
+
+
+@pytest.mark.parametrize("name,geo,prompts,steps,kind,splits", CASES, ids=[c[0] for c in CASES])
+def test_small_cases(name, geo, prompts, steps, kind, splits):
+    run_case(geo, prompts, steps, kind, seed=zlib.crc32(name.encode()) % 1000, splits=splits)
+
+
+def test_tiny_workload_every_step():
+    """Tiny single head, 512 tokens decoded from an empty cache."""
+    w = TINY
+    geo = _geo(w)
+    ts = TokenStream(w, 0, 0, 0, w.decode_steps)
+    kk, vv = ts.step_kv()
+    sl = ts.step_leaving_scores()
+    cache = make_cache(geo)
+    qd, kd, vd, sd = to_dev_bf16(ts.q), to_dev_bf16(kk), to_dev_bf16(vv), to_dev_f32(sl)
+    out = torch.empty((1, 1, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    outs, kept = [], []
+    for n in range(w.decode_steps):
+        cache.decode_step(0, qd[n:n + 1], kd[n:n + 1], vd[n:n + 1], sd[n:n + 1], out)
+        outs.append(out_to_f64(out)[0])
+        kept.append(cache.state(0, 0).kept[0].tolist())
+    cache.close()
+    orc = make_oracle(geo)
+    for n in range(w.decode_steps):
+        ref = orc.decode(ts.q[n], kk[n], vv[n], sl[n])
+        assert kept[n] == orc.kept(0) == kept_by_definition(ts.scores[0], n, w.n_sink, w.n_scored, w.n_recent)
+        check_output(outs[n], ref, f"step {n}")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads
+# ---------------------------------------------------------------------------
+
+def _full_layer(w, layer, steps, n_layers=1, cache=None, check_every=64, out_every=16, seq=0):
+    geo = _geo(w)
+    P = int(prompt_lengths(w)[seq])
+    ts = TokenStream(w, layer, seq, P, steps)
+    own = cache is None
+    if own:
+        cache = make_cache(geo, n_layers=n_layers, batch=1)
+    log(f"{w.name} layer {layer}: P={P} steps={steps}")
+    cache.prefill_compact(layer, 0, to_dev_bf16(ts.prompt_k()), to_dev_bf16(ts.prompt_v()),
+                          to_dev_f32(ts.prompt_scores()))
+    kk, vv = ts.step_kv()
+    sl = ts.step_leaving_scores()
+    qd, kd, vd, sd = to_dev_bf16(ts.q), to_dev_bf16(kk), to_dev_bf16(vv), to_dev_f32(sl)
+    out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    kept = {-1: cache.state(layer, 0)}
+    outs = {}
+    for i in range(steps):
+        cache.decode_step(layer, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], sd[i:i + 1], out)
+        if i % out_every == 0 or i == steps - 1:
+            outs[i] = out_to_f64(out)[0]
+        if i % check_every == 0 or i == steps - 1:
+            kept[i] = cache.state(layer, 0)
+    torch.cuda.synchronize()
+    if own:
+        cache.close()
+    orc = make_oracle(geo)
+    orc.prefill(ts.prompt_k(), ts.prompt_v(), ts.prompt_scores())
+    _cmp_kept(kept[-1], orc, "after prefill")
+    # the prefill kept set also equals the definition written out directly
+    for g in (0, w.n_kv_heads - 1):
+        assert kept[-1].kept[g].tolist() == kept_by_definition(ts.scores[g], P - 1, w.n_sink,
+                                                                w.n_scored, w.n_recent)
+    worst = 0.0
+    for i in range(steps):
+        ref = orc.decode(ts.q[i], kk[i], vv[i], sl[i], attend=(i in outs))
+        if i in outs:
+            worst = max(worst, check_output(outs[i], ref, f"step {i}")[0])
+        if i in kept:
+            _cmp_kept(kept[i], orc, f"step {i}")
+    log(f"  ok, worst max|err| {worst:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_layer_full():
+    """One Qwen3-8B layer at 4x: prefill 16,384 then 1,024 decode steps."""
+    _full_layer(QWEN3_8B_LAYER_4X, 0, QWEN3_8B_LAYER_4X.decode_steps)
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_36_layer_stack_sampled_layers():
+    """36-layer cache; layers 0, 17 and 35 (independent seeds), 96 steps each."""
+    w = QWEN3_8B_36L_4X
+    cache = make_cache(_geo(w), n_layers=w.n_layers, batch=1)
+    for layer in (0, 17, 35):
+        _full_layer(w, layer, 96, cache=cache, check_every=32, out_every=8)
+    cache.close()
+
+
+@pytest.mark.timeout(600)
+def test_long_context_131k_last_layer():
+    """131,072-token prefill at 88 % compression on the last of 36 layers."""
+    w = LONG_131K_8X
+    cache = make_cache(_geo(w), n_layers=w.n_layers, batch=1)
+    _full_layer(w, 35, 64, cache=cache, check_every=32, out_every=8)
+    cache.close()
+
+
+@pytest.mark.timeout(900)
+def test_batched_serving_b64():
+    """64 sequences with drawn prompt lengths and quantized (tied) scores."""
+    w = BATCH64_SERVING
+    geo = _geo(w)
+    steps = 48
+    Ps = prompt_lengths(w)
+    B = w.batch
+    cache = make_cache(geo, batch=B)
+    log(f"batched: prompts {Ps.min()}..{Ps.max()}, {steps} steps")
+    q = np.zeros((steps, B, w.n_q_heads, w.head_dim), np.uint16)
+    kn = np.zeros((steps, B, w.n_kv_heads, w.head_dim), np.uint16)
+    vn = np.zeros_like(kn)
+    sl = np.zeros((steps, B, w.n_kv_heads), np.float32)
+    for b in range(B):
+        if b % 16 == 0:
+            log(f"  prefill sequence {b}")
+        ts = TokenStream(w, 0, b, int(Ps[b]), steps)
+        cache.prefill_compact(0, b, to_dev_bf16(ts.prompt_k()), to_dev_bf16(ts.prompt_v()),
+                              to_dev_f32(ts.prompt_scores()))
+        k_, v_ = ts.step_kv()
+        q[:, b], kn[:, b], vn[:, b], sl[:, b] = ts.q, k_, v_, ts.step_leaving_scores()
+        del ts
+    torch.cuda.synchronize()
+    kept0 = [cache.state(0, b) for b in range(B)]
+    qd, kd, vd, sd = to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn), to_dev_f32(sl)
+    out = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    outs = {}
+    for i in range(steps):
+        cache.decode_step(0, qd[i], kd[i], vd[i], sd[i], out)
+        if i % 12 == 0 or i == steps - 1:
+            outs[i] = out_to_f64(out)
+    kept1 = [cache.state(0, b) for b in range(B)]
+    cache.close()
+    sample = set(range(0, B, 9)) | {B - 1}
+    for b in range(B):
+        ts = TokenStream(w, 0, b, int(Ps[b]), steps)
+        orc = make_oracle(geo)
+        orc.prefill(ts.prompt_k(), ts.prompt_v(), ts.prompt_scores())
+        _cmp_kept(kept0[b], orc, f"seq {b} after prefill")
+        k_, v_ = ts.step_kv()
+        sls = ts.step_leaving_scores()
+        for i in range(steps):
+            ref = orc.decode(ts.q[i], k_[i], v_[i], sls[i], attend=(b in sample and i in outs))
+            if ref is not None:
+                check_output(outs[i][b], ref, f"seq {b} step {i}")
+        _cmp_kept(kept1[b], orc, f"seq {b} after {steps} steps")
+        del ts, orc
+        if b % 8 == 7:
+            log(f"  oracle checked sequences 0..{b}")
+    log("  batched ok")
+
+
+# ---------------------------------------------------------------------------
+# Determinism, split invariance, state machine
+# ---------------------------------------------------------------------------
+
+def _decode_run(geo, P, steps, splits, seed=7, kind="normal"):
+    s = Stream(geo, P + steps, seed, kind)
+    cache = make_cache(geo, decode_splits=splits)
+    cache.prefill_compact(0, 0, to_dev_bf16(s.k[:, :P]), to_dev_bf16(s.v[:, :P]),
+                          to_dev_f32(s.scores[:, :P]))
+    out = torch.empty((1, geo.n_q_heads, geo.head_dim), dtype=torch.bfloat16, device="cuda")
+    outs = []
+    for i in range(steps):
+        n = P + i
+        cache.decode_step(0, to_dev_bf16(s.q[n][None]), to_dev_bf16(s.k[:, n][None]),
+                          to_dev_bf16(s.v[:, n][None]), to_dev_f32(s.leaving(n)[None]), out)
+        outs.append(out.view(torch.int16).cpu().numpy().copy())
+    st = cache.state(0, 0)
+    cache.close()
+    return outs, [k.tolist() for k in st.kept]
+
+
+def test_deterministic_and_split_invariant():
+    geo = Geo(32, 8, 128, 4, 3772, 256)
+    a_out, a_kept = _decode_run(geo, 16384, 24, 0)
+    b_out, b_kept = _decode_run(geo, 16384, 24, 0)
+    assert a_kept == b_kept
+    for x, y in zip(a_out, b_out):
+        assert np.array_equal(x, y), "two identical runs differ"
+    for splits in (1, 2, 33, 256):
+        c_out, c_kept = _decode_run(geo, 16384, 24, splits)
+        assert c_kept == a_kept
+        for x, y in zip(a_out, c_out):
+            xf = out_to_f64(torch.from_numpy(x).view(torch.bfloat16))
+            yf = out_to_f64(torch.from_numpy(y).view(torch.bfloat16))
+            assert np.abs(xf - yf).max() <= 2e-3
+
+
+def test_state_machine_errors_and_reset():
+    geo = Geo(4, 1, 64, 2, 10, 4)
+    cache = make_cache(geo, max_positions=40)
+    s = Stream(geo, 60, 3)
+    k, v, sc = to_dev_bf16(s.k[:, :30]), to_dev_bf16(s.v[:, :30]), to_dev_f32(s.scores[:, :30])
+    cache.prefill_compact(0, 0, k, v, sc)
+    with pytest.raises(abi.KVpopError) as e:
+        cache.prefill_compact(0, 0, k, v, sc)
+    assert e.value.code == abi.KVPOP_ESTATE
+    out = torch.empty((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    for n in range(30, 40):                      # positions up to max_positions - 1
+        cache.decode_step(0, to_dev_bf16(s.q[n][None]), to_dev_bf16(s.k[:, n][None]),
+                          to_dev_bf16(s.v[:, n][None]), to_dev_f32(s.leaving(n)[None]), out)
+    with pytest.raises(abi.KVpopError) as e:     # position 40 is past the limit
+        n = 40
+        cache.decode_step(0, to_dev_bf16(s.q[n][None]), to_dev_bf16(s.k[:, n][None]),
+                          to_dev_bf16(s.v[:, n][None]), to_dev_f32(s.leaving(n)[None]), out)
+    assert e.value.code == abi.KVPOP_ESTATE
+    assert cache.state(0, 0).n == 39
+    with pytest.raises(ValueError):
+        cache.decode_step(0, to_dev_bf16(s.q[0]), to_dev_bf16(s.k[:, 0][None]),
+                          to_dev_bf16(s.v[:, 0][None]), to_dev_f32(s.leaving(0)[None]), out)
+    # reset, then the same prompt again gives the oracle's kept set
+    cache.reset(0, 0)
+    assert cache.state(0, 0).n == -1
+    cache.prefill_compact(0, 0, k, v, sc)
+    orc = make_oracle(geo)
+    orc.prefill(s.k[:, :30], s.v[:, :30], s.scores[:, :30])
+    _cmp_kept(cache.state(0, 0), orc, "after reset + prefill")
+    # empty prompt is a no-op
+    cache.reset(0, 0)
+    cache.prefill_compact(0, 0, to_dev_bf16(s.k[:, :0]), to_dev_bf16(s.v[:, :0]),
+                          to_dev_f32(s.scores[:, :0]))
+    assert cache.state(0, 0).n == -1
+    cache.close()
+
+
+def test_nan_score_sets_flag():
+    geo = Geo(4, 1, 64, 2, 10, 4)
+    cache = make_cache(geo)
+    s = Stream(geo, 40, 5)
+    sc = s.scores[:, :30].copy()
+    sc[0, 7] = np.nan
+    cache.prefill_compact(0, 0, to_dev_bf16(s.k[:, :30]), to_dev_bf16(s.v[:, :30]), to_dev_f32(sc))
+    st = cache.state(0, 0)
+    assert st.flags & abi.KVPOP_FLAG_NAN_SCORE
+    cache.close()
+    cache = make_cache(geo)
+    out = torch.empty((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    for n in range(12):
+        sl = s.leaving(n)
+        if n == 9:
+            sl[:] = np.nan
+        cache.decode_step(0, to_dev_bf16(s.q[n][None]), to_dev_bf16(s.k[:, n][None]),
+                          to_dev_bf16(s.v[:, n][None]), to_dev_f32(sl[None]), out)
+    assert cache.state(0, 0).flags & abi.KVPOP_FLAG_NAN_SCORE
+    cache.close()

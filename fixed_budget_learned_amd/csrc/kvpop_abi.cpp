@@ -21,7 +21,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   size_t kc, vc, keys, pos, ring, ctl, sel, part_acc, part_ml, part_min, tickets, total;
-  int32_t nsplit, rows_per_split;
+  int32_t nsplit, rows_per_split, threads, rows_per_thread;
 };
 
 bool mul_ok(size_t a, size_t b, size_t* r) {
@@ -46,17 +46,26 @@ bool config_valid(const kvpop_config* c) {
   return true;
 }
 
-// Split count for decode: about four workgroups per compute unit in total,
-// at least 4 passes of rows per split.
-void choose_splits(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split) {
+// Decode launch shape.  Each KV head's slots are split over `nsplit`
+// workgroups of `threads` threads, each thread holding `rows_per_thread`
+// rows per pass.  Few heads (batch 1): about 128 workgroups in total, one
+// pass of 4 rows per thread each.  Many heads: one workgroup per head
+// streaming 2-row passes (measured fastest on MI355X for these shapes).
+void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
+                         int32_t* threads, int32_t* rows_per_thread) {
   const int64_t budget = int64_t(c.n_sink) + c.n_scored + c.n_recent;
-  const int64_t rpp = kvpop::decode_rows_per_pass(c.head_dim);
   const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
+  const int G = c.n_q_heads / c.n_kv_heads;
+  const int nt = 256;
+  int np = 4;
+  if (heads >= 256 && kvpop::decode_shape_supported(c.head_dim, G, nt, 2)) np = 2;
+  const int64_t rpp = nt / (c.head_dim / 16);
+  const int64_t chunk = rpp * np;
   int64_t ns = c.decode_splits;
   if (ns == 0) {
-    const int64_t target = 1024;
+    const int64_t target = 128;  // workgroups in flight
     ns = (target + heads - 1) / heads;
-    const int64_t cap = std::max<int64_t>(1, (budget + 4 * rpp - 1) / (4 * rpp));
+    const int64_t cap = std::max<int64_t>(1, (budget + chunk - 1) / chunk);
     ns = std::min<int64_t>(std::max<int64_t>(ns, 1), cap);
     ns = std::min<int64_t>(ns, kvpop::decode_max_splits());
   }
@@ -64,6 +73,8 @@ void choose_splits(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_spl
   rows = (rows + rpp - 1) / rpp * rpp;
   *nsplit = int32_t(ns);
   *rows_per_split = int32_t(rows);
+  *threads = nt;
+  *rows_per_thread = np;
 }
 
 bool compute_layout(const kvpop_config& c, Layout* L) {
@@ -71,7 +82,7 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   const size_t heads_all = size_t(c.n_layers) * c.batch * c.n_kv_heads;
   const size_t heads = size_t(c.batch) * c.n_kv_heads;
   const size_t G = size_t(c.n_q_heads / c.n_kv_heads);
-  choose_splits(c, &L->nsplit, &L->rows_per_split);
+  choose_decode_shape(c, &L->nsplit, &L->rows_per_split, &L->threads, &L->rows_per_thread);
   size_t rows, kvb, tmp;
   if (!mul_ok(heads_all, budget, &rows)) return false;
   if (!mul_ok(rows, size_t(c.head_dim) * 2, &kvb)) return false;
@@ -157,6 +168,8 @@ struct kvpop_cache {
     w.tickets = reinterpret_cast<uint32_t*>(base + lay.tickets);
     w.nsplit = lay.nsplit;
     w.rows_per_split = lay.rows_per_split;
+    w.threads = lay.threads;
+    w.rows_per_thread = lay.rows_per_thread;
     return w;
   }
 };

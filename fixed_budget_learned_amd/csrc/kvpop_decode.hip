@@ -15,24 +15,36 @@
 //
 // Decomposition.  The grid is (head, split): each workgroup owns a range of
 // slots of one KV head.  Every workgroup re-derives the same eviction
-// decision from the head's control block, so no workgroup waits for another.
-// A workgroup reads K/V of its slots from the cache, except the slot the new
-// token takes, whose row it takes from the k_new/v_new inputs.  It writes a
-// partial softmax state (running max, sum, unnormalised accumulator) and the
-// minimum key over its slots as they will be after this step.  The last
-// workgroup of a head to finish (a ticket counter with device-scope
-// release/acquire) merges the partials into the bf16 output, reduces the
-// next minimum, and only then writes the cache update (new K/V row, keys,
-// positions, window ring, control block).  All mutation therefore happens
-// after every workgroup of the head has finished reading, so no read in the
-// launch races with a write.
+// decision from the head's control block (which also carries the slot of the
+// token about to leave the window, so no dependent lookup is needed), so no
+// workgroup waits for another.  A workgroup reads K/V of its slots from the
+// cache, and substitutes the k_new/v_new row for the slot the new token
+// takes.  It writes a partial softmax state (max, sum, unnormalised
+// accumulator) and the minimum key over its slots as they will be after
+// this step.  The last workgroup of a head to finish (ticket counter,
+// device-scope release/acquire, one L2 writeback per workgroup) merges the
+// partials into the bf16 output, reduces the next minimum, and only then
+// writes the cache update (new K/V row, keys, positions, window ring,
+// control block).  Every mutation therefore happens after all workgroups of
+// the head have finished reading; no read in the launch races with a write.
 //
-// Inner loop.  16 lanes share one 256-byte K row (head_dim 128; 8 lanes for
-// 64) and each loads 16 bytes, so a wavefront reads 4 whole rows per
-// instruction, fully coalesced.  q.k uses v_dot2 on bf16 pairs with fp32
-// accumulation and a 16-lane DPP all-reduce; every row group keeps its own
-// online-softmax state (exp2 domain, scale * log2(e) folded in), so the loop
-// needs no workgroup barrier.  Row groups are merged through LDS at the end.
+// Latency.  All loads a workgroup needs (K/V and keys of its first chunk,
+// q, the new row, the control block, the score) are issued before anything
+// waits, and chunks (K/V rows and their keys) are double-buffered in
+// registers.  The merge issues all of its partial loads at once.
+//
+// Inner loop.  LPR = D/16 lanes share one row; each lane holds two 16-byte
+// pieces (offsets 16*lane and D + 16*lane bytes), so every load instruction
+// reads whole 128/64-byte row halves, coalesced.  q.k uses v_dot2 on bf16
+// pairs with fp32 accumulation and an LPR-lane DPP all-reduce.  Softmax runs
+// in the exp2 domain (scale * log2(e) folded in) with one running max per
+// wavefront that moves only when a logit exceeds it by 2^8, so rescaling is
+// rare and no barrier is needed.  P.V takes two rows at a time: the bf16
+// probabilities of both rows are packed into one register, the two rows' V
+// values are interleaved with v_perm, and v_dot2 adds both products into the
+// fp32 accumulator (the sum of probabilities uses the same rounded values).
+// Row groups are summed with DPP inside each wave and through LDS across
+// waves.
 #include <hip/hip_runtime.h>
 
 #include "kvpop_device.h"
@@ -41,7 +53,6 @@
 namespace kvpop {
 namespace {
 
-constexpr int DEC_THREADS = 256;
 constexpr int MAX_SPLITS = 256;
 
 struct DecodeParams {
@@ -67,6 +78,8 @@ struct DecodeParams {
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -77,46 +90,84 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;
-constexpr int DPP_MIRROR = 0x140;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over groups of LPR lanes (LPR = 8 or 16, aligned); result in all lanes.
+// Sum over aligned groups of LPR lanes (LPR = 4 or 8); result in all lanes.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp_f<DPP_QUAD_XOR1>(x);
   x += dpp_f<DPP_QUAD_XOR2>(x);
-  x += dpp_f<DPP_HALF_MIRROR>(x);
-  if constexpr (LPR == 16) x += dpp_f<DPP_MIRROR>(x);
+  if constexpr (LPR == 8) x += dpp_f<DPP_HALF_MIRROR>(x);
   return x;
 }
 
-__device__ __forceinline__ float safe_exp2_diff(float x, float m) {
-  // exp2(x - m) with exp2(-inf - anything) = 0 and m = -inf treated as 0.
-  return exp2f(x - m);
+__device__ __forceinline__ bool key_less(uint64_t ka, int32_t sa, uint64_t kb, int32_t sb) {
+  return ka < kb || (ka == kb && sa < sb);
 }
 
-template <int D, int G, int NP>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeParams p) {
-  constexpr int LPR = D / 8;            // lanes per row, 16 bytes each
-  constexpr int RPP = DEC_THREADS / LPR;  // rows per pass
-  constexpr int CHUNK = NP * RPP;
-  constexpr int NWAVE = DEC_THREADS / WAVE;
+// Lazy rescaling: the running max only moves when a logit exceeds it by
+// more than this many powers of two, so exponentials stay below 2^8 and the
+// accumulators are rescaled rarely.
+constexpr float RESCALE_SLACK = 8.f;
+constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
 
-  __shared__ float s_m[RPP][G];
-  __shared__ float s_l[RPP][G];
-  __shared__ float s_f[RPP][G];
-  __shared__ float s_acc[RPP][G * D];
+__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, WAVE)); }
+
+// Max over the whole wavefront of a value that is identical within aligned
+// groups of LPR lanes.
+template <int LPR>
+__device__ __forceinline__ float wave_max_groups(float x) {
+  if constexpr (LPR <= 4) x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                               0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF,
+                                                           false)));  // row_ror:8
+  x = xor_max(x, 16);
+  x = xor_max(x, 32);
+  return x;
+}
+
+// Sum over the row groups of one 16-lane DPP row (lanes i, i+8 [, i+4, i+12]).
+template <int LPR>
+__device__ __forceinline__ float row16_sum_groups(float x) {
+  if constexpr (LPR <= 4)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return x;
+}
+
+template <int D, int G, int NT, int NP>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
+  static_assert(NP % 2 == 0, "rows are consumed in pairs");
+  constexpr int LPR = D / 16;            // lanes per row; 2 x 16 bytes each
+  constexpr int HALF4 = D / 16;          // uint4 offset of the second half
+  constexpr int RPP = NT / LPR;          // rows per pass
+  constexpr int CHUNK = NP * RPP;        // rows per double-buffered chunk
+  static_assert(CHUNK <= NT, "one key per thread per chunk");
+  constexpr int NWAVE = NT / WAVE;
+  constexpr int R16 = WAVE / 16;         // 16-lane DPP rows per wavefront
+  constexpr int ACC = 16;                // accumulators per head per lane
+  constexpr int Q4 = G * D / 4;          // float4s in one split's accumulator
+  static_assert(Q4 <= NT, "merge needs one thread per float4");
+  constexpr int TS = NT / Q4;            // merge threads per float4 column
+  constexpr int MB = 16;                 // merge loads in flight per thread
+  // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators; the
+  // finishing workgroup reuses it for the split merge
+  constexpr int LDS_ROWS = NWAVE * R16 * LPR * G * ACC;
+  constexpr int LDS_MERGE = 3 * MAX_SPLITS * G + TS * G * D;
+  constexpr int LDS_F = LDS_ROWS > LDS_MERGE ? LDS_ROWS : LDS_MERGE;
+
+  __shared__ __align__(16) float s_buf[LDS_F];
+  __shared__ float s_wm[NWAVE][G];       // wave max (log2 units)
+  __shared__ float s_wl[NWAVE][R16][G];  // per DPP-row sums of p
+  __shared__ float s_f[NWAVE][G];
   __shared__ float s_M[G], s_L[G];
   __shared__ uint64_t s_mk[NWAVE];
   __shared__ int32_t s_ms[NWAVE];
   __shared__ int32_t s_last;
-  __shared__ float s_pm[MAX_SPLITS * G];
-  __shared__ float s_pl[MAX_SPLITS * G];
-  __shared__ float s_pf[MAX_SPLITS * G];
 
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
@@ -137,20 +188,58 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // ---- eviction decision, identical in every workgroup of the head -------
+  // ---- issue every independent load first ---------------------------------
   const HeadCtl c = p.ctl[head];
+  const float sg = p.score_leaving[head];
   const int32_t W = p.n_recent;
+  const int32_t lo = split * p.rows_per_split;
+  const int32_t hi_alloc = min(lo + p.rows_per_split, p.budget);
+  const int rg = tid / LPR;
+  const int cc = tid % LPR;
+  const int64_t hrow = static_cast<int64_t>(head) * p.budget;
+  constexpr int ROW4 = D / 8;            // uint4 per row
+  const uint4* kb = reinterpret_cast<const uint4*>(p.kc) + hrow * ROW4 + cc;
+  const uint4* vb = reinterpret_cast<const uint4*>(p.vc) + hrow * ROW4 + cc;
+  const uint64_t* kyb = p.keys + hrow;
+
+  uint4 ka[NP][2], va[NP][2];
+  uint64_t key_c = KEY_NONE;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int32_t r = lo + i * RPP + rg;
+    if (r < hi_alloc) {
+      ka[i][0] = kb[static_cast<int64_t>(r) * ROW4];
+      ka[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
+      va[i][0] = vb[static_cast<int64_t>(r) * ROW4];
+      va[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
+    } else {
+      ka[i][0] = ka[i][1] = va[i][0] = va[i][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  if (tid < CHUNK && lo + tid < hi_alloc) key_c = kyb[lo + tid];
+  const uint4* knp = reinterpret_cast<const uint4*>(p.k_new) + static_cast<int64_t>(head) * ROW4 + cc;
+  const uint4* vnp = reinterpret_cast<const uint4*>(p.v_new) + static_cast<int64_t>(head) * ROW4 + cc;
+  const uint4 knew0 = knp[0], knew1 = knp[HALF4];
+  const uint4 vnew0 = vnp[0], vnew1 = vnp[HALF4];
+  uint4 qv[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4* qp = reinterpret_cast<const uint4*>(p.q) + (static_cast<int64_t>(head) * G + h) * ROW4 + cc;
+    qv[h][0] = qp[0];
+    qv[h][1] = qp[HALF4];
+  }
+
+  // ---- eviction decision, identical in every workgroup of the head -------
   const int32_t n = c.n + 1;
   const int32_t t = n - W;
   int32_t newslot = c.count, count_new = c.count, nscored_new = c.nscored, st = -1;
-  bool admitted = false, evict = false;
+  bool admitted = false;
   uint64_t keyt = KEY_NONE;
   int32_t flags = c.flags;
   if (t < p.n_sink) {
-    count_new = c.count + 1;                     // sink or window still filling
+    count_new = c.count + 1;                     // sink, or window still filling
   } else {
-    st = p.ring[static_cast<int64_t>(head) * W + (t % W)];
-    const float sg = p.score_leaving[head];
+    st = c.leave_slot;
     if (score_is_nan(sg)) flags |= 1;
     keyt = make_key(score_code(sg), t);
     if (c.nscored < p.n_scored) {                // free scored slot
@@ -159,177 +248,226 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeParams p) {
       nscored_new = c.nscored + 1;
     } else if (keyt > c.minkey) {                // replaces the least important
       admitted = true;
-      evict = true;
       newslot = c.minslot;
     } else {                                     // dropped for good
       newslot = st;
     }
   }
+  // slot of the next token to leave (needed by the finishing workgroup)
+  const int32_t ring_next = p.ring[static_cast<int64_t>(head) * W + ((n + 1) % W)];
 
   // ---- attention over slots [lo, hi) --------------------------------------
-  const int32_t lo = split * p.rows_per_split;
   const int32_t hi = min(lo + p.rows_per_split, count_new);
-  const int rg = tid / LPR;
-  const int cc = tid % LPR;
-  const int64_t hrow = static_cast<int64_t>(head) * p.budget;
-  const uint4* kb = reinterpret_cast<const uint4*>(p.kc) + hrow * LPR + cc;
-  const uint4* vb = reinterpret_cast<const uint4*>(p.vc) + hrow * LPR + cc;
-  const uint4 knew = reinterpret_cast<const uint4*>(p.k_new)[static_cast<int64_t>(head) * LPR + cc];
-  const uint4 vnew = reinterpret_cast<const uint4*>(p.v_new)[static_cast<int64_t>(head) * LPR + cc];
-  uint4 qv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    qv[h] = reinterpret_cast<const uint4*>(p.q)[(static_cast<int64_t>(head) * G + h) * LPR + cc];
-
-  float m_run[G], l_run[G], acc[G][8];
+  float m_run[G], l_run[G], acc[G][ACC];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < ACC; ++e) acc[h][e] = 0.f;
   }
+  uint64_t mk = KEY_NONE;
+  int32_t msl = 0x7FFFFFFF;
 
   for (int32_t base = lo; base < hi; base += CHUNK) {
-    uint4 kr[NP], vr[NP];
+    const int32_t nb = base + CHUNK;
+    uint4 kn[NP][2], vn[NP][2];
+    uint64_t key_n = KEY_NONE;
+    if (nb < hi) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int32_t r = base + i * RPP + rg;
-      if (r < hi) {
-        if (r == newslot) {
-          kr[i] = knew;
-          vr[i] = vnew;
+      for (int i = 0; i < NP; ++i) {
+        const int32_t r = nb + i * RPP + rg;
+        if (r < hi_alloc) {
+          kn[i][0] = kb[static_cast<int64_t>(r) * ROW4];
+          kn[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
+          vn[i][0] = vb[static_cast<int64_t>(r) * ROW4];
+          vn[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
         } else {
-          kr[i] = kb[static_cast<int64_t>(r) * LPR];
-          vr[i] = vb[static_cast<int64_t>(r) * LPR];
+          kn[i][0] = kn[i][1] = vn[i][0] = vn[i][1] = make_uint4(0, 0, 0, 0);
         }
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+      if (tid < CHUNK && nb + tid < hi_alloc) key_n = kyb[nb + tid];
+    }
+    // keys of this chunk, as they stand after this step
+    {
+      const int32_t r = base + tid;
+      if (tid < CHUNK && r < hi) {
+        uint64_t kv = key_c;
+        if (r == newslot)
+          kv = KEY_NONE;
+        else if (admitted && r == st)
+          kv = keyt;
+        if (kv < mk) {
+          mk = kv;
+          msl = r;
+        }
       }
     }
+    // logits
     float x[NP][G];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const bool valid = (base + i * RPP + rg) < hi;
+      const int32_t r = base + i * RPP + rg;
+      const bool valid = r < hi;
+      if (r == newslot) {
+        ka[i][0] = knew0;
+        ka[i][1] = knew1;
+        va[i][0] = vnew0;
+        va[i][1] = vnew1;
+      }
+      if (!valid) va[i][0] = va[i][1] = make_uint4(0, 0, 0, 0);  // unwritten slots
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = dot2_bf16(kr[i].x, qv[h].x, 0.f);
-        d = dot2_bf16(kr[i].y, qv[h].y, d);
-        d = dot2_bf16(kr[i].z, qv[h].z, d);
-        d = dot2_bf16(kr[i].w, qv[h].w, d);
+        float d = dot2_bf16(ka[i][0].x, qv[h][0].x, 0.f);
+        d = dot2_bf16(ka[i][0].y, qv[h][0].y, d);
+        d = dot2_bf16(ka[i][0].z, qv[h][0].z, d);
+        d = dot2_bf16(ka[i][0].w, qv[h][0].w, d);
+        d = dot2_bf16(ka[i][1].x, qv[h][1].x, d);
+        d = dot2_bf16(ka[i][1].y, qv[h][1].y, d);
+        d = dot2_bf16(ka[i][1].z, qv[h][1].z, d);
+        d = dot2_bf16(ka[i][1].w, qv[h][1].w, d);
         d = group_sum<LPR>(d);
         x[i][h] = valid ? d * p.scale_log2e : -INFINITY;
       }
     }
+    // lazy rescale: the wave-shared running max moves only when needed
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = m_run[h];
+      float mx = x[0][h];
 #pragma unroll
-      for (int i = 0; i < NP; ++i) mx = fmaxf(mx, x[i][h]);
-      const float ms = (mx == -INFINITY) ? 0.f : mx;
-      const float alpha = safe_exp2_diff(m_run[h], ms);
-      l_run[h] *= alpha;
+      for (int i = 1; i < NP; ++i) mx = fmaxf(mx, x[i][h]);
+      if (__any(mx > m_run[h] + RESCALE_SLACK)) {
+        const float mnew = fmaxf(m_run[h], wave_max_groups<LPR>(mx));
+        const float alpha = exp2f(m_run[h] - mnew);  // 0 while m_run is -inf
+        l_run[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < ACC; ++e) acc[h][e] *= alpha;
+        m_run[h] = mnew;
+      }
+    }
+    // P V on row pairs: bf16 probabilities, v_dot2 over the two rows
+#pragma unroll
+    for (int i = 0; i < NP; i += 2) {
+      uint32_t ph[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ms = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
+        float2_t pf = {exp2f(x[i][h] - ms), exp2f(x[i + 1][h] - ms)};
+        ph[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2v_t));
+        l_run[h] = dot2_bf16(ph[h], BF16_ONE_PAIR, l_run[h]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t a[4] = {va[i][hf].x, va[i][hf].y, va[i][hf].z, va[i][hf].w};
+        const uint32_t b[4] = {va[i + 1][hf].x, va[i + 1][hf].y, va[i + 1][hf].z, va[i + 1][hf].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo2 = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+          const uint32_t hi2 = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][hf * 8 + 2 * j] = dot2_bf16(lo2, ph[h], acc[h][hf * 8 + 2 * j]);
+            acc[h][hf * 8 + 2 * j + 1] = dot2_bf16(hi2, ph[h], acc[h][hf * 8 + 2 * j + 1]);
+          }
+        }
+      }
+    }
+    if (nb < hi) {
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const float pr = safe_exp2_diff(x[i][h], ms);
-        l_run[h] += pr;
-        acc[h][0] = fmaf(pr, bf16_lo(vr[i].x), acc[h][0]);
-        acc[h][1] = fmaf(pr, bf16_hi(vr[i].x), acc[h][1]);
-        acc[h][2] = fmaf(pr, bf16_lo(vr[i].y), acc[h][2]);
-        acc[h][3] = fmaf(pr, bf16_hi(vr[i].y), acc[h][3]);
-        acc[h][4] = fmaf(pr, bf16_lo(vr[i].z), acc[h][4]);
-        acc[h][5] = fmaf(pr, bf16_hi(vr[i].z), acc[h][5]);
-        acc[h][6] = fmaf(pr, bf16_lo(vr[i].w), acc[h][6]);
-        acc[h][7] = fmaf(pr, bf16_hi(vr[i].w), acc[h][7]);
+        ka[i][0] = kn[i][0];
+        ka[i][1] = kn[i][1];
+        va[i][0] = vn[i][0];
+        va[i][1] = vn[i][1];
       }
-      m_run[h] = mx;
+      key_c = key_n;
     }
   }
 
-  // ---- minimum key over [lo, hi) as it stands after this step -------------
-  uint64_t mk = KEY_NONE;
-  int32_t msl = 0x7FFFFFFF;
-  for (int32_t r = lo + tid; r < hi; r += DEC_THREADS) {
-    uint64_t kv;
-    if (r == newslot)
-      kv = KEY_NONE;
-    else if (admitted && r == st)
-      kv = keyt;
-    else
-      kv = p.keys[hrow + r];
-    if (kv < mk) {
-      mk = kv;
-      msl = r;
-    }
-  }
+  // ---- minimum key of the workgroup ---------------------------------------
   wave_min_key(mk, msl);
   if (lane == 0) {
     s_mk[wid] = mk;
     s_ms[wid] = msl;
   }
 
-  // ---- merge the row groups of this workgroup ------------------------------
-  if (cc == 0) {
+  // ---- merge the row groups: DPP within each 16-lane row, LDS across ------
+  // All row groups of a wave share m_run, so their partial sums add plainly.
+  const int r16 = lane / 16;
+  const bool writer = (lane % 16) < LPR;       // first row group of the DPP row
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_m[rg][h] = m_run[h];
-      s_l[rg][h] = l_run[h];
-    }
+  for (int h = 0; h < G; ++h) {
+    const float lsum = row16_sum_groups<LPR>(l_run[h]);
+    if (lane % 16 == 0) s_wl[wid][r16][h] = lsum;
+    if (lane == 0) s_wm[wid][h] = m_run[h];
+#pragma unroll
+    for (int e = 0; e < ACC; ++e) acc[h][e] = row16_sum_groups<LPR>(acc[h][e]);
   }
+  if (writer) {
+    float4* dst = reinterpret_cast<float4*>(&s_buf[(((wid * R16 + r16) * LPR + cc) * G) * ACC]);
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_acc[rg][h * D + cc * 8 + e] = acc[h][e];
+      for (int e = 0; e < ACC; e += 4)
+        dst[(h * ACC + e) / 4] = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+  }
   __syncthreads();
   if (tid < G) {
     float M = -INFINITY;
-    for (int r = 0; r < RPP; ++r) M = fmaxf(M, s_m[r][tid]);
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_wm[w][tid]);
     const float Ms = (M == -INFINITY) ? 0.f : M;
     float L = 0.f;
-    for (int r = 0; r < RPP; ++r) {
-      const float f = safe_exp2_diff(s_m[r][tid], Ms);
-      s_f[r][tid] = f;
-      L += s_l[r][tid] * f;
+    for (int w = 0; w < NWAVE; ++w) {
+      const float f = exp2f(s_wm[w][tid] - Ms);
+      s_f[w][tid] = f;
+      float lw = 0.f;
+      for (int r = 0; r < R16; ++r) lw += s_wl[w][r][tid];
+      L = fmaf(lw, f, L);
     }
     s_M[tid] = M;
     s_L[tid] = L;
   }
   __syncthreads();
   const int64_t pidx = static_cast<int64_t>(head) * p.nsplit + split;
-  for (int e = tid; e < G * D; e += DEC_THREADS) {
+  for (int e = tid; e < G * D; e += NT) {
     const int h = e / D;
+    const int d = e % D;
+    const int cl = (d % (D / 2)) / 8;                  // lane in group holding d
+    const int j = (d / (D / 2)) * 8 + d % 8;           // its accumulator index
     float a = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPP; ++r) a = fmaf(s_acc[r][e], s_f[r][h], a);
+    for (int w = 0; w < NWAVE; ++w) {
+      float aw = 0.f;
+#pragma unroll
+      for (int r = 0; r < R16; ++r) aw += s_buf[(((w * R16 + r) * LPR + cl) * G + h) * ACC + j];
+      a = fmaf(aw, s_f[w][h], a);
+    }
     p.part_acc[pidx * (G * D) + e] = a;
   }
   if (tid < G) {
-    p.part_ml[(pidx * G + tid) * 2 + 0] = s_M[tid];
-    p.part_ml[(pidx * G + tid) * 2 + 1] = s_L[tid];
+    reinterpret_cast<float2*>(p.part_ml)[pidx * G + tid] = make_float2(s_M[tid], s_L[tid]);
   }
   if (tid == 0) {
     uint64_t k0 = s_mk[0];
     int32_t sl0 = s_ms[0];
-    for (int w = 1; w < NWAVE; ++w) {
-      if (s_mk[w] < k0 || (s_mk[w] == k0 && s_ms[w] < sl0)) {
+    for (int w = 1; w < NWAVE; ++w)
+      if (key_less(s_mk[w], s_ms[w], k0, sl0)) {
         k0 = s_mk[w];
         sl0 = s_ms[w];
       }
-    }
     MinPart mp;
     mp.key = k0;
     mp.slot = sl0;
     mp.pad = 0;
     p.part_min[pidx] = mp;
   }
-
   // ---- ticket: the last workgroup of the head finishes the step ----------
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Every thread's stores complete, then one device-scope release (an L2
+  // writeback) covers the whole workgroup before the ticket is taken.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t prev =
         __hip_atomic_fetch_add(&p.tickets[head], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
@@ -338,51 +476,57 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeParams p) {
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  const int64_t p0 = static_cast<int64_t>(head) * p.nsplit;
-  for (int i = tid; i < p.nsplit * G; i += DEC_THREADS) {
-    const float2 ml = reinterpret_cast<const float2*>(p.part_ml)[p0 * G + i];
-    s_pm[i] = ml.x;
-    s_pl[i] = ml.y;
+  // ---- merge the splits: every load issued before the first wait ---------
+  const int ns = p.nsplit;
+  const int64_t p0 = static_cast<int64_t>(head) * ns;
+  float* s_pm = s_buf;                        // [ns][G] partial max
+  float* s_pl = s_buf + MAX_SPLITS * G;       // [ns][G] partial sum
+  float* s_pf = s_buf + 2 * MAX_SPLITS * G;   // [ns][G] rescale factor
+  float* s_red = s_buf + 3 * MAX_SPLITS * G;  // [TS][G*D] per-thread-group sums
+  float2 ml_r[(MAX_SPLITS * G + NT - 1) / NT];
+#pragma unroll
+  for (int u = 0; u < (MAX_SPLITS * G + NT - 1) / NT; ++u) {
+    const int i = tid + u * NT;
+    ml_r[u] = (i < ns * G) ? reinterpret_cast<const float2*>(p.part_ml)[p0 * G + i]
+                           : make_float2(-INFINITY, 0.f);
   }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < p.nsplit; ++sp) M = fmaxf(M, s_pm[sp * G + tid]);
-    s_M[tid] = (M == -INFINITY) ? 0.f : M;
-  }
-  __syncthreads();
-  for (int i = tid; i < p.nsplit * G; i += DEC_THREADS) {
-    const int h = i % G;
-    s_pf[i] = safe_exp2_diff(s_pm[i], s_M[h]);
-  }
-  __syncthreads();
-  if (tid < G) {
-    float L = 0.f;
-    for (int sp = 0; sp < p.nsplit; ++sp)
-      L = fmaf(s_pl[sp * G + tid], s_pf[sp * G + tid], L);
-    s_L[tid] = L;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * D; e += DEC_THREADS) {
-    const int h = e / D;
-    float a = 0.f;
-    for (int sp = 0; sp < p.nsplit; ++sp)
-      a = fmaf(p.part_acc[(p0 + sp) * (G * D) + e], s_pf[sp * G + h], a);
-    const float o = a / s_L[h];
-    p.out[static_cast<int64_t>(head) * (G * D) + e] = static_cast<uint16_t>(f32_to_bf16_rne(o));
-  }
-
-  // next minimum over the head's scored slots
-  {
-    uint64_t k0 = KEY_NONE;
-    int32_t sl0 = 0x7FFFFFFF;
-    for (int sp = tid; sp < p.nsplit; sp += DEC_THREADS) {
-      const MinPart mp = p.part_min[p0 + sp];
-      if (mp.key < k0 || (mp.key == k0 && mp.slot < sl0)) {
-        k0 = mp.key;
-        sl0 = mp.slot;
-      }
+  MinPart mp_r[(MAX_SPLITS + NT - 1) / NT];
+#pragma unroll
+  for (int u = 0; u < (MAX_SPLITS + NT - 1) / NT; ++u) {
+    const int i = tid + u * NT;
+    if (i < ns) {
+      mp_r[u] = p.part_min[p0 + i];
+    } else {
+      mp_r[u].key = KEY_NONE;
+      mp_r[u].slot = 0x7FFFFFFF;
     }
+  }
+  const int j4 = tid % Q4;
+  const int s0 = tid / Q4;
+  const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc);
+  float4 raw[MB];
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int sp = s0 + u * TS;
+    raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < (MAX_SPLITS * G + NT - 1) / NT; ++u) {
+    const int i = tid + u * NT;
+    if (i < ns * G) {
+      s_pm[i] = ml_r[u].x;
+      s_pl[i] = ml_r[u].y;
+    }
+  }
+  {
+    uint64_t k0 = mp_r[0].key;
+    int32_t sl0 = mp_r[0].slot;
+#pragma unroll
+    for (int u = 1; u < (MAX_SPLITS + NT - 1) / NT; ++u)
+      if (key_less(mp_r[u].key, mp_r[u].slot, k0, sl0)) {
+        k0 = mp_r[u].key;
+        sl0 = mp_r[u].slot;
+      }
     wave_min_key(k0, sl0);
     if (lane == 0) {
       s_mk[wid] = k0;
@@ -390,23 +534,81 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_pm[sp * G + tid]);
+    s_M[tid] = (M == -INFINITY) ? 0.f : M;
+  }
+  __syncthreads();
+  for (int i = tid; i < ns * G; i += NT) s_pf[i] = exp2f(s_pm[i] - s_M[i % G]);
+  __syncthreads();
+  if (tid < G) {
+    float L = 0.f;
+    for (int sp = 0; sp < ns; ++sp) L = fmaf(s_pl[sp * G + tid], s_pf[sp * G + tid], L);
+    s_L[tid] = L;
+  }
+  const int hq = (j4 * 4) / D;
+  float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int sp = s0 + u * TS;
+    const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
+    a4.x = fmaf(raw[u].x, f, a4.x);
+    a4.y = fmaf(raw[u].y, f, a4.y);
+    a4.z = fmaf(raw[u].z, f, a4.z);
+    a4.w = fmaf(raw[u].w, f, a4.w);
+  }
+  for (int sb = s0 + MB * TS; sb < ns; sb += MB * TS) {  // more than MB*TS splits
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int sp = sb + u * TS;
+      raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int sp = sb + u * TS;
+      const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
+      a4.x = fmaf(raw[u].x, f, a4.x);
+      a4.y = fmaf(raw[u].y, f, a4.y);
+      a4.z = fmaf(raw[u].z, f, a4.z);
+      a4.w = fmaf(raw[u].w, f, a4.w);
+    }
+  }
+  reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
+  __syncthreads();
+  if (s0 == 0) {
+    float4 o = reinterpret_cast<const float4*>(s_red)[j4];
+    for (int ts = 1; ts < TS; ++ts) {
+      const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
+      o.x += y.x;
+      o.y += y.y;
+      o.z += y.z;
+      o.w += y.w;
+    }
+    const float invL = 1.f / s_L[hq];
+    const uint32_t b0 = f32_to_bf16_rne(o.x * invL), b1 = f32_to_bf16_rne(o.y * invL);
+    const uint32_t b2 = f32_to_bf16_rne(o.z * invL), b3 = f32_to_bf16_rne(o.w * invL);
+    reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + j4] =
+        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+  }
 
-  // cache update: the new token's row, slot metadata, window ring, control
-  uint4* kw = reinterpret_cast<uint4*>(p.kc) + (hrow + newslot) * LPR;
-  uint4* vw = reinterpret_cast<uint4*>(p.vc) + (hrow + newslot) * LPR;
-  if (tid < LPR) {
-    kw[tid] = reinterpret_cast<const uint4*>(p.k_new)[static_cast<int64_t>(head) * LPR + tid];
-    vw[tid] = reinterpret_cast<const uint4*>(p.v_new)[static_cast<int64_t>(head) * LPR + tid];
+  // ---- cache update: new row, slot metadata, window ring, control block --
+  if (tid < LPR) {  // lane tid holds chunks tid and tid + D/16 of the new row
+    uint4* kw = reinterpret_cast<uint4*>(p.kc) + (hrow + newslot) * ROW4 + tid;
+    uint4* vw = reinterpret_cast<uint4*>(p.vc) + (hrow + newslot) * ROW4 + tid;
+    kw[0] = knew0;
+    kw[HALF4] = knew1;
+    vw[0] = vnew0;
+    vw[HALF4] = vnew1;
   }
   if (tid == 0) {
     uint64_t k0 = s_mk[0];
     int32_t sl0 = s_ms[0];
-    for (int w = 1; w < NWAVE; ++w) {
-      if (s_mk[w] < k0 || (s_mk[w] == k0 && s_ms[w] < sl0)) {
+    for (int w = 1; w < NWAVE; ++w)
+      if (key_less(s_mk[w], s_ms[w], k0, sl0)) {
         k0 = s_mk[w];
         sl0 = s_ms[w];
       }
-    }
     if (admitted) p.keys[hrow + st] = keyt;
     p.keys[hrow + newslot] = KEY_NONE;
     p.pos[hrow + newslot] = n;
@@ -418,35 +620,60 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeParams p) {
     nc.minslot = (k0 == KEY_NONE) ? -1 : sl0;
     nc.minkey = k0;
     nc.flags = flags;
-    nc.pad = 0;
+    // with a one-token window the next leaving token is the one just added
+    nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? newslot : ring_next);
     p.ctl[head] = nc;
     p.tickets[head] = 0u;
   }
-  (void)evict;
 }
 
-template <int D, int G>
-hipError_t launch_dg(const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G, 4>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(DEC_THREADS), 0, stream, prm);
+template <int D, int G, int NT, int NP>
+hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, G, NT, NP>), dim3(static_cast<uint32_t>(blocks)), dim3(NT),
+                     0, stream, prm);
   return hipGetLastError();
 }
 
+// Compiled launch shapes: (256 threads, 4 rows per thread) for every head
+// size and group; the Qwen3 shape (D 128, G 4) also gets 2 or 8 rows per
+// thread, and 512-thread workgroups with 2.
+template <int D, int G>
+hipError_t launch_dg(int nt, int np, const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
+  if (nt == 256 && np == 4) return launch_one<D, G, 256, 4>(prm, blocks, stream);
+  if constexpr (D == 128 && G == 4) {
+    if (nt == 256 && np == 2) return launch_one<D, G, 256, 2>(prm, blocks, stream);
+    if (nt == 256 && np == 8) return launch_one<D, G, 256, 8>(prm, blocks, stream);
+    if (nt == 512 && np == 2) return launch_one<D, G, 512, 2>(prm, blocks, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int D>
-hipError_t launch_d(int G, const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
+hipError_t launch_d(int G, int nt, int np, const DecodeParams& prm, int64_t blocks,
+                    hipStream_t stream) {
   switch (G) {
-    case 1: return launch_dg<D, 1>(prm, blocks, stream);
-    case 2: return launch_dg<D, 2>(prm, blocks, stream);
-    case 4: return launch_dg<D, 4>(prm, blocks, stream);
-    case 8: return launch_dg<D, 8>(prm, blocks, stream);
+    case 1: return launch_dg<D, 1>(nt, np, prm, blocks, stream);
+    case 2: return launch_dg<D, 2>(nt, np, prm, blocks, stream);
+    case 4: return launch_dg<D, 4>(nt, np, prm, blocks, stream);
+    case 8: return launch_dg<D, 8>(nt, np, prm, blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int decode_rows_per_pass(int head_dim) { return DEC_THREADS / (head_dim / 8); }
 int decode_max_splits() { return MAX_SPLITS; }
+
+bool decode_shape_supported(int head_dim, int group, int threads, int rows_per_thread) {
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return false;
+  if (threads == 256 && rows_per_thread == 4) return true;
+  if (head_dim == 128 && group == 4) {
+    if (threads == 256 && (rows_per_thread == 2 || rows_per_thread == 8)) return true;
+    if (threads == 512 && rows_per_thread == 2) return true;
+  }
+  return false;
+}
 
 hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeWork& work,
                          const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
@@ -477,10 +704,14 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
   prm.rows_per_split = work.rows_per_split;
   prm.scale_log2e = scale_log2e;
   const int G = geo.n_q_heads / geo.n_kv_heads;
+  if (work.nsplit < 1 || work.nsplit > MAX_SPLITS ||
+      int64_t(work.nsplit) * work.rows_per_split < geo.budget ||
+      !decode_shape_supported(geo.head_dim, G, work.threads, work.rows_per_thread))
+    return hipErrorInvalidValue;
   const int64_t blocks = static_cast<int64_t>(prm.n_heads) * work.nsplit;
-  if (geo.head_dim == 128) return launch_d<128>(G, prm, blocks, stream);
-  if (geo.head_dim == 64) return launch_d<64>(G, prm, blocks, stream);
-  return hipErrorInvalidValue;
+  if (geo.head_dim == 128)
+    return launch_d<128>(G, work.threads, work.rows_per_thread, prm, blocks, stream);
+  return launch_d<64>(G, work.threads, work.rows_per_thread, prm, blocks, stream);
 }
 
 }  // namespace kvpop

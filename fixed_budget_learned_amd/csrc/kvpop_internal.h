@@ -23,7 +23,8 @@ struct HeadCtl {
   int32_t minslot;  // slot of the least important scored token (-1: none)
   uint64_t minkey;  // its key, KEY_NONE when nscored == 0
   int32_t flags;    // KVPOP_FLAG_* bits
-  int32_t pad;
+  int32_t leave_slot;  // slot of position n + 1 - W (the next token to leave
+                       // the window); meaningful only when that is >= s
 };
 static_assert(sizeof(HeadCtl) == 32, "HeadCtl layout");
 
@@ -58,6 +59,8 @@ struct DecodeWork {
   uint32_t* tickets;   // [B*Hkv], zero between calls
   int32_t nsplit;
   int32_t rows_per_split;
+  int32_t threads;     // workgroup size of the decode kernel (256 or 512)
+  int32_t rows_per_thread;  // K/V rows one thread holds per pass (2, 4 or 8)
 };
 
 // Launchers: return hipSuccess or the launch error.  All work is enqueued
@@ -67,10 +70,10 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
 hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
                           const uint16_t* k, const uint16_t* v, const float* scores,
                           int32_t* sel, hipStream_t stream);
-// Rows one decode pass covers (a multiple of which every split spans), and
-// the largest split count the decode kernel accepts.
-int decode_rows_per_pass(int head_dim);
+// Largest split count the decode kernel accepts, and whether a launch shape
+// (head_dim, group size, workgroup size, rows per thread) is compiled.
 int decode_max_splits();
+bool decode_shape_supported(int head_dim, int group, int threads, int rows_per_thread);
 
 hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeWork& work,
                          const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,

@@ -37,6 +37,7 @@ struct PrefillShape {
   int32_t kk;      // scored slots filled: min(k, c1 - c0)
   int32_t w0;      // first window position
   int32_t count;   // s_eff + kk + (P - w0)
+  int32_t leave;   // slot of position P - W (leaves at the next step) or -1
 };
 
 __host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int32_t k, int32_t W) {
@@ -51,6 +52,9 @@ __host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int3
   r.w0 = (P - W) > s ? (P - W) : s;
   if (r.w0 > P) r.w0 = P;
   r.count = r.s_eff + r.kk + (P - r.w0);
+  // position P - W, when it is not a sink, is the oldest window token and
+  // sits in the first window slot
+  r.leave = (P - W >= s) ? r.s_eff + r.kk : -1;
   return r;
 }
 
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
     c.minslot = s_minslot;
     c.minkey = s_minkey;
     c.flags = s_nan ? 1 : 0;
-    c.pad = 0;
+    c.leave_slot = sh.leave;
     ctl[g] = c;
   }
 }
@@ -207,7 +211,7 @@ __global__ void init_ctl_kernel(HeadCtl* __restrict__ ctl, int64_t n_heads,
     c.minslot = -1;
     c.minkey = KEY_NONE;
     c.flags = 0;
-    c.pad = 0;
+    c.leave_slot = -1;
     ctl[i] = c;
   }
   if (tickets != nullptr && i < n_tickets) tickets[i] = 0u;

@@ -115,6 +115,10 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_layer_4x")
     ap.add_argument("--cpu-sample-steps", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="decode steps per pass (default: the workload's); for short profiles")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the cache path shards by sequence and KV head with no "
@@ -127,6 +131,16 @@ def main():
     from fixed_budget_learned_amd.configs import BY_NAME
     from fixed_budget_learned_amd.inputs import TokenStream
 
+    if args.copy_bytes:
+        x = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").uniform_()
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps)):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": x.numel() * 4, "copies": max(1, args.steps)}), flush=True)
+        return
+
     w = BY_NAME[args.workload]
     if w.batch != 1 or w.n_layers != 1 or w.prompt_len is None:
         print("bench.py drives one-layer, batch-1 workloads", file=sys.stderr)
@@ -134,7 +148,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     abi.load()
     dev = torch.device("cuda:0")
-    P, S = w.prompt_len, w.decode_steps
+    P, S = w.prompt_len, (args.decode_steps or w.decode_steps)
 
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -244,7 +258,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": "decode_kernel<128,4,4>",
+            "traffic_unit": "bytes per launch (FETCH_SIZE and WRITE_SIZE, copy-calibrated)",
+            "kernel": "decode_kernel (head_dim 128, 4 query heads per KV head)",
             "bytes_per_launch": bpl,
             "note": "one layer's working set (16.5 MB) fits in the 256 MB last-level cache, so "
                     "back-to-back steps can be served partly from cache",

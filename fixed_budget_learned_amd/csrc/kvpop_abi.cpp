@@ -48,17 +48,15 @@ bool config_valid(const kvpop_config* c) {
 
 // Decode launch shape.  Each KV head's slots are split over `nsplit`
 // workgroups of `threads` threads, each thread holding `rows_per_thread`
-// rows per pass.  Few heads (batch 1): about 128 workgroups in total, one
-// pass of 4 rows per thread each.  Many heads: one workgroup per head
-// streaming 2-row passes (measured fastest on MI355X for these shapes).
+// rows per pass.  About 128 workgroups in total when there are few heads
+// (batch 1); one workgroup per head when there are many.
 void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
                          int32_t* threads, int32_t* rows_per_thread) {
   const int64_t budget = int64_t(c.n_sink) + c.n_scored + c.n_recent;
   const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
   const int G = c.n_q_heads / c.n_kv_heads;
   const int nt = 256;
-  int np = 4;
-  if (heads >= 256 && kvpop::decode_shape_supported(c.head_dim, G, nt, 2)) np = 2;
+  const int np = kvpop::decode_shape_supported(c.head_dim, G, nt, 4) ? 4 : 2;
   const int64_t rpp = nt / (c.head_dim / 16);
   const int64_t chunk = rpp * np;
   int64_t ns = c.decode_splits;

@@ -90,6 +90,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -109,11 +110,77 @@ __device__ __forceinline__ bool key_less(uint64_t ka, int32_t sa, uint64_t kb, i
   return ka < kb || (ka == kb && sa < sb);
 }
 
+// Full-wavefront reductions: DPP inside each 16-lane row, then two
+// cross-row exchanges.  Results land in every lane.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
+  x = fmaxf(x, dpp_f<DPP_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<DPP_QUAD_XOR1>(x);
+  x += dpp_f<DPP_QUAD_XOR2>(x);
+  x += dpp_f<DPP_HALF_MIRROR>(x);
+  x += dpp_f<DPP_ROW_MIRROR>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row16_max(x);
+  x = fmaxf(x, __shfl_xor(x, 16, WAVE));
+  return fmaxf(x, __shfl_xor(x, 32, WAVE));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  x += __shfl_xor(x, 16, WAVE);
+  return x + __shfl_xor(x, 32, WAVE);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_min_key_step(uint64_t& key, int32_t& slot) {
+  const uint32_t lo = static_cast<uint32_t>(key), hi = static_cast<uint32_t>(key >> 32);
+  const uint32_t lo2 = __builtin_amdgcn_update_dpp(0u, lo, CTRL, 0xF, 0xF, false);
+  const uint32_t hi2 = __builtin_amdgcn_update_dpp(0u, hi, CTRL, 0xF, 0xF, false);
+  const int32_t s2 = __builtin_amdgcn_update_dpp(0, slot, CTRL, 0xF, 0xF, false);
+  const uint64_t k2 = (static_cast<uint64_t>(hi2) << 32) | lo2;
+  if (key_less(k2, s2, key, slot)) {
+    key = k2;
+    slot = s2;
+  }
+}
+
+// Lexicographic minimum of (key, slot) over each 16-lane row, in all lanes.
+__device__ __forceinline__ void row16_min_key(uint64_t& key, int32_t& slot) {
+  dpp_min_key_step<DPP_QUAD_XOR1>(key, slot);
+  dpp_min_key_step<DPP_QUAD_XOR2>(key, slot);
+  dpp_min_key_step<DPP_HALF_MIRROR>(key, slot);
+  dpp_min_key_step<DPP_ROW_MIRROR>(key, slot);
+}
+
+// ... and over the whole wavefront.
+__device__ __forceinline__ void wave_min_key_dpp(uint64_t& key, int32_t& slot) {
+  row16_min_key(key, slot);
+#pragma unroll
+  for (int m = 16; m <= 32; m *= 2) {
+    const uint64_t k2 = __shfl_xor(key, m, WAVE);
+    const int32_t s2 = __shfl_xor(slot, m, WAVE);
+    if (key_less(k2, s2, key, slot)) {
+      key = k2;
+      slot = s2;
+    }
+  }
+}
+
 // Lazy rescaling: the running max only moves when a logit exceeds it by
 // more than this many powers of two, so exponentials stay below 2^8 and the
 // accumulators are rescaled rarely.
 constexpr float RESCALE_SLACK = 8.f;
 constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
+
+// 2^x with the hardware instruction; no denormal range fix-up (results below
+// 2^-126 flush to zero, which the softmax weights tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, WAVE)); }
 
@@ -157,18 +224,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators; the
   // finishing workgroup reuses it for the split merge
   constexpr int LDS_ROWS = NWAVE * R16 * LPR * G * ACC;
-  constexpr int LDS_MERGE = 3 * MAX_SPLITS * G + TS * G * D;
+  constexpr int LDS_MERGE = MAX_SPLITS * G + TS * G * D;
+  static_assert(NWAVE * R16 <= WAVE, "key minima of the workgroup fit one wavefront");
   constexpr int LDS_F = LDS_ROWS > LDS_MERGE ? LDS_ROWS : LDS_MERGE;
 
   __shared__ __align__(16) float s_buf[LDS_F];
   __shared__ float s_wm[NWAVE][G];       // wave max (log2 units)
   __shared__ float s_wl[NWAVE][R16][G];  // per DPP-row sums of p
-  __shared__ float s_f[NWAVE][G];
-  __shared__ float s_M[G], s_L[G];
-  __shared__ uint64_t s_mk[NWAVE];
-  __shared__ int32_t s_ms[NWAVE];
+  __shared__ float s_L[G];
+  __shared__ uint64_t s_mk[NWAVE * R16];
+  __shared__ int32_t s_ms[NWAVE * R16];
   __shared__ int32_t s_last;
-
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wid = tid / WAVE;
@@ -202,21 +268,25 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   const uint4* vb = reinterpret_cast<const uint4*>(p.vc) + hrow * ROW4 + cc;
   const uint64_t* kyb = p.keys + hrow;
 
-  uint4 ka[NP][2], va[NP][2];
-  uint64_t key_c = KEY_NONE;
+  // load the K/V rows and keys of the chunk starting at slot b
+  auto load_chunk = [&](uint4 (&kk)[NP][2], uint4 (&vv)[NP][2], uint64_t& key, int32_t b) {
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int32_t r = lo + i * RPP + rg;
-    if (r < hi_alloc) {
-      ka[i][0] = kb[static_cast<int64_t>(r) * ROW4];
-      ka[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
-      va[i][0] = vb[static_cast<int64_t>(r) * ROW4];
-      va[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
-    } else {
-      ka[i][0] = ka[i][1] = va[i][0] = va[i][1] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < NP; ++i) {
+      const int32_t r = b + i * RPP + rg;
+      if (r < hi_alloc) {
+        kk[i][0] = kb[static_cast<int64_t>(r) * ROW4];
+        kk[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
+        vv[i][0] = vb[static_cast<int64_t>(r) * ROW4];
+        vv[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
+      } else {
+        kk[i][0] = kk[i][1] = vv[i][0] = vv[i][1] = make_uint4(0, 0, 0, 0);
+      }
     }
-  }
-  if (tid < CHUNK && lo + tid < hi_alloc) key_c = kyb[lo + tid];
+    key = (tid < CHUNK && b + tid < hi_alloc) ? kyb[b + tid] : KEY_NONE;
+  };
+  uint4 kA[NP][2], vA[NP][2], kB[NP][2], vB[NP][2];
+  uint64_t keyA, keyB = KEY_NONE;
+  load_chunk(kA, vA, keyA, lo);
   const uint4* knp = reinterpret_cast<const uint4*>(p.k_new) + static_cast<int64_t>(head) * ROW4 + cc;
   const uint4* vnp = reinterpret_cast<const uint4*>(p.v_new) + static_cast<int64_t>(head) * ROW4 + cc;
   const uint4 knew0 = knp[0], knew1 = knp[HALF4];
@@ -269,30 +339,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   uint64_t mk = KEY_NONE;
   int32_t msl = 0x7FFFFFFF;
 
-  for (int32_t base = lo; base < hi; base += CHUNK) {
-    const int32_t nb = base + CHUNK;
-    uint4 kn[NP][2], vn[NP][2];
-    uint64_t key_n = KEY_NONE;
-    if (nb < hi) {
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        const int32_t r = nb + i * RPP + rg;
-        if (r < hi_alloc) {
-          kn[i][0] = kb[static_cast<int64_t>(r) * ROW4];
-          kn[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
-          vn[i][0] = vb[static_cast<int64_t>(r) * ROW4];
-          vn[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
-        } else {
-          kn[i][0] = kn[i][1] = vn[i][0] = vn[i][1] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      if (tid < CHUNK && nb + tid < hi_alloc) key_n = kyb[nb + tid];
-    }
+  // one chunk: keys, logits, lazy rescale, P.V
+  auto compute_chunk = [&](uint4 (&kk)[NP][2], uint4 (&vv)[NP][2], uint64_t key, int32_t base) {
+    const bool full = base + CHUNK <= hi;  // uniform: every row of the chunk is kept
     // keys of this chunk, as they stand after this step
     {
       const int32_t r = base + tid;
       if (tid < CHUNK && r < hi) {
-        uint64_t kv = key_c;
+        uint64_t kv = key;
         if (r == newslot)
           kv = KEY_NONE;
         else if (admitted && r == st)
@@ -303,31 +357,39 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         }
       }
     }
-    // logits
+    if (newslot >= base && newslot < base + CHUNK) {  // uniform: the new token's row
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        if (base + i * RPP + rg == newslot) {
+          kk[i][0] = knew0;
+          kk[i][1] = knew1;
+          vv[i][0] = vnew0;
+          vv[i][1] = vnew1;
+        }
+    }
+    if (!full) {  // unwritten slots may hold anything: zero their V
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        if (base + i * RPP + rg >= hi) vv[i][0] = vv[i][1] = make_uint4(0, 0, 0, 0);
+    }
     float x[NP][G];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int32_t r = base + i * RPP + rg;
-      const bool valid = r < hi;
-      if (r == newslot) {
-        ka[i][0] = knew0;
-        ka[i][1] = knew1;
-        va[i][0] = vnew0;
-        va[i][1] = vnew1;
-      }
-      if (!valid) va[i][0] = va[i][1] = make_uint4(0, 0, 0, 0);  // unwritten slots
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = dot2_bf16(ka[i][0].x, qv[h][0].x, 0.f);
-        d = dot2_bf16(ka[i][0].y, qv[h][0].y, d);
-        d = dot2_bf16(ka[i][0].z, qv[h][0].z, d);
-        d = dot2_bf16(ka[i][0].w, qv[h][0].w, d);
-        d = dot2_bf16(ka[i][1].x, qv[h][1].x, d);
-        d = dot2_bf16(ka[i][1].y, qv[h][1].y, d);
-        d = dot2_bf16(ka[i][1].z, qv[h][1].z, d);
-        d = dot2_bf16(ka[i][1].w, qv[h][1].w, d);
-        d = group_sum<LPR>(d);
-        x[i][h] = valid ? d * p.scale_log2e : -INFINITY;
+        float d0 = dot2_bf16(kk[i][0].x, qv[h][0].x, 0.f);
+        float d1 = dot2_bf16(kk[i][1].x, qv[h][1].x, 0.f);
+        d0 = dot2_bf16(kk[i][0].y, qv[h][0].y, d0);
+        d1 = dot2_bf16(kk[i][1].y, qv[h][1].y, d1);
+        d0 = dot2_bf16(kk[i][0].z, qv[h][0].z, d0);
+        d1 = dot2_bf16(kk[i][1].z, qv[h][1].z, d1);
+        d0 = dot2_bf16(kk[i][0].w, qv[h][0].w, d0);
+        d1 = dot2_bf16(kk[i][1].w, qv[h][1].w, d1);
+        x[i][h] = group_sum<LPR>(d0 + d1) * p.scale_log2e;
+      }
+      if (!full && base + i * RPP + rg >= hi) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) x[i][h] = -INFINITY;
       }
     }
     // lazy rescale: the wave-shared running max moves only when needed
@@ -338,7 +400,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
       for (int i = 1; i < NP; ++i) mx = fmaxf(mx, x[i][h]);
       if (__any(mx > m_run[h] + RESCALE_SLACK)) {
         const float mnew = fmaxf(m_run[h], wave_max_groups<LPR>(mx));
-        const float alpha = exp2f(m_run[h] - mnew);  // 0 while m_run is -inf
+        const float alpha = fast_exp2(m_run[h] - mnew);  // 0 while m_run is -inf
         l_run[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < ACC; ++e) acc[h][e] *= alpha;
@@ -352,14 +414,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float ms = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
-        float2_t pf = {exp2f(x[i][h] - ms), exp2f(x[i + 1][h] - ms)};
+        float2_t pf = {fast_exp2(x[i][h] - ms), fast_exp2(x[i + 1][h] - ms)};
         ph[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2v_t));
         l_run[h] = dot2_bf16(ph[h], BF16_ONE_PAIR, l_run[h]);
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const uint32_t a[4] = {va[i][hf].x, va[i][hf].y, va[i][hf].z, va[i][hf].w};
-        const uint32_t b[4] = {va[i + 1][hf].x, va[i + 1][hf].y, va[i + 1][hf].z, va[i + 1][hf].w};
+        const uint32_t a[4] = {vv[i][hf].x, vv[i][hf].y, vv[i][hf].z, vv[i][hf].w};
+        const uint32_t b[4] = {vv[i + 1][hf].x, vv[i + 1][hf].y, vv[i + 1][hf].z, vv[i + 1][hf].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t lo2 = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
@@ -372,29 +434,30 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         }
       }
     }
-    if (nb < hi) {
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        ka[i][0] = kn[i][0];
-        ka[i][1] = kn[i][1];
-        va[i][0] = vn[i][0];
-        va[i][1] = vn[i][1];
-      }
-      key_c = key_n;
-    }
+  };
+
+  // ping-pong over chunks: load the next chunk while computing this one
+  for (int32_t base = lo; base < hi;) {
+    if (base + CHUNK < hi) load_chunk(kB, vB, keyB, base + CHUNK);
+    compute_chunk(kA, vA, keyA, base);
+    base += CHUNK;
+    if (base >= hi) break;
+    if (base + CHUNK < hi) load_chunk(kA, vA, keyA, base + CHUNK);
+    compute_chunk(kB, vB, keyB, base);
+    base += CHUNK;
   }
 
-  // ---- minimum key of the workgroup ---------------------------------------
-  wave_min_key(mk, msl);
-  if (lane == 0) {
-    s_mk[wid] = mk;
-    s_ms[wid] = msl;
-  }
-
-  // ---- merge the row groups: DPP within each 16-lane row, LDS across ------
-  // All row groups of a wave share m_run, so their partial sums add plainly.
+  // ---- merge the row groups of the workgroup -----------------------------
+  // Key minimum: DPP inside each 16-lane row, one LDS entry per row.
   const int r16 = lane / 16;
-  const bool writer = (lane % 16) < LPR;       // first row group of the DPP row
+  row16_min_key(mk, msl);
+  if (lane % 16 == 0) {
+    s_mk[wid * R16 + r16] = mk;
+    s_ms[wid * R16 + r16] = msl;
+  }
+  // Accumulators: all row groups of a wave share m_run, so they add plainly;
+  // DPP sums the groups of each 16-lane row, LDS takes one copy per row.
+  const bool writer = (lane % 16) < LPR;  // first row group of the DPP row
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float lsum = row16_sum_groups<LPR>(l_run[h]);
@@ -412,55 +475,54 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         dst[(h * ACC + e) / 4] = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
   }
   __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_wm[w][tid]);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
-    for (int w = 0; w < NWAVE; ++w) {
-      const float f = exp2f(s_wm[w][tid] - Ms);
-      s_f[w][tid] = f;
-      float lw = 0.f;
-      for (int r = 0; r < R16; ++r) lw += s_wl[w][r][tid];
-      L = fmaf(lw, f, L);
-    }
-    s_M[tid] = M;
-    s_L[tid] = L;
-  }
-  __syncthreads();
   const int64_t pidx = static_cast<int64_t>(head) * p.nsplit + split;
-  for (int e = tid; e < G * D; e += NT) {
-    const int h = e / D;
-    const int d = e % D;
-    const int cl = (d % (D / 2)) / 8;                  // lane in group holding d
-    const int j = (d / (D / 2)) * 8 + d % 8;           // its accumulator index
-    float a = 0.f;
+  // Each thread forms 4 consecutive outputs (same lane slot, same head):
+  // element d of head h sits at lane (d mod D/2)/8, accumulator 8*(2d/D) + d%8.
+  for (int o4 = tid; o4 < Q4; o4 += NT) {
+    const int h = (o4 * 4) / D;
+    const int d = (o4 * 4) % D;
+    const int cl = (d % (D / 2)) / 8;
+    const int j = (d / (D / 2)) * 8 + d % 8;
+    float M = s_wm[0][h];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, s_wm[w][h]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) {
-      float aw = 0.f;
+      const float f = fast_exp2(s_wm[w][h] - Ms);
 #pragma unroll
-      for (int r = 0; r < R16; ++r) aw += s_buf[(((w * R16 + r) * LPR + cl) * G + h) * ACC + j];
-      a = fmaf(aw, s_f[w][h], a);
-    }
-    p.part_acc[pidx * (G * D) + e] = a;
-  }
-  if (tid < G) {
-    reinterpret_cast<float2*>(p.part_ml)[pidx * G + tid] = make_float2(s_M[tid], s_L[tid]);
-  }
-  if (tid == 0) {
-    uint64_t k0 = s_mk[0];
-    int32_t sl0 = s_ms[0];
-    for (int w = 1; w < NWAVE; ++w)
-      if (key_less(s_mk[w], s_ms[w], k0, sl0)) {
-        k0 = s_mk[w];
-        sl0 = s_ms[w];
+      for (int r = 0; r < R16; ++r) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            &s_buf[(((w * R16 + r) * LPR + cl) * G + h) * ACC + j]);
+        a.x = fmaf(v.x, f, a.x);
+        a.y = fmaf(v.y, f, a.y);
+        a.z = fmaf(v.z, f, a.z);
+        a.w = fmaf(v.w, f, a.w);
+        L = fmaf(s_wl[w][r][h], f, L);
       }
-    MinPart mp;
-    mp.key = k0;
-    mp.slot = sl0;
-    mp.pad = 0;
-    p.part_min[pidx] = mp;
+    }
+    reinterpret_cast<float4*>(p.part_acc)[pidx * Q4 + o4] = a;
+    if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
   }
+  if (wid == 0) {
+    uint64_t k0 = KEY_NONE;
+    int32_t sl0 = 0x7FFFFFFF;
+    if (lane < NWAVE * R16) {
+      k0 = s_mk[lane];
+      sl0 = s_ms[lane];
+    }
+    wave_min_key_dpp(k0, sl0);
+    if (lane == 0) {
+      MinPart mp;
+      mp.key = k0;
+      mp.slot = sl0;
+      mp.pad = 0;
+      p.part_min[pidx] = mp;
+    }
+  }
+
   // ---- ticket: the last workgroup of the head finishes the step ----------
   // Every thread's stores complete, then one device-scope release (an L2
   // writeback) covers the whole workgroup before the ticket is taken.
@@ -476,31 +538,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // ---- merge the splits: every load issued before the first wait ---------
+  // ---- merge the splits ----------------------------------------------------
+  // Wave h (and h + NWAVE, ...) reduces head h's split maxima and sums with
+  // one split per lane; the accumulator loads are issued first so that their
+  // latency overlaps the reductions.
   const int ns = p.nsplit;
   const int64_t p0 = static_cast<int64_t>(head) * ns;
-  float* s_pm = s_buf;                        // [ns][G] partial max
-  float* s_pl = s_buf + MAX_SPLITS * G;       // [ns][G] partial sum
-  float* s_pf = s_buf + 2 * MAX_SPLITS * G;   // [ns][G] rescale factor
-  float* s_red = s_buf + 3 * MAX_SPLITS * G;  // [TS][G*D] per-thread-group sums
-  float2 ml_r[(MAX_SPLITS * G + NT - 1) / NT];
-#pragma unroll
-  for (int u = 0; u < (MAX_SPLITS * G + NT - 1) / NT; ++u) {
-    const int i = tid + u * NT;
-    ml_r[u] = (i < ns * G) ? reinterpret_cast<const float2*>(p.part_ml)[p0 * G + i]
-                           : make_float2(-INFINITY, 0.f);
-  }
-  MinPart mp_r[(MAX_SPLITS + NT - 1) / NT];
-#pragma unroll
-  for (int u = 0; u < (MAX_SPLITS + NT - 1) / NT; ++u) {
-    const int i = tid + u * NT;
-    if (i < ns) {
-      mp_r[u] = p.part_min[p0 + i];
-    } else {
-      mp_r[u].key = KEY_NONE;
-      mp_r[u].slot = 0x7FFFFFFF;
-    }
-  }
+  float* s_pf = s_buf;                         // [ns][G] rescale factor
+  float* s_red = s_buf + MAX_SPLITS * G;       // [TS][G*D] per-thread-group sums
   const int j4 = tid % Q4;
   const int s0 = tid / Q4;
   const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc);
@@ -510,43 +555,48 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     const int sp = s0 + u * TS;
     raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  const float2* pml2 = reinterpret_cast<const float2*>(p.part_ml);
+  for (int h = wid; h < G; h += NWAVE) {
+    constexpr int SPL = MAX_SPLITS / WAVE;  // splits per lane
+    float2 ml[SPL];
 #pragma unroll
-  for (int u = 0; u < (MAX_SPLITS * G + NT - 1) / NT; ++u) {
-    const int i = tid + u * NT;
-    if (i < ns * G) {
-      s_pm[i] = ml_r[u].x;
-      s_pl[i] = ml_r[u].y;
+    for (int u = 0; u < SPL; ++u) {
+      const int sp = lane + u * WAVE;
+      ml[u] = (sp < ns) ? pml2[(p0 + sp) * G + h] : make_float2(-INFINITY, 0.f);
     }
+    float M = ml[0].x;
+#pragma unroll
+    for (int u = 1; u < SPL; ++u) M = fmaxf(M, ml[u].x);
+    M = wave_max(M);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int sp = lane + u * WAVE;
+      const float f = fast_exp2(ml[u].x - Ms);
+      if (sp < ns) s_pf[sp * G + h] = f;
+      L = fmaf(ml[u].y, f, L);
+    }
+    L = wave_sum(L);
+    if (lane == 0) s_L[h] = L;
   }
   {
-    uint64_t k0 = mp_r[0].key;
-    int32_t sl0 = mp_r[0].slot;
-#pragma unroll
-    for (int u = 1; u < (MAX_SPLITS + NT - 1) / NT; ++u)
-      if (key_less(mp_r[u].key, mp_r[u].slot, k0, sl0)) {
-        k0 = mp_r[u].key;
-        sl0 = mp_r[u].slot;
+    uint64_t k0 = KEY_NONE;
+    int32_t sl0 = 0x7FFFFFFF;
+    for (int sp = tid; sp < ns; sp += NT) {
+      const MinPart mp = p.part_min[p0 + sp];
+      if (key_less(mp.key, mp.slot, k0, sl0)) {
+        k0 = mp.key;
+        sl0 = mp.slot;
       }
-    wave_min_key(k0, sl0);
-    if (lane == 0) {
-      s_mk[wid] = k0;
-      s_ms[wid] = sl0;
+    }
+    row16_min_key(k0, sl0);
+    if (lane % 16 == 0) {
+      s_mk[wid * R16 + r16] = k0;
+      s_ms[wid * R16 + r16] = sl0;
     }
   }
   __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_pm[sp * G + tid]);
-    s_M[tid] = (M == -INFINITY) ? 0.f : M;
-  }
-  __syncthreads();
-  for (int i = tid; i < ns * G; i += NT) s_pf[i] = exp2f(s_pm[i] - s_M[i % G]);
-  __syncthreads();
-  if (tid < G) {
-    float L = 0.f;
-    for (int sp = 0; sp < ns; ++sp) L = fmaf(s_pl[sp * G + tid], s_pf[sp * G + tid], L);
-    s_L[tid] = L;
-  }
   const int hq = (j4 * 4) / D;
   float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -574,10 +624,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
       a4.w = fmaf(raw[u].w, f, a4.w);
     }
   }
-  reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
-  __syncthreads();
+  if (TS > 1) reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
+  if (TS > 1) __syncthreads();
   if (s0 == 0) {
-    float4 o = reinterpret_cast<const float4*>(s_red)[j4];
+    float4 o = a4;
     for (int ts = 1; ts < TS; ++ts) {
       const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
       o.x += y.x;
@@ -601,29 +651,31 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     vw[0] = vnew0;
     vw[HALF4] = vnew1;
   }
-  if (tid == 0) {
-    uint64_t k0 = s_mk[0];
-    int32_t sl0 = s_ms[0];
-    for (int w = 1; w < NWAVE; ++w)
-      if (key_less(s_mk[w], s_ms[w], k0, sl0)) {
-        k0 = s_mk[w];
-        sl0 = s_ms[w];
-      }
-    if (admitted) p.keys[hrow + st] = keyt;
-    p.keys[hrow + newslot] = KEY_NONE;
-    p.pos[hrow + newslot] = n;
-    if (n >= p.n_sink) p.ring[static_cast<int64_t>(head) * W + (n % W)] = newslot;
-    HeadCtl nc;
-    nc.n = n;
-    nc.count = count_new;
-    nc.nscored = nscored_new;
-    nc.minslot = (k0 == KEY_NONE) ? -1 : sl0;
-    nc.minkey = k0;
-    nc.flags = flags;
-    // with a one-token window the next leaving token is the one just added
-    nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? newslot : ring_next);
-    p.ctl[head] = nc;
-    p.tickets[head] = 0u;
+  if (wid == 0) {
+    uint64_t k0 = KEY_NONE;
+    int32_t sl0 = 0x7FFFFFFF;
+    if (lane < NWAVE * R16) {
+      k0 = s_mk[lane];
+      sl0 = s_ms[lane];
+    }
+    wave_min_key_dpp(k0, sl0);
+    if (lane == 0) {
+      if (admitted) p.keys[hrow + st] = keyt;
+      p.keys[hrow + newslot] = KEY_NONE;
+      p.pos[hrow + newslot] = n;
+      if (n >= p.n_sink) p.ring[static_cast<int64_t>(head) * W + (n % W)] = newslot;
+      HeadCtl nc;
+      nc.n = n;
+      nc.count = count_new;
+      nc.nscored = nscored_new;
+      nc.minslot = (k0 == KEY_NONE) ? -1 : sl0;
+      nc.minkey = k0;
+      nc.flags = flags;
+      // with a one-token window the next leaving token is the one just added
+      nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? newslot : ring_next);
+      p.ctl[head] = nc;
+      p.tickets[head] = 0u;
+    }
   }
 }
 
@@ -634,15 +686,17 @@ hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t strea
   return hipGetLastError();
 }
 
-// Compiled launch shapes: (256 threads, 4 rows per thread) for every head
-// size and group; the Qwen3 shape (D 128, G 4) also gets 2 or 8 rows per
-// thread, and 512-thread workgroups with 2.
+// Compiled launch shapes: 256 threads with 2 rows per thread for every head
+// size and group (the register budget of double-buffered chunks); groups of
+// up to 2 query heads also get 4 rows per thread, and the Qwen3 shape
+// (D 128, G 4) gets 512-thread workgroups.
 template <int D, int G>
 hipError_t launch_dg(int nt, int np, const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
-  if (nt == 256 && np == 4) return launch_one<D, G, 256, 4>(prm, blocks, stream);
+  if (nt == 256 && np == 2) return launch_one<D, G, 256, 2>(prm, blocks, stream);
+  if constexpr (G <= 2) {
+    if (nt == 256 && np == 4) return launch_one<D, G, 256, 4>(prm, blocks, stream);
+  }
   if constexpr (D == 128 && G == 4) {
-    if (nt == 256 && np == 2) return launch_one<D, G, 256, 2>(prm, blocks, stream);
-    if (nt == 256 && np == 8) return launch_one<D, G, 256, 8>(prm, blocks, stream);
     if (nt == 512 && np == 2) return launch_one<D, G, 512, 2>(prm, blocks, stream);
   }
   return hipErrorInvalidValue;
@@ -667,11 +721,9 @@ int decode_max_splits() { return MAX_SPLITS; }
 bool decode_shape_supported(int head_dim, int group, int threads, int rows_per_thread) {
   if (head_dim != 64 && head_dim != 128) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8) return false;
-  if (threads == 256 && rows_per_thread == 4) return true;
-  if (head_dim == 128 && group == 4) {
-    if (threads == 256 && (rows_per_thread == 2 || rows_per_thread == 8)) return true;
-    if (threads == 512 && rows_per_thread == 2) return true;
-  }
+  if (threads == 256 && rows_per_thread == 2) return true;
+  if (threads == 256 && rows_per_thread == 4 && group <= 2) return true;
+  if (threads == 512 && rows_per_thread == 2 && head_dim == 128 && group == 4) return true;
   return false;
 }
 

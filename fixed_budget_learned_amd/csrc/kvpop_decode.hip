@@ -221,9 +221,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   static_assert(Q4 <= NT, "merge needs one thread per float4");
   constexpr int TS = NT / Q4;            // merge threads per float4 column
   constexpr int MB = 16;                 // merge loads in flight per thread
-  // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators; the
-  // finishing workgroup reuses it for the split merge
-  constexpr int LDS_ROWS = NWAVE * R16 * LPR * G * ACC;
+  // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators, each
+  // block padded by 8 floats so that neighbouring lanes' blocks start in
+  // different LDS banks; the finishing workgroup reuses it for the split merge
+  constexpr int ACC_STRIDE = G * ACC + 8;
+  constexpr int LDS_ROWS = NWAVE * R16 * LPR * ACC_STRIDE;
   constexpr int LDS_MERGE = MAX_SPLITS * G + TS * G * D;
   static_assert(NWAVE * R16 <= WAVE, "key minima of the workgroup fit one wavefront");
   constexpr int LDS_F = LDS_ROWS > LDS_MERGE ? LDS_ROWS : LDS_MERGE;
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     for (int e = 0; e < ACC; ++e) acc[h][e] = row16_sum_groups<LPR>(acc[h][e]);
   }
   if (writer) {
-    float4* dst = reinterpret_cast<float4*>(&s_buf[(((wid * R16 + r16) * LPR + cc) * G) * ACC]);
+    float4* dst = reinterpret_cast<float4*>(&s_buf[((wid * R16 + r16) * LPR + cc) * ACC_STRIDE]);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < R16; ++r) {
         const float4 v = *reinterpret_cast<const float4*>(
-            &s_buf[(((w * R16 + r) * LPR + cl) * G + h) * ACC + j]);
+            &s_buf[((w * R16 + r) * LPR + cl) * ACC_STRIDE + h * ACC + j]);
         a.x = fmaf(v.x, f, a.x);
         a.y = fmaf(v.y, f, a.y);
         a.z = fmaf(v.z, f, a.z);

@@ -8,12 +8,15 @@
 // token leaves it, per the card's "Delayed scoring").
 //
 // Two kernels per call:
-//   select  one 1024-thread workgroup per KV head.  A 4 x 8-bit radix select
-//           over the order-preserving score codes finds the threshold code
-//           and how many tokens carrying it survive; a tiled ordered scan
-//           then keeps every code above the threshold and the newest of the
-//           tied ones, and writes the kept positions in ascending order plus
-//           the head's control block (count, min key and its slot).
+//   select  one 1024-thread workgroup per KV head; each thread owns a
+//           contiguous block of candidate positions (kept in registers when
+//           it is at most 32 long).  A 4 x 8-bit radix select over the
+//           order-preserving score codes (one LDS histogram per wave) finds
+//           the threshold code and how many tokens carrying it survive; one
+//           workgroup scan of per-thread (greater, equal) counts then places
+//           every code above the threshold and the newest of the tied ones,
+//           writing the kept positions in ascending order plus the head's
+//           control block (count, min key and its slot).
 //   gather  many 256-thread workgroups per head copy the kept K/V rows into
 //           slots [0, count) with 16-byte coalesced loads/stores and write
 //           per-slot position and key, and the window ring.
@@ -58,87 +61,139 @@ __host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int3
   return r;
 }
 
+// Candidate scores of one head, seen by thread `tid` as the contiguous block
+// of positions [c0 + tid*L, c0 + (tid+1)*L) clipped to [c0, c1).  With VPT > 0
+// the block (L <= VPT) is loaded once into registers as order codes; with
+// VPT == 0 it is re-read from memory (through the caches) on every pass.
+template <int VPT>
+struct CandBlock {
+  uint32_t code[VPT > 0 ? VPT : 1];
+  const float* sc;
+  int32_t lo, hi;  // this thread's positions [lo, hi)
+
+  __device__ __forceinline__ void init(const float* scores, const PrefillShape& sh, int32_t L,
+                                       int tid, bool* saw_nan) {
+    sc = scores;
+    lo = min(sh.c0 + tid * L, sh.c1);
+    hi = min(lo + L, sh.c1);
+    bool nan = false;
+    if constexpr (VPT > 0) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int32_t i = lo + j;
+        const float x = (i < hi) ? sc[i] : 0.f;
+        nan |= (i < hi) && score_is_nan(x);
+        code[j] = score_code(x);
+      }
+    } else {
+      for (int32_t i = lo; i < hi; ++i) nan |= score_is_nan(sc[i]);
+    }
+    *saw_nan = nan;
+  }
+
+  // f(position, code) for every candidate of the block, in ascending order.
+  template <typename F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    if constexpr (VPT > 0) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if (lo + j < hi) f(lo + j, code[j]);
+    } else {
+      constexpr int U = 8;  // loads in flight per batch
+      for (int32_t b = lo; b < hi; b += U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = (b + u < hi) ? sc[b + u] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (b + u < hi) f(b + u, score_code(x[u]));
+      }
+    }
+  }
+};
+
+template <int VPT>
 __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
     const float* __restrict__ scores, PrefillShape sh, int32_t k, int32_t* __restrict__ sel,
     HeadCtl* __restrict__ ctl) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_buf[SEL_THREADS / WAVE + 1];
-  __shared__ uint32_t s_bin, s_above, s_nan;
+  constexpr int NWAVE = SEL_THREADS / WAVE;
+  __shared__ uint32_t whist[NWAVE][256];  // one histogram per wave: less atomic contention
+  __shared__ uint32_t scan_buf[NWAVE + 1];
+  __shared__ uint32_t s_bin, s_above, s_nan, s_neq;
   __shared__ int32_t s_minslot;
   __shared__ uint64_t s_minkey;
 
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
-  const float* sc = scores + static_cast<int64_t>(g) * sh.P;
+  const int wid = tid / WAVE;
   int32_t* out = sel + static_cast<int64_t>(g) * (k > 0 ? k : 1);
+  const int32_t C = sh.c1 - sh.c0;
+  const int32_t L = (C + SEL_THREADS - 1) / SEL_THREADS;
 
   if (tid == 0) {
     s_nan = 0;
     s_minslot = -1;
     s_minkey = KEY_NONE;
   }
+  CandBlock<VPT> blk;
+  bool saw_nan = false;
+  if (sh.kk > 0) blk.init(scores + static_cast<int64_t>(g) * sh.P, sh, L, tid, &saw_nan);
   __syncthreads();
+  if (saw_nan) s_nan = 1;
 
-  uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
-  uint32_t n_eq = 0;
   if (sh.kk > 0) {
-    // ---- radix select of the kk-th largest code ---------------------------
+    // ---- radix select of the kk-th largest code, 8 bits at a time --------
+    uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
     for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
+      for (int i = tid; i < NWAVE * 256; i += SEL_THREADS) (&whist[0][0])[i] = 0;
       __syncthreads();
-      bool saw_nan = false;
-      for (int32_t i = sh.c0 + tid; i < sh.c1; i += SEL_THREADS) {
-        float x = sc[i];
-        saw_nan |= score_is_nan(x);
-        uint32_t o = score_code(x);
-        if ((o & mask) == prefix) atomicAdd(&hist[(o >> shift) & 255u], 1u);
+      blk.for_each([&](int32_t, uint32_t o) {
+        if ((o & mask) == prefix) atomicAdd(&whist[wid][(o >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      // bins from the top: thread t < 256 holds bin 255 - t
+      uint32_t h = 0;
+      if (tid < 256) {
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) h += whist[w][255 - tid];
       }
-      if (shift == 24 && saw_nan) s_nan = 1;
-      __syncthreads();
-      // Bins from the top: thread t holds bin 255 - t.
-      uint32_t h = tid < 256 ? hist[255 - tid] : 0u;
       uint32_t tot;
-      uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>(h, scan_buf, &tot);
+      const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>(h, scan_buf, &tot);
       if (tid < 256 && ex < krem && krem <= ex + h) {
         s_bin = 255u - tid;
         s_above = ex;
+        s_neq = h;
       }
       __syncthreads();
-      const uint32_t bin = s_bin;
       krem -= s_above;
-      prefix |= bin << shift;
+      prefix |= s_bin << shift;
       mask |= 0xFFu << shift;
-      if (shift == 0) n_eq = hist[bin];
-      __syncthreads();
     }
-    // ---- ordered compaction: codes > prefix, then the newest krem ties ----
+    // ---- ordered compaction: codes above the threshold, then the newest
+    // krem tokens carrying it (ties: the older ones lose) --------------------
     const uint32_t thr = prefix;
-    const uint32_t drop = n_eq - krem;  // oldest ties that lose
-    uint32_t run_gt = 0, run_eq = 0;
-    for (int32_t base = sh.c0; base < sh.c1; base += SEL_THREADS) {
-      const int32_t i = base + tid;
-      uint32_t gt = 0, eq = 0;
-      if (i < sh.c1) {
-        uint32_t o = score_code(sc[i]);
-        gt = o > thr;
-        eq = o == thr;
-      }
-      uint32_t tot;
-      uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
-      const uint32_t eq_before = run_eq + (ex >> 16);
-      const uint32_t gt_before = run_gt + (ex & 0xFFFFu);
-      if (gt || (eq && eq_before >= drop)) {
-        const uint32_t kept_ties_before = eq_before > drop ? eq_before - drop : 0u;
-        const uint32_t idx = gt_before + kept_ties_before;
+    const uint32_t drop = s_neq - krem;
+    uint32_t gt = 0, eq = 0;
+    blk.for_each([&](int32_t, uint32_t o) {
+      gt += o > thr;
+      eq += o == thr;
+    });
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
+    uint32_t eq_before = ex >> 16, gt_before = ex & 0xFFFFu;
+    blk.for_each([&](int32_t i, uint32_t o) {
+      const bool is_gt = o > thr, is_eq = o == thr;
+      if (is_gt || (is_eq && eq_before >= drop)) {
+        const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
         out[idx] = i;
-        if (eq && eq_before == drop) {  // the least important kept token
+        if (is_eq && eq_before == drop) {  // the least important kept token
           s_minslot = sh.s_eff + static_cast<int32_t>(idx);
           s_minkey = make_key(thr, i);
         }
       }
-      run_eq += tot >> 16;
-      run_gt += tot & 0xFFFFu;
-    }
+      gt_before += is_gt;
+      eq_before += is_eq;
+    });
   }
   __syncthreads();
   if (tid == 0) {
@@ -178,24 +233,47 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(
   const int32_t* selg = sel + static_cast<int64_t>(g) * kcap;
   const float* scg = scores + static_cast<int64_t>(g) * sh.P;
 
-  for (int32_t r = r0 + rg; r < r1; r += RPP) {
-    int32_t p;
-    bool scored = false;
-    if (r < sh.s_eff) {
-      p = r;
-    } else if (r < sh.s_eff + sh.kk) {
-      p = selg[r - sh.s_eff];
-      scored = true;
-    } else {
-      p = sh.w0 + (r - sh.s_eff - sh.kk);
+  constexpr int RPT = 4;  // rows per thread per batch: loads issued before stores
+  for (int32_t rb = r0 + rg; rb < r1; rb += RPT * RPP) {
+    int32_t pos_r[RPT];
+    bool scored_r[RPT];
+    uint4 kr[RPT], vr[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int32_t r = rb + u * RPP;
+      int32_t p = 0;
+      bool scored = false;
+      if (r < r1) {
+        if (r < sh.s_eff) {
+          p = r;
+        } else if (r < sh.s_eff + sh.kk) {
+          p = selg[r - sh.s_eff];
+          scored = true;
+        } else {
+          p = sh.w0 + (r - sh.s_eff - sh.kk);
+        }
+        kr[u] = ksrc[static_cast<int64_t>(p) * LPR + c];
+        vr[u] = vsrc[static_cast<int64_t>(p) * LPR + c];
+      }
+      pos_r[u] = p;
+      scored_r[u] = scored;
     }
-    kdst[static_cast<int64_t>(r) * LPR + c] = ksrc[static_cast<int64_t>(p) * LPR + c];
-    vdst[static_cast<int64_t>(r) * LPR + c] = vsrc[static_cast<int64_t>(p) * LPR + c];
-    if (c == 0) {
-      const int64_t hs = static_cast<int64_t>(g) * budget + r;
-      pos[hs] = p;
-      keys[hs] = scored ? make_key(score_code(scg[p]), p) : KEY_NONE;
-      if (!scored && r >= sh.s_eff) ring[static_cast<int64_t>(g) * W + (p % W)] = r;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int32_t r = rb + u * RPP;
+      if (r < r1) {
+        kdst[static_cast<int64_t>(r) * LPR + c] = kr[u];
+        vdst[static_cast<int64_t>(r) * LPR + c] = vr[u];
+        if (c == 0) {
+          const int64_t hs = static_cast<int64_t>(g) * budget + r;
+          const int32_t p = pos_r[u];
+          pos[hs] = p;
+          keys[hs] = scored_r[u] ? make_key(score_code(scg[p]), p) : KEY_NONE;
+          if (!scored_r[u] && r >= sh.s_eff) ring[static_cast<int64_t>(g) * W + (p % W)] = r;
+        }
+      }
     }
   }
 }
@@ -236,8 +314,16 @@ hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq,
   const PrefillShape sh = prefill_shape(n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
   const int64_t head0 = static_cast<int64_t>(seq) * geo.n_kv_heads;
   const int32_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
-  hipLaunchKernelGGL(prefill_select_kernel, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0, stream,
-                     scores, sh, geo.n_scored, sel, lv.ctl + head0);
+  const int32_t per_thread = (sh.c1 - sh.c0 + SEL_THREADS - 1) / SEL_THREADS;
+  if (per_thread <= 16)
+    hipLaunchKernelGGL(prefill_select_kernel<16>, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0,
+                       stream, scores, sh, geo.n_scored, sel, lv.ctl + head0);
+  else if (per_thread <= 32)
+    hipLaunchKernelGGL(prefill_select_kernel<32>, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0,
+                       stream, scores, sh, geo.n_scored, sel, lv.ctl + head0);
+  else
+    hipLaunchKernelGGL(prefill_select_kernel<0>, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0,
+                       stream, scores, sh, geo.n_scored, sel, lv.ctl + head0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sh.count == 0) return hipSuccess;

@@ -106,6 +106,82 @@ def cpu_baseline(w, sample_steps: int):
     }
 
 
+def dense_vs_kvpop(contexts, steps: int, reps: int):
+    """Decode time per step of the fixed-budget cache against a cache that
+    never evicts (dense attention over all n tokens), at growing context.
+
+    Both use the Qwen3-8B layer shape at batch 1 and the same kernels; the
+    dense cache is the special case whose scored region holds every token.
+    Inputs: seeded device-side N(0,1) K/V/q and scores.
+    """
+    import torch
+    from fixed_budget_learned_amd import abi
+    from fixed_budget_learned_amd.configs import QWEN3_8B_LAYER_4X as w
+    D, Hq, Hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260706)
+    rows = []
+    for P in contexts:
+        T = P + steps
+        k = torch.randn((Hkv, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+        v = torch.randn((Hkv, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+        sc = torch.randn((Hkv, T), generator=gen, device="cuda")
+        q = torch.randn((steps, 1, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+        kn = k[:, P:].transpose(0, 1).contiguous().view(steps, 1, Hkv, D)
+        vn = v[:, P:].transpose(0, 1).contiguous().view(steps, 1, Hkv, D)
+        sl = sc[:, P - w.n_recent:T - w.n_recent].transpose(0, 1).contiguous().view(steps, 1, Hkv)
+        pk, pv, ps = k[:, :P].contiguous(), v[:, :P].contiguous(), sc[:, :P].contiguous()
+        out = torch.empty((steps, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
+        res = {"context": P}
+        for mode in ("kvpop", "dense"):
+            n_scored = w.n_scored if mode == "kvpop" else T
+            cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, n_scored, w.n_recent,
+                                                   max_positions=T))
+            budget = w.n_sink + n_scored + w.n_recent
+
+            def pre():
+                cache.reset(0, 0)
+                cache.prefill_compact(0, 0, pk, pv, ps)
+
+            def dec():
+                for i in range(steps):
+                    cache.decode_step(0, q[i], kn[i], vn[i], sl[i], out[i])
+
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                pre()
+                dec()
+            torch.cuda.synchronize()
+            gp, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gp, stream=stream):
+                pre()
+            with torch.cuda.graph(gd, stream=stream):
+                dec()
+            ms = 0.0
+            for r in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    gp.replay()
+                    e0.record(stream)
+                    gd.replay()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                if r > 0:
+                    ms += e0.elapsed_time(e1)
+            us = ms * 1e3 / (reps * steps)
+            kept = min(budget, P + steps // 2)
+            nbytes = Hkv * kept * D * 4 + Hq * D * 4 + Hkv * D * 4
+            res[f"{mode}_us_per_step"] = us
+            res[f"{mode}_GBps"] = nbytes / (us * 1e-6) / 1e9
+            cache.close()
+            del gp, gd
+        res["dense_over_kvpop"] = res["dense_us_per_step"] / res["kvpop_us_per_step"]
+        rows.append(res)
+        del k, v, sc, q, kn, vn, sl, pk, pv, ps, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +193,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="decode steps per pass (default: the workload's); for short profiles")
+    ap.add_argument("--no-dense-sweep", action="store_true",
+                    help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -266,6 +344,8 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    if not args.no_dense_sweep:
+        result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_steps)
     print(json.dumps(result), flush=True)

@@ -49,7 +49,9 @@ bool config_valid(const kvpop_config* c) {
 // Decode launch shape.  Each KV head's slots are split over `nsplit`
 // workgroups of `threads` threads, each thread holding `rows_per_thread`
 // rows per pass.  About 128 workgroups in total when there are few heads
-// (batch 1); one workgroup per head when there are many.
+// (batch 1); one workgroup per head when there are many; long budgets (a
+// cache that never evicts) are cut into ~2,048-slot pieces up to ~512
+// workgroups.
 void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
                          int32_t* threads, int32_t* rows_per_thread) {
   const int64_t budget = int64_t(c.n_sink) + c.n_scored + c.n_recent;
@@ -61,8 +63,11 @@ void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_p
   const int64_t chunk = rpp * np;
   int64_t ns = c.decode_splits;
   if (ns == 0) {
-    const int64_t target = 128;  // workgroups in flight
-    ns = (target + heads - 1) / heads;
+    // at least ~128 workgroups in total; long slot ranges are cut into
+    // pieces of ~2,048 slots while the grid stays within ~512 workgroups
+    const int64_t ns_par = (128 + heads - 1) / heads;
+    const int64_t ns_len = std::min((512 + heads - 1) / heads, (budget + 2047) / 2048);
+    ns = std::max(ns_par, ns_len);
     const int64_t cap = std::max<int64_t>(1, (budget + chunk - 1) / chunk);
     ns = std::min<int64_t>(std::max<int64_t>(ns, 1), cap);
     ns = std::min<int64_t>(ns, kvpop::decode_max_splits());

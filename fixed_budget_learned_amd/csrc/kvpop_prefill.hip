@@ -141,7 +141,37 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
   __syncthreads();
   if (saw_nan) s_nan = 1;
 
-  if (sh.kk > 0) {
+  if (sh.kk > 0 && sh.kk == C) {
+    // ---- every candidate is kept: positions in order, and the least
+    // important one is the smallest (code, position) -------------------------
+    uint64_t mk = KEY_NONE;
+    int32_t mpos = 0x7FFFFFFF;
+    blk.for_each([&](int32_t i, uint32_t o) {
+      out[i - sh.c0] = i;
+      const uint64_t key = make_key(o, i);
+      if (key < mk) {
+        mk = key;
+        mpos = i;
+      }
+    });
+    wave_min_key(mk, mpos);
+    __shared__ uint64_t s_wmk[NWAVE];
+    __shared__ int32_t s_wmp[NWAVE];
+    if ((tid & (WAVE - 1)) == 0) {
+      s_wmk[wid] = mk;
+      s_wmp[wid] = mpos;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NWAVE; ++w)
+        if (s_wmk[w] < mk) {
+          mk = s_wmk[w];
+          mpos = s_wmp[w];
+        }
+      s_minkey = mk;
+      s_minslot = sh.s_eff + (mpos - sh.c0);
+    }
+  } else if (sh.kk > 0) {
     // ---- radix select of the kk-th largest code, 8 bits at a time --------
     uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
     for (int shift = 24; shift >= 0; shift -= 8) {

@@ -17,7 +17,7 @@ from fixed_budget_learned_amd import abi
 from fixed_budget_learned_amd.configs import (BATCH64_SERVING, LONG_131K_8X, QWEN3_8B_36L_4X,
                                               QWEN3_8B_LAYER_4X, TINY)
 from fixed_budget_learned_amd.inputs import TokenStream, prompt_lengths
-from oracle import KVpopOracle, kept_by_definition
+from oracle import KVpopOracle, bf16_to_f64, kept_by_definition
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,9 @@ CASES = [
     ("odd_splits", Geo(8, 2, 128, 4, 500, 64), [3000, 700], 40, "ties", 7),
     ("big_budget_multi_chunk", Geo(32, 8, 128, 4, 6000, 256), [9000], 30, "normal", 0),
     ("gqa8_d128", Geo(64, 8, 128, 4, 200, 32), [1000], 30, "normal", 0),
+    # a scored region that can hold every candidate never evicts: dense attention
+    ("dense_no_eviction", Geo(8, 2, 128, 4, 10000, 32), [3000, 57, 0], 40, "normal", 0),
+    ("dense_prompt_fills_region_exactly", Geo(8, 2, 128, 4, 200, 16), [220], 30, "ties", 0),
 ]
 
 
@@ -276,6 +279,44 @@ def test_batched_serving_b64():
         if b % 8 == 7:
             log(f"  oracle checked sequences 0..{b}")
     log("  batched ok")
+
+
+@pytest.mark.timeout(600)
+def test_dense_131k_context():
+    """Dense decode (no eviction) over a 131,072-token prompt: every token is
+    kept, so the output is plain softmax attention over all positions."""
+    P, steps, Hq, Hkv, D, W = 131072, 12, 32, 8, 128, 256
+    geo = Geo(Hq, Hkv, D, 4, P + steps, W)
+    rng = np.random.default_rng(131072)
+    from fixed_budget_learned_amd.inputs import bf16_bits_rne
+    T = P + steps
+    K = bf16_bits_rne(rng.standard_normal((Hkv, T, D), dtype=np.float32))
+    V = bf16_bits_rne(rng.standard_normal((Hkv, T, D), dtype=np.float32))
+    Q = bf16_bits_rne(rng.standard_normal((steps, Hq, D), dtype=np.float32))
+    S = rng.standard_normal((Hkv, T), dtype=np.float32)
+    cache = make_cache(geo, max_positions=T)
+    cache.prefill_compact(0, 0, to_dev_bf16(K[:, :P]), to_dev_bf16(V[:, :P]), to_dev_f32(S[:, :P]))
+    out = torch.empty((1, Hq, D), dtype=torch.bfloat16, device="cuda")
+    outs = []
+    for i in range(steps):
+        n = P + i
+        cache.decode_step(0, to_dev_bf16(Q[i][None]), to_dev_bf16(K[:, n][None]),
+                          to_dev_bf16(V[:, n][None]), to_dev_f32(S[:, n - W][None]), out)
+        outs.append(out_to_f64(out)[0])
+    st = cache.state(0, 0)
+    cache.close()
+    assert st.n == T - 1
+    for g in range(Hkv):
+        assert st.kept[g].tolist() == list(range(T))
+    from oracle import softmax_attention
+    import math
+    Kf, Vf = bf16_to_f64(K), bf16_to_f64(V)
+    for i in (0, steps - 1):
+        n = P + i
+        q = bf16_to_f64(Q[i])
+        ref = np.stack([softmax_attention(q[h], Kf[h // 4, :n + 1], Vf[h // 4, :n + 1], 1 / math.sqrt(D))
+                        for h in range(Hq)])
+        check_output(outs[i], ref, f"dense step {i}")
 
 
 # ---------------------------------------------------------------------------

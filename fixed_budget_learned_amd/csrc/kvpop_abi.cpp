@@ -47,30 +47,25 @@ bool config_valid(const kvpop_config* c) {
 }
 
 // Decode launch shape.  Each KV head's slots are split over `nsplit`
-// workgroups of `threads` threads, each thread holding `rows_per_thread`
-// rows per pass.  About 128 workgroups in total when there are few heads
-// (batch 1); one workgroup per head when there are many; long budgets (a
-// cache that never evicts) are cut into ~2,048-slot pieces up to ~512
-// workgroups.
+// workgroups of 256 threads, each thread holding 2 rows per pass.  With 256
+// or more heads (batched serving) each head is one workgroup: the step needs
+// no cross-workgroup merge at all.  With fewer heads the splits fill the
+// 256 compute units once (one workgroup per unit): more workgroups than
+// units would have the first ones publish their partial results, with a
+// device-scope release, while the others still stream K/V, and the release
+// then stalls the stream.  Every split keeps at least 128 slots.
 void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
                          int32_t* threads, int32_t* rows_per_thread) {
   const int64_t budget = int64_t(c.n_sink) + c.n_scored + c.n_recent;
   const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
-  const int G = c.n_q_heads / c.n_kv_heads;
-  const int nt = 256;
-  const int np = kvpop::decode_shape_supported(c.head_dim, G, nt, 4) ? 4 : 2;
+  const int nt = 256, np = 2;
   const int64_t rpp = nt / (c.head_dim / 16);
-  const int64_t chunk = rpp * np;
   int64_t ns = c.decode_splits;
   if (ns == 0) {
-    // at least ~128 workgroups in total; long slot ranges are cut into
-    // pieces of ~2,048 slots while the grid stays within ~512 workgroups
-    const int64_t ns_par = (128 + heads - 1) / heads;
-    const int64_t ns_len = std::min((512 + heads - 1) / heads, (budget + 2047) / 2048);
-    ns = std::max(ns_par, ns_len);
-    const int64_t cap = std::max<int64_t>(1, (budget + chunk - 1) / chunk);
-    ns = std::min<int64_t>(std::max<int64_t>(ns, 1), cap);
+    ns = std::max<int64_t>(1, 256 / heads);
+    ns = std::min<int64_t>(ns, (budget + 127) / 128);
     ns = std::min<int64_t>(ns, kvpop::decode_max_splits());
+    ns = std::max<int64_t>(ns, 1);
   }
   int64_t rows = (budget + ns - 1) / ns;
   rows = (rows + rpp - 1) / rpp * rpp;

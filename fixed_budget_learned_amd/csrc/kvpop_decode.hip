@@ -206,13 +206,17 @@ __device__ __forceinline__ float row16_sum_groups(float x) {
   return x;
 }
 
-template <int D, int G, int NT, int NP>
-__global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
-  static_assert(NP % 2 == 0, "rows are consumed in pairs");
+// One workgroup of 256 threads per (KV head, split).  K/V rows stream
+// through registers in chunks of 2 rows per thread, double-buffered: the
+// loads of the next chunk are in flight while the current one is computed.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  constexpr int NT = 256;
+  constexpr int NP = 2;                  // rows per thread per chunk
   constexpr int LPR = D / 16;            // lanes per row; 2 x 16 bytes each
   constexpr int HALF4 = D / 16;          // uint4 offset of the second half
   constexpr int RPP = NT / LPR;          // rows per pass
-  constexpr int CHUNK = NP * RPP;        // rows per double-buffered chunk
+  constexpr int CHUNK = NP * RPP;        // rows per chunk
   static_assert(CHUNK <= NT, "one key per thread per chunk");
   constexpr int NWAVE = NT / WAVE;
   constexpr int R16 = WAVE / 16;         // 16-lane DPP rows per wavefront
@@ -270,24 +274,25 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   const uint4* vb = reinterpret_cast<const uint4*>(p.vc) + hrow * ROW4 + cc;
   const uint64_t* kyb = p.keys + hrow;
 
-  // load the K/V rows and keys of the chunk starting at slot b
+  // Load the K/V rows and keys of the chunk starting at slot b.  The loads
+  // are unconditional (rows past the slot range read slot 0, and compute
+  // masks them), so every chunk issues the same number of loads and the
+  // compiler can wait for one chunk while the next is still in flight.
   auto load_chunk = [&](uint4 (&kk)[NP][2], uint4 (&vv)[NP][2], uint64_t& key, int32_t b) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int32_t r = b + i * RPP + rg;
-      if (r < hi_alloc) {
-        kk[i][0] = kb[static_cast<int64_t>(r) * ROW4];
-        kk[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
-        vv[i][0] = vb[static_cast<int64_t>(r) * ROW4];
-        vv[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
-      } else {
-        kk[i][0] = kk[i][1] = vv[i][0] = vv[i][1] = make_uint4(0, 0, 0, 0);
-      }
+      int32_t r = b + i * RPP + rg;
+      if (r >= hi_alloc) r = 0;
+      kk[i][0] = kb[static_cast<int64_t>(r) * ROW4];
+      kk[i][1] = kb[static_cast<int64_t>(r) * ROW4 + HALF4];
+      vv[i][0] = vb[static_cast<int64_t>(r) * ROW4];
+      vv[i][1] = vb[static_cast<int64_t>(r) * ROW4 + HALF4];
     }
-    key = (tid < CHUNK && b + tid < hi_alloc) ? kyb[b + tid] : KEY_NONE;
+    const int32_t rk = b + tid % CHUNK;
+    key = kyb[rk < hi_alloc ? rk : 0];  // used by threads tid < CHUNK only
   };
   uint4 kA[NP][2], vA[NP][2], kB[NP][2], vB[NP][2];
-  uint64_t keyA, keyB = KEY_NONE;
+  uint64_t keyA, keyB;
   load_chunk(kA, vA, keyA, lo);
   const uint4* knp = reinterpret_cast<const uint4*>(p.k_new) + static_cast<int64_t>(head) * ROW4 + cc;
   const uint4* vnp = reinterpret_cast<const uint4*>(p.v_new) + static_cast<int64_t>(head) * ROW4 + cc;
@@ -439,12 +444,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   };
 
   // ping-pong over chunks: load the next chunk while computing this one
+  // (also after the last one, so that the load count never depends on the
+  // path taken)
   for (int32_t base = lo; base < hi;) {
-    if (base + CHUNK < hi) load_chunk(kB, vB, keyB, base + CHUNK);
+    load_chunk(kB, vB, keyB, base + CHUNK);
     compute_chunk(kA, vA, keyA, base);
     base += CHUNK;
     if (base >= hi) break;
-    if (base + CHUNK < hi) load_chunk(kA, vA, keyA, base + CHUNK);
+    load_chunk(kA, vA, keyA, base + CHUNK);
     compute_chunk(kB, vB, keyB, base);
     base += CHUNK;
   }
@@ -478,6 +485,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   }
   __syncthreads();
   const int64_t pidx = static_cast<int64_t>(head) * p.nsplit + split;
+  const bool single = (p.nsplit == 1);  // uniform
   // Each thread forms 4 consecutive outputs (same lane slot, same head):
   // element d of head h sits at lane (d mod D/2)/8, accumulator 8*(2d/D) + d%8.
   for (int o4 = tid; o4 < Q4; o4 += NT) {
@@ -505,143 +513,155 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         L = fmaf(s_wl[w][r][h], f, L);
       }
     }
-    reinterpret_cast<float4*>(p.part_acc)[pidx * Q4 + o4] = a;
-    if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
-  }
-  if (wid == 0) {
-    uint64_t k0 = KEY_NONE;
-    int32_t sl0 = 0x7FFFFFFF;
-    if (lane < NWAVE * R16) {
-      k0 = s_mk[lane];
-      sl0 = s_ms[lane];
-    }
-    wave_min_key_dpp(k0, sl0);
-    if (lane == 0) {
-      MinPart mp;
-      mp.key = k0;
-      mp.slot = sl0;
-      mp.pad = 0;
-      p.part_min[pidx] = mp;
+    if (single) {  // the only split: normalise and store the output row
+      const float invL = 1.f / L;
+      const uint32_t b0 = f32_to_bf16_rne(a.x * invL), b1 = f32_to_bf16_rne(a.y * invL);
+      const uint32_t b2 = f32_to_bf16_rne(a.z * invL), b3 = f32_to_bf16_rne(a.w * invL);
+      reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + o4] =
+          make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    } else {
+      reinterpret_cast<float4*>(p.part_acc)[pidx * Q4 + o4] = a;
+      if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
     }
   }
-
-  // ---- ticket: the last workgroup of the head finishes the step ----------
-  // Every thread's stores complete, then one device-scope release (an L2
-  // writeback) covers the whole workgroup before the ticket is taken.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev =
-        __hip_atomic_fetch_add(&p.tickets[head], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // ---- merge the splits ----------------------------------------------------
-  // Wave h (and h + NWAVE, ...) reduces head h's split maxima and sums with
-  // one split per lane; the accumulator loads are issued first so that their
-  // latency overlaps the reductions.
-  const int ns = p.nsplit;
-  const int64_t p0 = static_cast<int64_t>(head) * ns;
-  float* s_pf = s_buf;                         // [ns][G] rescale factor
-  float* s_red = s_buf + MAX_SPLITS * G;       // [TS][G*D] per-thread-group sums
-  const int j4 = tid % Q4;
-  const int s0 = tid / Q4;
-  const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc);
-  float4 raw[MB];
-#pragma unroll
-  for (int u = 0; u < MB; ++u) {
-    const int sp = s0 + u * TS;
-    raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float2* pml2 = reinterpret_cast<const float2*>(p.part_ml);
-  for (int h = wid; h < G; h += NWAVE) {
-    constexpr int SPL = MAX_SPLITS / WAVE;  // splits per lane
-    float2 ml[SPL];
-#pragma unroll
-    for (int u = 0; u < SPL; ++u) {
-      const int sp = lane + u * WAVE;
-      ml[u] = (sp < ns) ? pml2[(p0 + sp) * G + h] : make_float2(-INFINITY, 0.f);
-    }
-    float M = ml[0].x;
-#pragma unroll
-    for (int u = 1; u < SPL; ++u) M = fmaxf(M, ml[u].x);
-    M = wave_max(M);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
-#pragma unroll
-    for (int u = 0; u < SPL; ++u) {
-      const int sp = lane + u * WAVE;
-      const float f = fast_exp2(ml[u].x - Ms);
-      if (sp < ns) s_pf[sp * G + h] = f;
-      L = fmaf(ml[u].y, f, L);
-    }
-    L = wave_sum(L);
-    if (lane == 0) s_L[h] = L;
-  }
-  {
-    uint64_t k0 = KEY_NONE;
-    int32_t sl0 = 0x7FFFFFFF;
-    for (int sp = tid; sp < ns; sp += NT) {
-      const MinPart mp = p.part_min[p0 + sp];
-      if (key_less(mp.key, mp.slot, k0, sl0)) {
-        k0 = mp.key;
-        sl0 = mp.slot;
+  // Several splits: publish the partial results; the last workgroup of the
+  // head to finish merges them.  A single split is complete already.
+  if (!single) {
+    if (wid == 0) {
+      uint64_t k0 = KEY_NONE;
+      int32_t sl0 = 0x7FFFFFFF;
+      if (lane < NWAVE * R16) {
+        k0 = s_mk[lane];
+        sl0 = s_ms[lane];
+      }
+      wave_min_key_dpp(k0, sl0);
+      if (lane == 0) {
+        MinPart mp;
+        mp.key = k0;
+        mp.slot = sl0;
+        mp.pad = 0;
+        p.part_min[pidx] = mp;
       }
     }
-    row16_min_key(k0, sl0);
-    if (lane % 16 == 0) {
-      s_mk[wid * R16 + r16] = k0;
-      s_ms[wid * R16 + r16] = sl0;
+
+    // ---- ticket: the last workgroup of the head finishes the step ----------
+    // Every thread's stores complete, then one device-scope release (an L2
+    // writeback) covers the whole workgroup before the ticket is taken.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&p.tickets[head], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
     }
-  }
-  __syncthreads();
-  const int hq = (j4 * 4) / D;
-  float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int u = 0; u < MB; ++u) {
-    const int sp = s0 + u * TS;
-    const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
-    a4.x = fmaf(raw[u].x, f, a4.x);
-    a4.y = fmaf(raw[u].y, f, a4.y);
-    a4.z = fmaf(raw[u].z, f, a4.z);
-    a4.w = fmaf(raw[u].w, f, a4.w);
-  }
-  for (int sb = s0 + MB * TS; sb < ns; sb += MB * TS) {  // more than MB*TS splits
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    // ---- merge the splits ----------------------------------------------------
+    // Wave h (and h + NWAVE, ...) reduces head h's split maxima and sums with
+    // one split per lane; the accumulator loads are issued first so that their
+    // latency overlaps the reductions.
+    const int ns = p.nsplit;
+    const int64_t p0 = static_cast<int64_t>(head) * ns;
+    float* s_pf = s_buf;                     // [ns][G] rescale factor
+    float* s_red = s_buf + MAX_SPLITS * G;   // [TS][G*D] per-thread-group sums
+    const int j4 = tid % Q4;
+    const int s0 = tid / Q4;
+    const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc);
+    float4 raw[MB];
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
-      const int sp = sb + u * TS;
+      const int sp = s0 + u * TS;
       raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const float2* pml2 = reinterpret_cast<const float2*>(p.part_ml);
+    for (int h = wid; h < G; h += NWAVE) {
+      constexpr int SPL = MAX_SPLITS / WAVE;  // splits per lane
+      float2 ml[SPL];
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        const int sp = lane + u * WAVE;
+        ml[u] = (sp < ns) ? pml2[(p0 + sp) * G + h] : make_float2(-INFINITY, 0.f);
+      }
+      float M = ml[0].x;
+#pragma unroll
+      for (int u = 1; u < SPL; ++u) M = fmaxf(M, ml[u].x);
+      M = wave_max(M);
+      const float Ms = (M == -INFINITY) ? 0.f : M;
+      float L = 0.f;
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        const int sp = lane + u * WAVE;
+        const float f = fast_exp2(ml[u].x - Ms);
+        if (sp < ns) s_pf[sp * G + h] = f;
+        L = fmaf(ml[u].y, f, L);
+      }
+      L = wave_sum(L);
+      if (lane == 0) s_L[h] = L;
+    }
+    {
+      uint64_t k0 = KEY_NONE;
+      int32_t sl0 = 0x7FFFFFFF;
+      for (int sp = tid; sp < ns; sp += NT) {
+        const MinPart mp = p.part_min[p0 + sp];
+        if (key_less(mp.key, mp.slot, k0, sl0)) {
+          k0 = mp.key;
+          sl0 = mp.slot;
+        }
+      }
+      row16_min_key(k0, sl0);
+      if (lane % 16 == 0) {
+        s_mk[wid * R16 + r16] = k0;
+        s_ms[wid * R16 + r16] = sl0;
+      }
+    }
+    __syncthreads();
+    const int hq = (j4 * 4) / D;
+    float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
-      const int sp = sb + u * TS;
+      const int sp = s0 + u * TS;
       const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
       a4.x = fmaf(raw[u].x, f, a4.x);
       a4.y = fmaf(raw[u].y, f, a4.y);
       a4.z = fmaf(raw[u].z, f, a4.z);
       a4.w = fmaf(raw[u].w, f, a4.w);
     }
-  }
-  if (TS > 1) reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
-  if (TS > 1) __syncthreads();
-  if (s0 == 0) {
-    float4 o = a4;
-    for (int ts = 1; ts < TS; ++ts) {
-      const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
-      o.x += y.x;
-      o.y += y.y;
-      o.z += y.z;
-      o.w += y.w;
+    for (int sb = s0 + MB * TS; sb < ns; sb += MB * TS) {  // more than MB*TS splits
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const int sp = sb + u * TS;
+        raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const int sp = sb + u * TS;
+        const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
+        a4.x = fmaf(raw[u].x, f, a4.x);
+        a4.y = fmaf(raw[u].y, f, a4.y);
+        a4.z = fmaf(raw[u].z, f, a4.z);
+        a4.w = fmaf(raw[u].w, f, a4.w);
+      }
     }
-    const float invL = 1.f / s_L[hq];
-    const uint32_t b0 = f32_to_bf16_rne(o.x * invL), b1 = f32_to_bf16_rne(o.y * invL);
-    const uint32_t b2 = f32_to_bf16_rne(o.z * invL), b3 = f32_to_bf16_rne(o.w * invL);
-    reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + j4] =
-        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    if (TS > 1) reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
+    if (TS > 1) __syncthreads();
+    if (s0 == 0) {
+      float4 o = a4;
+      for (int ts = 1; ts < TS; ++ts) {
+        const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
+        o.x += y.x;
+        o.y += y.y;
+        o.z += y.z;
+        o.w += y.w;
+      }
+      const float invL = 1.f / s_L[hq];
+      const uint32_t b0 = f32_to_bf16_rne(o.x * invL), b1 = f32_to_bf16_rne(o.y * invL);
+      const uint32_t b2 = f32_to_bf16_rne(o.z * invL), b3 = f32_to_bf16_rne(o.w * invL);
+      reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + j4] =
+          make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
   }
 
   // ---- cache update: new row, slot metadata, window ring, control block --
@@ -681,37 +701,20 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int G, int NT, int NP>
+template <int D, int G>
 hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G, NT, NP>), dim3(static_cast<uint32_t>(blocks)), dim3(NT),
-                     0, stream, prm);
+  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, prm);
   return hipGetLastError();
 }
 
-// Compiled launch shapes: 256 threads with 2 rows per thread for every head
-// size and group (the register budget of double-buffered chunks); groups of
-// up to 2 query heads also get 4 rows per thread, and the Qwen3 shape
-// (D 128, G 4) gets 512-thread workgroups.
-template <int D, int G>
-hipError_t launch_dg(int nt, int np, const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
-  if (nt == 256 && np == 2) return launch_one<D, G, 256, 2>(prm, blocks, stream);
-  if constexpr (G <= 2) {
-    if (nt == 256 && np == 4) return launch_one<D, G, 256, 4>(prm, blocks, stream);
-  }
-  if constexpr (D == 128 && G == 4) {
-    if (nt == 512 && np == 2) return launch_one<D, G, 512, 2>(prm, blocks, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
 template <int D>
-hipError_t launch_d(int G, int nt, int np, const DecodeParams& prm, int64_t blocks,
-                    hipStream_t stream) {
+hipError_t launch_d(int G, const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_dg<D, 1>(nt, np, prm, blocks, stream);
-    case 2: return launch_dg<D, 2>(nt, np, prm, blocks, stream);
-    case 4: return launch_dg<D, 4>(nt, np, prm, blocks, stream);
-    case 8: return launch_dg<D, 8>(nt, np, prm, blocks, stream);
+    case 1: return launch_one<D, 1>(prm, blocks, stream);
+    case 2: return launch_one<D, 2>(prm, blocks, stream);
+    case 4: return launch_one<D, 4>(prm, blocks, stream);
+    case 8: return launch_one<D, 8>(prm, blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -723,10 +726,7 @@ int decode_max_splits() { return MAX_SPLITS; }
 bool decode_shape_supported(int head_dim, int group, int threads, int rows_per_thread) {
   if (head_dim != 64 && head_dim != 128) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8) return false;
-  if (threads == 256 && rows_per_thread == 2) return true;
-  if (threads == 256 && rows_per_thread == 4 && group <= 2) return true;
-  if (threads == 512 && rows_per_thread == 2 && head_dim == 128 && group == 4) return true;
-  return false;
+  return threads == 256 && rows_per_thread == 2;
 }
 
 hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeWork& work,
@@ -763,9 +763,8 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
       !decode_shape_supported(geo.head_dim, G, work.threads, work.rows_per_thread))
     return hipErrorInvalidValue;
   const int64_t blocks = static_cast<int64_t>(prm.n_heads) * work.nsplit;
-  if (geo.head_dim == 128)
-    return launch_d<128>(G, work.threads, work.rows_per_thread, prm, blocks, stream);
-  return launch_d<64>(G, work.threads, work.rows_per_thread, prm, blocks, stream);
+  if (geo.head_dim == 128) return launch_d<128>(G, prm, blocks, stream);
+  return launch_d<64>(G, prm, blocks, stream);
 }
 
 }  // namespace kvpop

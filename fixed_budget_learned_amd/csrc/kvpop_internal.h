@@ -59,8 +59,8 @@ struct DecodeWork {
   uint32_t* tickets;   // [B*Hkv], zero between calls
   int32_t nsplit;
   int32_t rows_per_split;
-  int32_t threads;     // workgroup size of the decode kernel (256 or 512)
-  int32_t rows_per_thread;  // K/V rows one thread holds per pass (2, 4 or 8)
+  int32_t threads;     // workgroup size of the decode kernel (256)
+  int32_t rows_per_thread;  // K/V rows one thread holds per pass (2)
 };
 
 // Launchers: return hipSuccess or the launch error.  All work is enqueued

@@ -126,6 +126,12 @@ CASES = [
     # a scored region that can hold every candidate never evicts: dense attention
     ("dense_no_eviction", Geo(8, 2, 128, 4, 10000, 32), [3000, 57, 0], 40, "normal", 0),
     ("dense_prompt_fills_region_exactly", Geo(8, 2, 128, 4, 200, 16), [220], 30, "ties", 0),
+    # 256 KV heads in all: one workgroup per head, no cross-workgroup merge
+    ("auto_single_split_256_heads", Geo(2, 2, 64, 4, 40, 16),
+     [(37 * i) % 300 for i in range(128)], 30, "ties", 0),
+    # slot ranges rounded up to whole passes leave the last split empty
+    ("empty_last_split", Geo(4, 1, 128, 4, 64, 32), [150, 20], 40, "normal", 3),
+    ("single_split_g8_d64", Geo(16, 2, 64, 4, 700, 64), [2000, 90], 30, "normal", 1),
 ]
 
 

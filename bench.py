@@ -182,6 +182,93 @@ def dense_vs_kvpop(contexts, steps: int, reps: int):
     return rows
 
 
+def batched_serving(steps: int, reps: int):
+    """Batched serving: 64 sequences of the Qwen3-8B layer shape with 4,032
+    slots per KV head, prompts uniform in [4096, 32768] (seeded), scores
+    lognormal quantised to 256 levels.  One decode launch serves all 64
+    sequences.  Prefill (reset + compaction of every prompt) and decode are
+    captured as HIP graphs and replayed; K/V/q are seeded device-side N(0,1).
+    """
+    import numpy as np
+    import torch
+    from fixed_budget_learned_amd import abi
+    from fixed_budget_learned_amd.configs import BATCH64_SERVING as w
+    from fixed_budget_learned_amd.inputs import T_SCORES, draw_scores, prompt_lengths, rng_for
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    lens = [int(x) for x in prompt_lengths(w)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + w.wid)
+    pk, pv, ps = [], [], []
+    for b, P in enumerate(lens):
+        pk.append(torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16))
+        pv.append(torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16))
+        ps.append(torch.from_numpy(draw_scores(rng_for(w.wid, 0, b, T_SCORES), w.score_dist,
+                                               (Hkv, P))).to("cuda"))
+    q = torch.randn((steps, B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    kn = torch.randn((steps, B, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((steps, B, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+    # leaving-token scores of the decode steps: a stream of its own (seq index B)
+    sl = torch.from_numpy(draw_scores(rng_for(w.wid, 0, B, T_SCORES), w.score_dist,
+                                      (steps, B, Hkv))).to("cuda")
+    out = torch.empty((steps, B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    cache = abi.KVpopCache(abi.make_config(1, B, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
+                                           max_positions=max(lens) + steps + 1))
+
+    def pre():
+        for b in range(B):
+            cache.reset(0, b)
+            cache.prefill_compact(0, b, pk[b], pv[b], ps[b])
+
+    def dec():
+        for i in range(steps):
+            cache.decode_step(0, q[i], kn[i], vn[i], sl[i], out[i])
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        pre()
+        dec()
+    torch.cuda.synchronize()
+    gp, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gp, stream=stream):
+        pre()
+    with torch.cuda.graph(gd, stream=stream):
+        dec()
+    pre_ms = dec_ms = 0.0
+    for r in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        with torch.cuda.stream(stream):
+            e[0].record(stream)
+            gp.replay()
+            e[1].record(stream)
+            gd.replay()
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            pre_ms += e[0].elapsed_time(e[1])
+            dec_ms += e[1].elapsed_time(e[2])
+    counts = cache.state(0, B - 1).counts
+    assert all(int(c) == w.budget for c in counts), "batched caches not full"
+    cache.close()
+    us = dec_ms * 1e3 / (reps * steps)
+    bpl = decode_bytes_per_launch(w, w.budget)
+    gbps = bpl / (us * 1e-6) / 1e9
+    ptok = sum(lens)
+    pbytes = sum(prefill_bytes(w, P) for P in lens)
+    pre_s = pre_ms / 1e3 / reps
+    return {
+        "workload": w.name, "batch": B, "budget": w.budget,
+        "prompt_tokens": ptok, "decode_steps_timed": steps * reps,
+        "decode_us_per_step": us, "decode_steps_per_s": 1e6 / us,
+        "decode_tokens_per_s": B * 1e6 / us,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "bytes_per_launch": bpl,
+                     "kernel": "decode_kernel (head_dim 128, 4 query heads per KV head)"},
+        "prefill_tokens_per_s": ptok / pre_s,
+        "prefill_GBps": pbytes / pre_s / 1e9,
+        "prefill_frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBPS,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +280,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="decode steps per pass (default: the workload's); for short profiles")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batch-64 serving measurement")
     ap.add_argument("--no-dense-sweep", action="store_true",
                     help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -344,6 +433,8 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    if not args.no_batched:
+        result["batched_serving"] = batched_serving(64, 3)
     if not args.no_dense_sweep:
         result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
     if not args.no_cpu_baseline:

@@ -61,102 +61,133 @@ __host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int3
   return r;
 }
 
-// Candidate scores of one head, seen by thread `tid` as the contiguous block
-// of positions [c0 + tid*L, c0 + (tid+1)*L) clipped to [c0, c1).  With VPT > 0
-// the block (L <= VPT) is loaded once into registers as order codes; with
-// VPT == 0 it is re-read from memory (through the caches) on every pass.
-template <int VPT>
-struct CandBlock {
-  uint32_t code[VPT > 0 ? VPT : 1];
-  const float* sc;
-  int32_t lo, hi;  // this thread's positions [lo, hi)
+constexpr int NBINS = 4096;  // radix digits of 12, 12 and 8 bits over the 32-bit code
+constexpr int TILE_LG = 5;   // streamed compaction: tiles of 32 candidates per thread
 
-  __device__ __forceinline__ void init(const float* scores, const PrefillShape& sh, int32_t L,
-                                       int tid, bool* saw_nan) {
-    sc = scores;
-    lo = min(sh.c0 + tid * L, sh.c1);
-    hi = min(lo + L, sh.c1);
-    bool nan = false;
-    if constexpr (VPT > 0) {
+// Coalesced load of candidates [0, n) at `sc` into LDS as order codes, laid
+// out thread-contiguously: candidate i belongs to thread i >> lg, entry
+// i & (2^lg - 1), stored at (i >> lg) * (2^lg + 1) + (i & (2^lg - 1)); the pad
+// word keeps the 64 lanes of a wave in distinct banks when each then reads
+// its own block.  Returns whether this thread saw a NaN.
+__device__ __forceinline__ bool stage_codes(const float* __restrict__ sc, int32_t n, int lg,
+                                            uint32_t* stage) {
+  const int32_t L = 1 << lg;
+  bool nan = false;
+  constexpr int U = 8;  // loads in flight per thread
+  for (int32_t i0 = threadIdx.x; i0 < n; i0 += SEL_THREADS * U) {
+    float x[U];
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const int32_t i = lo + j;
-        const float x = (i < hi) ? sc[i] : 0.f;
-        nan |= (i < hi) && score_is_nan(x);
-        code[j] = score_code(x);
-      }
-    } else {
-      for (int32_t i = lo; i < hi; ++i) nan |= score_is_nan(sc[i]);
-    }
-    *saw_nan = nan;
-  }
-
-  // f(position, code) for every candidate of the block, in ascending order.
-  template <typename F>
-  __device__ __forceinline__ void for_each(F&& f) const {
-    if constexpr (VPT > 0) {
+    for (int u = 0; u < U; ++u) x[u] = sc[min(i0 + u * SEL_THREADS, n - 1)];
 #pragma unroll
-      for (int j = 0; j < VPT; ++j)
-        if (lo + j < hi) f(lo + j, code[j]);
-    } else {
-      constexpr int U = 8;  // loads in flight per batch
-      for (int32_t b = lo; b < hi; b += U) {
-        float x[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = (b + u < hi) ? sc[b + u] : 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (b + u < hi) f(b + u, score_code(x[u]));
+    for (int u = 0; u < U; ++u) {
+      const int32_t i = i0 + u * SEL_THREADS;
+      if (i < n) {
+        nan |= score_is_nan(x[u]);
+        stage[(i >> lg) * (L + 1) + (i & (L - 1))] = score_code(x[u]);
       }
     }
   }
-};
+  return nan;
+}
 
+// f(code) for every candidate [0, n) at `sc`, read with coalesced loads (the
+// order of the calls is unspecified).  With check_nan, *nan collects NaNs.
+template <typename F>
+__device__ __forceinline__ void stream_codes(const float* __restrict__ sc, int32_t n, bool check_nan,
+                                             bool* nan, F&& f) {
+  constexpr int U = 8;
+  for (int32_t i0 = threadIdx.x; i0 < n; i0 += SEL_THREADS * U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = sc[min(i0 + u * SEL_THREADS, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * SEL_THREADS < n) {
+        if (check_nan) *nan |= score_is_nan(x[u]);
+        f(score_code(x[u]));
+      }
+    }
+  }
+}
+
+// One radix pass over the codes that match `prefix` under `mask`: histogram
+// of the digit (code >> shift) & (nbins - 1), then the bin that holds the
+// krem-th largest matching code.  Results land in *s_bin, *s_above (matching
+// codes in higher bins) and *s_neq (codes in the bin).  All threads call it.
+template <typename Visit>
+__device__ __forceinline__ void radix_pass(Visit&& visit, uint32_t prefix, uint32_t mask, int shift,
+                                           int nbins, uint32_t krem, uint32_t* hist,
+                                           uint32_t* scan_buf, uint32_t* s_bin, uint32_t* s_above,
+                                           uint32_t* s_neq) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nbins; i += SEL_THREADS) hist[i] = 0;
+  __syncthreads();
+  visit([&](uint32_t o) {
+    if ((o & mask) == prefix) atomicAdd(&hist[(o >> shift) & static_cast<uint32_t>(nbins - 1)], 1u);
+  });
+  __syncthreads();
+  // thread t holds bins nbins-1-4t down to nbins-4-4t
+  uint32_t hb[4], h = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bin = nbins - 1 - 4 * tid - q;
+    hb[q] = bin >= 0 ? hist[bin] : 0u;
+    h += hb[q];
+  }
+  uint32_t tot;
+  uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>(h, scan_buf, &tot);
+  if (ex < krem && krem <= ex + h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (krem <= ex + hb[q]) {
+        *s_bin = static_cast<uint32_t>(nbins - 1 - 4 * tid - q);
+        *s_above = ex;
+        *s_neq = hb[q];
+        break;
+      }
+      ex += hb[q];
+    }
+  }
+  __syncthreads();
+}
+
+// Select kernel: one 1024-thread workgroup per KV head.  VPT 16 / 32: every
+// thread holds a contiguous block of at most VPT candidate codes in
+// registers (staged through LDS from coalesced loads); VPT 0: longer prompts
+// stream the scores (through the caches) on every pass and compact them in
+// tiles of 32 candidates per thread.
 template <int VPT>
 __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
     const float* __restrict__ scores, PrefillShape sh, int32_t k, int32_t* __restrict__ sel,
     HeadCtl* __restrict__ ctl) {
   constexpr int NWAVE = SEL_THREADS / WAVE;
-  __shared__ uint32_t whist[NWAVE][256];  // one histogram per wave: less atomic contention
+  constexpr int LMAX = VPT > 0 ? VPT : (1 << TILE_LG);
+  __shared__ uint32_t hist[NBINS];
+  __shared__ uint32_t stage[SEL_THREADS * (LMAX + 1)];
   __shared__ uint32_t scan_buf[NWAVE + 1];
   __shared__ uint32_t s_bin, s_above, s_nan, s_neq;
   __shared__ int32_t s_minslot;
   __shared__ uint64_t s_minkey;
+  __shared__ uint64_t s_wmk[NWAVE];
+  __shared__ int32_t s_wmp[NWAVE];
 
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int wid = tid / WAVE;
   int32_t* out = sel + static_cast<int64_t>(g) * (k > 0 ? k : 1);
   const int32_t C = sh.c1 - sh.c0;
-  const int32_t L = (C + SEL_THREADS - 1) / SEL_THREADS;
+  const float* sc = scores + static_cast<int64_t>(g) * sh.P + sh.c0;  // candidate 0
 
   if (tid == 0) {
     s_nan = 0;
     s_minslot = -1;
     s_minkey = KEY_NONE;
   }
-  CandBlock<VPT> blk;
-  bool saw_nan = false;
-  if (sh.kk > 0) blk.init(scores + static_cast<int64_t>(g) * sh.P, sh, L, tid, &saw_nan);
   __syncthreads();
-  if (saw_nan) s_nan = 1;
 
-  if (sh.kk > 0 && sh.kk == C) {
-    // ---- every candidate is kept: positions in order, and the least
-    // important one is the smallest (code, position) -------------------------
-    uint64_t mk = KEY_NONE;
-    int32_t mpos = 0x7FFFFFFF;
-    blk.for_each([&](int32_t i, uint32_t o) {
-      out[i - sh.c0] = i;
-      const uint64_t key = make_key(o, i);
-      if (key < mk) {
-        mk = key;
-        mpos = i;
-      }
-    });
+  // smallest (code, position) over the workgroup -> s_minkey and its slot
+  auto publish_min = [&](uint64_t mk, int32_t mpos) {
     wave_min_key(mk, mpos);
-    __shared__ uint64_t s_wmk[NWAVE];
-    __shared__ int32_t s_wmp[NWAVE];
     if ((tid & (WAVE - 1)) == 0) {
       s_wmk[wid] = mk;
       s_wmp[wid] = mpos;
@@ -171,59 +202,157 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       s_minkey = mk;
       s_minslot = sh.s_eff + (mpos - sh.c0);
     }
-  } else if (sh.kk > 0) {
-    // ---- radix select of the kk-th largest code, 8 bits at a time --------
-    uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < NWAVE * 256; i += SEL_THREADS) (&whist[0][0])[i] = 0;
-      __syncthreads();
-      blk.for_each([&](int32_t, uint32_t o) {
-        if ((o & mask) == prefix) atomicAdd(&whist[wid][(o >> shift) & 255u], 1u);
-      });
-      __syncthreads();
-      // bins from the top: thread t < 256 holds bin 255 - t
-      uint32_t h = 0;
-      if (tid < 256) {
+  };
+
+  if (sh.kk > 0 && VPT > 0) {
+    // ---- codes into registers: thread-contiguous blocks of L = 2^lg --------
+    int lg = 0;
+    while ((SEL_THREADS << lg) < C) ++lg;
+    const int32_t L = 1 << lg;
+    const bool nan = stage_codes(sc, C, lg, stage);
+    if (nan) s_nan = 1;
+    __syncthreads();
+    uint32_t code[LMAX];
 #pragma unroll
-        for (int w = 0; w < NWAVE; ++w) h += whist[w][255 - tid];
+    for (int j = 0; j < LMAX; ++j) code[j] = (j < L) ? stage[tid * (L + 1) + j] : 0u;
+    const int32_t lo = sh.c0 + min(tid * L, C), hi = min(lo + L, sh.c1);
+    auto for_each = [&](auto&& f) {
+#pragma unroll
+      for (int j = 0; j < LMAX; ++j)
+        if (lo + j < hi) f(lo + j, code[j]);
+    };
+
+    if (sh.kk == C) {
+      // every candidate is kept: positions in order; the least important one
+      // is the smallest (code, position)
+      uint64_t mk = KEY_NONE;
+      int32_t mpos = 0x7FFFFFFF;
+      for_each([&](int32_t i, uint32_t o) {
+        out[i - sh.c0] = i;
+        const uint64_t key = make_key(o, i);
+        if (key < mk) {
+          mk = key;
+          mpos = i;
+        }
+      });
+      publish_min(mk, mpos);
+    } else {
+      // ---- radix select of the kk-th largest code: 12, 12, 8 bits --------
+      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
+      auto visit = [&](auto&& f) { for_each([&](int32_t, uint32_t o) { f(o); }); };
+      const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
+#pragma unroll
+      for (int ps = 0; ps < 3; ++ps) {
+        radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
+                   &s_above, &s_neq);
+        krem -= s_above;
+        prefix |= s_bin << shifts[ps];
+        mask |= static_cast<uint32_t>(nbins[ps] - 1) << shifts[ps];
       }
+      // ---- ordered compaction: codes above the threshold, then the newest
+      // krem tokens carrying it (ties: the older ones lose) ------------------
+      const uint32_t thr = prefix;
+      const uint32_t drop = s_neq - krem;
+      uint32_t gt = 0, eq = 0;
+      for_each([&](int32_t, uint32_t o) {
+        gt += o > thr;
+        eq += o == thr;
+      });
       uint32_t tot;
-      const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>(h, scan_buf, &tot);
-      if (tid < 256 && ex < krem && krem <= ex + h) {
-        s_bin = 255u - tid;
-        s_above = ex;
-        s_neq = h;
-      }
-      __syncthreads();
-      krem -= s_above;
-      prefix |= s_bin << shift;
-      mask |= 0xFFu << shift;
+      const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
+      uint32_t eq_before = ex >> 16, gt_before = ex & 0xFFFFu;
+      for_each([&](int32_t i, uint32_t o) {
+        const bool is_gt = o > thr, is_eq = o == thr;
+        if (is_gt || (is_eq && eq_before >= drop)) {
+          const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
+          out[idx] = i;
+          if (is_eq && eq_before == drop) {  // the least important kept token
+            s_minslot = sh.s_eff + static_cast<int32_t>(idx);
+            s_minkey = make_key(thr, i);
+          }
+        }
+        gt_before += is_gt;
+        eq_before += is_eq;
+      });
     }
-    // ---- ordered compaction: codes above the threshold, then the newest
-    // krem tokens carrying it (ties: the older ones lose) --------------------
-    const uint32_t thr = prefix;
-    const uint32_t drop = s_neq - krem;
-    uint32_t gt = 0, eq = 0;
-    blk.for_each([&](int32_t, uint32_t o) {
-      gt += o > thr;
-      eq += o == thr;
-    });
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
-    uint32_t eq_before = ex >> 16, gt_before = ex & 0xFFFFu;
-    blk.for_each([&](int32_t i, uint32_t o) {
-      const bool is_gt = o > thr, is_eq = o == thr;
-      if (is_gt || (is_eq && eq_before >= drop)) {
-        const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
-        out[idx] = i;
-        if (is_eq && eq_before == drop) {  // the least important kept token
-          s_minslot = sh.s_eff + static_cast<int32_t>(idx);
-          s_minkey = make_key(thr, i);
+  } else if (sh.kk > 0) {
+    // ---- long prompts: stream the scores on every pass ---------------------
+    bool nan = false;
+    if (sh.kk == C) {
+      uint64_t mk = KEY_NONE;
+      int32_t mpos = 0x7FFFFFFF;
+      for (int32_t i = tid; i < C; i += SEL_THREADS) {
+        const float x = sc[i];
+        nan |= score_is_nan(x);
+        out[i] = sh.c0 + i;
+        const uint64_t key = make_key(score_code(x), sh.c0 + i);
+        if (key < mk) {
+          mk = key;
+          mpos = sh.c0 + i;
         }
       }
-      gt_before += is_gt;
-      eq_before += is_eq;
-    });
+      if (nan) s_nan = 1;
+      publish_min(mk, mpos);
+    } else {
+      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
+      const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
+#pragma unroll
+      for (int ps = 0; ps < 3; ++ps) {
+        auto visit = [&](auto&& f) { stream_codes(sc, C, ps == 0, &nan, f); };
+        radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
+                   &s_above, &s_neq);
+        krem -= s_above;
+        prefix |= s_bin << shifts[ps];
+        mask |= static_cast<uint32_t>(nbins[ps] - 1) << shifts[ps];
+      }
+      if (nan) s_nan = 1;
+      const uint32_t thr = prefix;
+      const uint32_t drop = s_neq - krem;
+      // ordered compaction in tiles of 32 candidates per thread, staged
+      // through LDS so that each thread walks a contiguous block
+      constexpr int TL = 1 << TILE_LG;
+      uint32_t gt_base = 0, eq_base = 0;
+      for (int32_t t0 = 0; t0 < C; t0 += SEL_THREADS * TL) {
+        const int32_t n = min(SEL_THREADS * TL, C - t0);
+        stage_codes(sc + t0, n, TILE_LG, stage);
+        __syncthreads();
+        uint32_t code[TL];
+#pragma unroll
+        for (int j = 0; j < TL; ++j) code[j] = stage[tid * (TL + 1) + j];
+        const int32_t lo = min(tid * TL, n), hi = min(lo + TL, n);  // tile-relative
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int j = 0; j < TL; ++j)
+          if (lo + j < hi) {
+            gt += code[j] > thr;
+            eq += code[j] == thr;
+          }
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
+        uint32_t eq_before = eq_base + (ex >> 16), gt_before = gt_base + (ex & 0xFFFFu);
+#pragma unroll
+        for (int j = 0; j < TL; ++j) {
+          if (lo + j < hi) {
+            const uint32_t o = code[j];
+            const int32_t i = sh.c0 + t0 + lo + j;
+            const bool is_gt = o > thr, is_eq = o == thr;
+            if (is_gt || (is_eq && eq_before >= drop)) {
+              const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
+              out[idx] = i;
+              if (is_eq && eq_before == drop) {
+                s_minslot = sh.s_eff + static_cast<int32_t>(idx);
+                s_minkey = make_key(thr, i);
+              }
+            }
+            gt_before += is_gt;
+            eq_before += is_eq;
+          }
+        }
+        gt_base += tot & 0xFFFFu;
+        eq_base += tot >> 16;
+        __syncthreads();  // the stage is refilled by the next tile
+      }
+    }
   }
   __syncthreads();
   if (tid == 0) {

@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "decode steps/sec + achieved HBM GB/s, 4032-entry/head cache, Qwen3-8B layer shapes"
 HBM_PEAK_GBPS = 8000.0
 PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_kernel_qwen3_8b_layer_4x_traffic.json")
+PROFILE_PMC_B64 = os.path.join(ROOT, "profiles", "decode_kernel_batched_serving_b64_traffic.json")
 
 
 def decode_bytes_per_launch(w, n_kept: int) -> int:
@@ -50,11 +51,11 @@ def prefill_bytes(w, P: int) -> int:
     return Hkv * (C * 4 + 2 * kept * D * 2 * 2 + kept * 12)
 
 
-def _load_traffic(kernel_hash: str):
+def _load_traffic(kernel_hash: str, path: str = PROFILE_PMC):
     """HBM traffic per decode launch from the committed counter summary, if it
     was taken on the current kernel source."""
     try:
-        with open(PROFILE_PMC) as f:
+        with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -182,12 +183,13 @@ def dense_vs_kvpop(contexts, steps: int, reps: int):
     return rows
 
 
-def batched_serving(steps: int, reps: int):
+def batched_serving(steps: int, reps: int, mode: str = "graph"):
     """Batched serving: 64 sequences of the Qwen3-8B layer shape with 4,032
     slots per KV head, prompts uniform in [4096, 32768] (seeded), scores
     lognormal quantised to 256 levels.  One decode launch serves all 64
     sequences.  Prefill (reset + compaction of every prompt) and decode are
-    captured as HIP graphs and replayed; K/V/q are seeded device-side N(0,1).
+    captured as HIP graphs and replayed (mode "eager": plain launches); K/V/q
+    are seeded device-side N(0,1).
     """
     import numpy as np
     import torch
@@ -228,19 +230,23 @@ def batched_serving(steps: int, reps: int):
         pre()
         dec()
     torch.cuda.synchronize()
-    gp, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gp, stream=stream):
-        pre()
-    with torch.cuda.graph(gd, stream=stream):
-        dec()
+    if mode == "graph":
+        gp, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gp, stream=stream):
+            pre()
+        with torch.cuda.graph(gd, stream=stream):
+            dec()
+        run_pre, run_dec = gp.replay, gd.replay
+    else:
+        run_pre, run_dec = pre, dec
     pre_ms = dec_ms = 0.0
     for r in range(reps + 1):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         with torch.cuda.stream(stream):
             e[0].record(stream)
-            gp.replay()
+            run_pre()
             e[1].record(stream)
-            gd.replay()
+            run_dec()
             e[2].record(stream)
         torch.cuda.synchronize()
         if r > 0:
@@ -262,6 +268,7 @@ def batched_serving(steps: int, reps: int):
         "decode_tokens_per_s": B * 1e6 / us,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "bytes_per_launch": bpl,
+                     "traffic": _load_traffic(_kernel_hash(), PROFILE_PMC_B64),
                      "kernel": "decode_kernel (head_dim 128, 4 query heads per KV head)"},
         "prefill_tokens_per_s": ptok / pre_s,
         "prefill_GBps": pbytes / pre_s / 1e9,
@@ -282,6 +289,8 @@ def main():
                     help="decode steps per pass (default: the workload's); for short profiles")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batch-64 serving measurement")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="run only the batch-64 serving measurement (for profiles)")
     ap.add_argument("--no-dense-sweep", action="store_true",
                     help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -306,6 +315,12 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": x.numel() * 4, "copies": max(1, args.steps)}), flush=True)
+        return
+
+    if args.batched_only:
+        abi.load()
+        print(json.dumps({"batched_serving": batched_serving(args.decode_steps or 64, args.steps,
+                                                             args.mode)}), flush=True)
         return
 
     w = BY_NAME[args.workload]
@@ -434,7 +449,7 @@ def main():
         "wall_s_timed": wall,
     }
     if not args.no_batched:
-        result["batched_serving"] = batched_serving(64, 3)
+        result["batched_serving"] = batched_serving(64, 3, args.mode)
     if not args.no_dense_sweep:
         result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
     if not args.no_cpu_baseline:

@@ -68,12 +68,13 @@ constexpr int TILE_LG = 5;   // streamed compaction: tiles of 32 candidates per 
 // out thread-contiguously: candidate i belongs to thread i >> lg, entry
 // i & (2^lg - 1), stored at (i >> lg) * (2^lg + 1) + (i & (2^lg - 1)); the pad
 // word keeps the 64 lanes of a wave in distinct banks when each then reads
-// its own block.  Returns whether this thread saw a NaN.
+// its own block.  U loads per thread are in flight at once (U * 1024 >= n
+// makes it one round trip).  Returns whether this thread saw a NaN.
+template <int U>
 __device__ __forceinline__ bool stage_codes(const float* __restrict__ sc, int32_t n, int lg,
                                             uint32_t* stage) {
   const int32_t L = 1 << lg;
   bool nan = false;
-  constexpr int U = 8;  // loads in flight per thread
   for (int32_t i0 = threadIdx.x; i0 < n; i0 += SEL_THREADS * U) {
     float x[U];
 #pragma unroll
@@ -90,12 +91,12 @@ __device__ __forceinline__ bool stage_codes(const float* __restrict__ sc, int32_
   return nan;
 }
 
-// f(code) for every candidate [0, n) at `sc`, read with coalesced loads (the
-// order of the calls is unspecified).  With check_nan, *nan collects NaNs.
-template <typename F>
+// f(code) for every candidate [0, n) at `sc`, read with coalesced loads, U
+// per thread in flight (the order of the calls is unspecified).  With
+// check_nan, *nan collects NaNs.
+template <int U, typename F>
 __device__ __forceinline__ void stream_codes(const float* __restrict__ sc, int32_t n, bool check_nan,
                                              bool* nan, F&& f) {
-  constexpr int U = 8;
   for (int32_t i0 = threadIdx.x; i0 < n; i0 += SEL_THREADS * U) {
     float x[U];
 #pragma unroll
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
     int lg = 0;
     while ((SEL_THREADS << lg) < C) ++lg;
     const int32_t L = 1 << lg;
-    const bool nan = stage_codes(sc, C, lg, stage);
+    const bool nan = stage_codes<LMAX>(sc, C, lg, stage);
     if (nan) s_nan = 1;
     __syncthreads();
     uint32_t code[LMAX];
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
 #pragma unroll
       for (int ps = 0; ps < 3; ++ps) {
-        auto visit = [&](auto&& f) { stream_codes(sc, C, ps == 0, &nan, f); };
+        auto visit = [&](auto&& f) { stream_codes<16>(sc, C, ps == 0, &nan, f); };
         radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
                    &s_above, &s_neq);
         krem -= s_above;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       uint32_t gt_base = 0, eq_base = 0;
       for (int32_t t0 = 0; t0 < C; t0 += SEL_THREADS * TL) {
         const int32_t n = min(SEL_THREADS * TL, C - t0);
-        stage_codes(sc + t0, n, TILE_LG, stage);
+        stage_codes<16>(sc + t0, n, TILE_LG, stage);
         __syncthreads();
         uint32_t code[TL];
 #pragma unroll

@@ -20,7 +20,8 @@ constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t kc, vc, keys, pos, ring, ctl, sel, part_acc, part_ml, part_min, tickets, total;
+  size_t kc, vc, keys, pos, ring, ctl, sel, slice_keys, slice_nan, part_acc, part_ml, part_min,
+      tickets, total;
   int32_t nsplit, rows_per_split, threads, rows_per_thread;
 };
 
@@ -98,6 +99,9 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   ok = ok && mul_ok(heads_all, size_t(c.n_recent) * 4, &tmp) && take(tmp, &L->ring);
   ok = ok && mul_ok(heads_all, sizeof(kvpop::HeadCtl), &tmp) && take(tmp, &L->ctl);
   ok = ok && take(size_t(c.n_kv_heads) * size_t(std::max(c.n_scored, 1)) * 4, &L->sel);
+  ok = ok && take(size_t(c.n_kv_heads) * kvpop::SLICE_MAX * size_t(std::max(c.n_scored, 1)) * 8,
+                  &L->slice_keys);
+  ok = ok && take(size_t(c.n_kv_heads) * kvpop::SLICE_MAX * 4, &L->slice_nan);
   const size_t parts = heads * size_t(L->nsplit);
   ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
   ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
@@ -284,9 +288,12 @@ int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_
   if (k == nullptr || v == nullptr || scores == nullptr) return KVPOP_EINVAL;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
+  kvpop::PrefillWork pw;
+  pw.sel = reinterpret_cast<int32_t*>(cache->base + cache->lay.sel);
+  pw.slice_keys = reinterpret_cast<uint64_t*>(cache->base + cache->lay.slice_keys);
+  pw.slice_nan = reinterpret_cast<int32_t*>(cache->base + cache->lay.slice_nan);
   hipError_t e = kvpop::launch_prefill(cache->geo(), cache->layer(layer), seq, n_tokens, k, v,
-                                       scores, reinterpret_cast<int32_t*>(cache->base + cache->lay.sel),
-                                       static_cast<hipStream_t>(stream));
+                                       scores, pw, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;
     return KVPOP_EHIP;

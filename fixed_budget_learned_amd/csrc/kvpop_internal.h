@@ -67,9 +67,18 @@ struct DecodeWork {
 // on `stream`; nothing is synchronised.
 hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int64_t n_tickets,
                            hipStream_t stream);
+// Prefill workspace (one per cache; calls are stream-ordered).  Long prompts
+// select in two levels: up to SLICE_MAX slices per head first keep their own
+// top k, then one workgroup per head selects from the union.
+constexpr int SLICE_MAX = 16;
+struct PrefillWork {
+  int32_t* sel;          // [Hkv][k] kept candidate positions of the call
+  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level keys
+  int32_t* slice_nan;    // [Hkv][SLICE_MAX] first-level NaN flags
+};
 hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
                           const uint16_t* k, const uint16_t* v, const float* scores,
-                          int32_t* sel, hipStream_t stream);
+                          const PrefillWork& pw, hipStream_t stream);
 // Largest split count the decode kernel accepts, and whether a launch shape
 // (head_dim, group size, workgroup size, rows per thread) is compiled.
 int decode_max_splits();

@@ -152,19 +152,42 @@ __device__ __forceinline__ void radix_pass(Visit&& visit, uint32_t prefix, uint3
   __syncthreads();
 }
 
-// Select kernel: one 1024-thread workgroup per KV head.  VPT 16 / 32: every
-// thread holds a contiguous block of at most VPT candidate codes in
-// registers (staged through LDS from coalesced loads); VPT 0: longer prompts
-// stream the scores (through the caches) on every pass and compact them in
-// tiles of 32 candidates per thread.
-template <int VPT>
-__global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
-    const float* __restrict__ scores, PrefillShape sh, int32_t k, int32_t* __restrict__ sel,
-    HeadCtl* __restrict__ ctl) {
+// Select kernels.  1024 threads per workgroup; MODE:
+//   SEL_HEAD   one workgroup per KV head selects from all its candidates.
+//              VPT 16 / 32: each thread holds a contiguous block of at most
+//              VPT candidate codes in registers (staged through LDS from
+//              coalesced loads); VPT 0: the scores are streamed on every pass
+//              and compacted in LDS-staged tiles (fallback for any length).
+//   SEL_SLICE  first level for long prompts: workgroup (head, slice) selects
+//              the top min(k, slice length) of a slice of the candidates and
+//              writes their keys, ascending in position, padded with key 0 to
+//              k entries.  The global top-k lies in the union of the slices'
+//              top-k, since a slice contributes at most k of it.
+//   SEL_LIST   second level: one workgroup per head selects the top k of that
+//              union (read as keys, in position order) and writes positions
+//              and the control block like SEL_HEAD.
+constexpr int SEL_HEAD = 0, SEL_SLICE = 1, SEL_LIST = 2;
+
+struct SelectArgs {
+  const float* scores;   // [Hkv][P] of this sequence
+  PrefillShape sh;
+  int32_t k;             // scored slots (stride of the selection buffers)
+  int32_t* sel;          // [Hkv][k] kept candidate positions, ascending
+  HeadCtl* ctl;          // [Hkv]
+  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level keys
+  int32_t* slice_nan;    // [Hkv][SLICE_MAX] first-level NaN flags
+  int32_t n_slices, slice_len;
+};
+
+template <int VPT, int MODE>
+__global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectArgs a) {
+  static_assert(MODE != SEL_LIST || VPT == 16, "list mode stages 64-bit keys: at most 16 per thread");
+  static_assert(MODE == SEL_HEAD || VPT > 0, "slice and list modes keep codes in registers");
   constexpr int NWAVE = SEL_THREADS / WAVE;
   constexpr int LMAX = VPT > 0 ? VPT : (1 << TILE_LG);
+  constexpr int STAGE_WORDS = (MODE == SEL_LIST ? 2 : 1) * SEL_THREADS * (LMAX + 1);
   __shared__ uint32_t hist[NBINS];
-  __shared__ uint32_t stage[SEL_THREADS * (LMAX + 1)];
+  __shared__ __align__(16) uint32_t stage[STAGE_WORDS];
   __shared__ uint32_t scan_buf[NWAVE + 1];
   __shared__ uint32_t s_bin, s_above, s_nan, s_neq;
   __shared__ int32_t s_minslot;
@@ -172,12 +195,25 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
   __shared__ uint64_t s_wmk[NWAVE];
   __shared__ int32_t s_wmp[NWAVE];
 
+  const PrefillShape& sh = a.sh;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int wid = tid / WAVE;
-  int32_t* out = sel + static_cast<int64_t>(g) * (k > 0 ? k : 1);
-  const int32_t C = sh.c1 - sh.c0;
-  const float* sc = scores + static_cast<int64_t>(g) * sh.P + sh.c0;  // candidate 0
+  const int32_t kst = a.k > 0 ? a.k : 1;  // stride of the per-head buffers
+  int32_t* out = a.sel + static_cast<int64_t>(g) * kst;
+  // this workgroup's candidates: [cb, cb + C) of the head's candidate range
+  // (SEL_LIST: entries of the head's first-level key list)
+  int32_t cb = 0, C = sh.c1 - sh.c0, kk = sh.kk;
+  if constexpr (MODE == SEL_SLICE) {
+    cb = static_cast<int32_t>(blockIdx.y) * a.slice_len;
+    C = min(a.slice_len, sh.c1 - sh.c0 - cb);
+    kk = min(a.k, C);
+  } else if constexpr (MODE == SEL_LIST) {
+    C = a.n_slices * a.k;
+  }
+  const float* sc = a.scores + static_cast<int64_t>(g) * sh.P + sh.c0 + cb;  // candidate 0
+  const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * a.k;
+  uint64_t* outk = a.slice_keys + list0 + static_cast<int64_t>(blockIdx.y) * a.k;
 
   if (tid == 0) {
     s_nan = 0;
@@ -185,6 +221,9 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
     s_minkey = KEY_NONE;
   }
   __syncthreads();
+  if constexpr (MODE == SEL_LIST) {
+    if (tid < a.n_slices && a.slice_nan[g * SLICE_MAX + tid]) s_nan = 1;
+  }
 
   // smallest (code, position) over the workgroup -> s_minkey and its slot
   auto publish_min = [&](uint64_t mk, int32_t mpos) {
@@ -204,43 +243,84 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       s_minslot = sh.s_eff + (mpos - sh.c0);
     }
   };
+  // where the kept candidate of rank idx goes
+  auto emit = [&](uint32_t idx, int32_t pos, uint32_t code) {
+    if constexpr (MODE == SEL_SLICE)
+      outk[idx] = make_key(code, pos);
+    else
+      out[idx] = pos;
+  };
 
-  if (sh.kk > 0 && VPT > 0) {
-    // ---- codes into registers: thread-contiguous blocks of L = 2^lg --------
+  if (kk > 0 && VPT > 0) {
+    // ---- codes (and list positions) into registers: thread-contiguous
+    // blocks of L = 2^lg entries ----------------------------------------------
     int lg = 0;
     while ((SEL_THREADS << lg) < C) ++lg;
     const int32_t L = 1 << lg;
-    const bool nan = stage_codes<LMAX>(sc, C, lg, stage);
-    if (nan) s_nan = 1;
-    __syncthreads();
     uint32_t code[LMAX];
+    int32_t lpos[MODE == SEL_LIST ? LMAX : 1];
+    if constexpr (MODE == SEL_LIST) {
+      // coalesced loads of the keys, transposed through LDS like the codes
+      uint64_t* st64 = reinterpret_cast<uint64_t*>(stage);
+      const uint64_t* lk = a.slice_keys + list0;
+      constexpr int U = 16;
+      for (int32_t i0 = tid; i0 < C; i0 += SEL_THREADS * U) {
+        uint64_t x[U];
 #pragma unroll
-    for (int j = 0; j < LMAX; ++j) code[j] = (j < L) ? stage[tid * (L + 1) + j] : 0u;
-    const int32_t lo = sh.c0 + min(tid * L, C), hi = min(lo + L, sh.c1);
+        for (int u = 0; u < U; ++u) x[u] = lk[min(i0 + u * SEL_THREADS, C - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int32_t i = i0 + u * SEL_THREADS;
+          if (i < C) st64[(i >> lg) * (L + 1) + (i & (L - 1))] = x[u];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < LMAX; ++j) {
+        const uint64_t key = (j < L) ? st64[tid * (L + 1) + j] : 0ull;
+        code[j] = static_cast<uint32_t>(key >> 32);
+        lpos[j] = static_cast<int32_t>(static_cast<uint32_t>(key));
+      }
+    } else {
+      const bool nan = stage_codes<LMAX>(sc, C, lg, stage);
+      if (nan) s_nan = 1;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < LMAX; ++j) code[j] = (j < L) ? stage[tid * (L + 1) + j] : 0u;
+    }
+    const int32_t lo = min(tid * L, C), hi = min(lo + L, C);  // workgroup-relative
     auto for_each = [&](auto&& f) {
 #pragma unroll
-      for (int j = 0; j < LMAX; ++j)
-        if (lo + j < hi) f(lo + j, code[j]);
+      for (int j = 0; j < LMAX; ++j) {
+        if (lo + j < hi) {
+          int32_t pos;
+          if constexpr (MODE == SEL_LIST)
+            pos = lpos[j];
+          else
+            pos = sh.c0 + cb + lo + j;
+          f(lo + j, pos, code[j]);
+        }
+      }
     };
 
-    if (sh.kk == C) {
+    if (kk == C) {
       // every candidate is kept: positions in order; the least important one
       // is the smallest (code, position)
       uint64_t mk = KEY_NONE;
       int32_t mpos = 0x7FFFFFFF;
-      for_each([&](int32_t i, uint32_t o) {
-        out[i - sh.c0] = i;
+      for_each([&](int32_t r, int32_t i, uint32_t o) {
+        emit(static_cast<uint32_t>(r), i, o);
         const uint64_t key = make_key(o, i);
         if (key < mk) {
           mk = key;
           mpos = i;
         }
       });
-      publish_min(mk, mpos);
+      if constexpr (MODE != SEL_SLICE) publish_min(mk, mpos);
     } else {
       // ---- radix select of the kk-th largest code: 12, 12, 8 bits --------
-      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
-      auto visit = [&](auto&& f) { for_each([&](int32_t, uint32_t o) { f(o); }); };
+      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
+      auto visit = [&](auto&& f) { for_each([&](int32_t, int32_t, uint32_t o) { f(o); }); };
       const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
 #pragma unroll
       for (int ps = 0; ps < 3; ++ps) {
@@ -255,18 +335,18 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       const uint32_t thr = prefix;
       const uint32_t drop = s_neq - krem;
       uint32_t gt = 0, eq = 0;
-      for_each([&](int32_t, uint32_t o) {
+      for_each([&](int32_t, int32_t, uint32_t o) {
         gt += o > thr;
         eq += o == thr;
       });
       uint32_t tot;
       const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
       uint32_t eq_before = ex >> 16, gt_before = ex & 0xFFFFu;
-      for_each([&](int32_t i, uint32_t o) {
+      for_each([&](int32_t, int32_t i, uint32_t o) {
         const bool is_gt = o > thr, is_eq = o == thr;
         if (is_gt || (is_eq && eq_before >= drop)) {
           const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
-          out[idx] = i;
+          emit(idx, i, o);
           if (is_eq && eq_before == drop) {  // the least important kept token
             s_minslot = sh.s_eff + static_cast<int32_t>(idx);
             s_minkey = make_key(thr, i);
@@ -276,10 +356,10 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
         eq_before += is_eq;
       });
     }
-  } else if (sh.kk > 0) {
-    // ---- long prompts: stream the scores on every pass ---------------------
+  } else if (kk > 0) {
+    // ---- SEL_HEAD, long prompts: stream the scores on every pass -----------
     bool nan = false;
-    if (sh.kk == C) {
+    if (kk == C) {
       uint64_t mk = KEY_NONE;
       int32_t mpos = 0x7FFFFFFF;
       for (int32_t i = tid; i < C; i += SEL_THREADS) {
@@ -295,7 +375,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       if (nan) s_nan = 1;
       publish_min(mk, mpos);
     } else {
-      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(sh.kk);
+      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
       const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
 #pragma unroll
       for (int ps = 0; ps < 3; ++ps) {
@@ -317,16 +397,16 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
         const int32_t n = min(SEL_THREADS * TL, C - t0);
         stage_codes<16>(sc + t0, n, TILE_LG, stage);
         __syncthreads();
-        uint32_t code[TL];
+        uint32_t tcode[TL];
 #pragma unroll
-        for (int j = 0; j < TL; ++j) code[j] = stage[tid * (TL + 1) + j];
+        for (int j = 0; j < TL; ++j) tcode[j] = stage[tid * (TL + 1) + j];
         const int32_t lo = min(tid * TL, n), hi = min(lo + TL, n);  // tile-relative
         uint32_t gt = 0, eq = 0;
 #pragma unroll
         for (int j = 0; j < TL; ++j)
           if (lo + j < hi) {
-            gt += code[j] > thr;
-            eq += code[j] == thr;
+            gt += tcode[j] > thr;
+            eq += tcode[j] == thr;
           }
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
@@ -334,7 +414,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
 #pragma unroll
         for (int j = 0; j < TL; ++j) {
           if (lo + j < hi) {
-            const uint32_t o = code[j];
+            const uint32_t o = tcode[j];
             const int32_t i = sh.c0 + t0 + lo + j;
             const bool is_gt = o > thr, is_eq = o == thr;
             if (is_gt || (is_eq && eq_before >= drop)) {
@@ -355,6 +435,13 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
       }
     }
   }
+  if constexpr (MODE == SEL_SLICE) {
+    // pad the slice's list to k entries with the smallest key; record NaNs
+    for (int32_t j = kk + tid; j < a.k; j += SEL_THREADS) outk[j] = 0ull;
+    __syncthreads();
+    if (tid == 0) a.slice_nan[g * SLICE_MAX + blockIdx.y] = s_nan ? 1 : 0;
+    return;
+  }
   __syncthreads();
   if (tid == 0) {
     HeadCtl c;
@@ -365,7 +452,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(
     c.minkey = s_minkey;
     c.flags = s_nan ? 1 : 0;
     c.leave_slot = sh.leave;
-    ctl[g] = c;
+    a.ctl[g] = c;
   }
 }
 
@@ -470,20 +557,62 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
 
 hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
                           const uint16_t* k, const uint16_t* v, const float* scores,
-                          int32_t* sel, hipStream_t stream) {
+                          const PrefillWork& pw, hipStream_t stream) {
   const PrefillShape sh = prefill_shape(n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
   const int64_t head0 = static_cast<int64_t>(seq) * geo.n_kv_heads;
   const int32_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
-  const int32_t per_thread = (sh.c1 - sh.c0 + SEL_THREADS - 1) / SEL_THREADS;
-  if (per_thread <= 16)
-    hipLaunchKernelGGL(prefill_select_kernel<16>, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0,
-                       stream, scores, sh, geo.n_scored, sel, lv.ctl + head0);
-  else if (per_thread <= 32)
-    hipLaunchKernelGGL(prefill_select_kernel<32>, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0,
-                       stream, scores, sh, geo.n_scored, sel, lv.ctl + head0);
-  else
-    hipLaunchKernelGGL(prefill_select_kernel<0>, dim3(geo.n_kv_heads), dim3(SEL_THREADS), 0,
-                       stream, scores, sh, geo.n_scored, sel, lv.ctl + head0);
+  int32_t* sel = pw.sel;
+  SelectArgs sa;
+  sa.scores = scores;
+  sa.sh = sh;
+  sa.k = geo.n_scored;
+  sa.sel = sel;
+  sa.ctl = lv.ctl + head0;
+  sa.slice_keys = pw.slice_keys;
+  sa.slice_nan = pw.slice_nan;
+  sa.n_slices = 1;
+  sa.slice_len = 0;
+  const int32_t C = sh.c1 - sh.c0;
+  const int32_t per_thread = (C + SEL_THREADS - 1) / SEL_THREADS;
+  const dim3 heads(geo.n_kv_heads);
+  if (per_thread <= 16) {
+    hipLaunchKernelGGL((prefill_select_kernel<16, SEL_HEAD>), heads, dim3(SEL_THREADS), 0, stream,
+                       sa);
+  } else if (per_thread <= 32) {
+    hipLaunchKernelGGL((prefill_select_kernel<32, SEL_HEAD>), heads, dim3(SEL_THREADS), 0, stream,
+                       sa);
+  } else {
+    // Long prompts: two levels when the union of the slices' top-k fits one
+    // workgroup's registers (at most 16 per thread), else the streaming path.
+    const int64_t k64 = geo.n_scored;
+    const int32_t ns16 = (C + 16383) / 16384, ns32 = (C + 32767) / 32768;
+    int vpt = 0;
+    if (sh.kk < C && ns16 <= SLICE_MAX && ns16 * k64 <= 16384) {
+      vpt = 16;
+      sa.n_slices = ns16;
+      sa.slice_len = 16384;
+    } else if (sh.kk < C && ns32 <= SLICE_MAX && ns32 * k64 <= 16384) {
+      vpt = 32;
+      sa.n_slices = ns32;
+      sa.slice_len = 32768;
+    }
+    if (vpt == 0) {
+      hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD>), heads, dim3(SEL_THREADS), 0, stream,
+                         sa);
+    } else {
+      const dim3 slices(geo.n_kv_heads, sa.n_slices);
+      if (vpt == 16)
+        hipLaunchKernelGGL((prefill_select_kernel<16, SEL_SLICE>), slices, dim3(SEL_THREADS), 0,
+                           stream, sa);
+      else
+        hipLaunchKernelGGL((prefill_select_kernel<32, SEL_SLICE>), slices, dim3(SEL_THREADS), 0,
+                           stream, sa);
+      hipError_t e1 = hipGetLastError();
+      if (e1 != hipSuccess) return e1;
+      hipLaunchKernelGGL((prefill_select_kernel<16, SEL_LIST>), heads, dim3(SEL_THREADS), 0, stream,
+                         sa);
+    }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sh.count == 0) return hipSuccess;

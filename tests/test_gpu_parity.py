@@ -132,6 +132,12 @@ CASES = [
     # slot ranges rounded up to whole passes leave the last split empty
     ("empty_last_split", Geo(4, 1, 128, 4, 64, 32), [150, 20], 40, "normal", 3),
     ("single_split_g8_d64", Geo(16, 2, 64, 4, 700, 64), [2000, 90], 30, "normal", 1),
+    # prompts longer than one workgroup's registers hold: two-level select
+    # (slices of 16k candidates, tie-heavy across slice borders; 32k slices),
+    # and the streaming select when the union of the slices is too large
+    ("two_level_16k_slices_ties", Geo(4, 1, 64, 4, 500, 16), [40000], 20, "ties", 0),
+    ("two_level_32k_slices", Geo(8, 2, 128, 4, 5000, 32), [70000], 10, "normal", 0),
+    ("long_prompt_streaming_select", Geo(4, 1, 64, 4, 20000, 16), [40000], 10, "normal", 0),
 ]
 
 

@@ -183,6 +183,131 @@ def dense_vs_kvpop(contexts, steps: int, reps: int):
     return rows
 
 
+def layered_config(w, steps: int, reps: int):
+    """Decode steps/s and prefill tokens/s of a batch-1 workload over all its
+    layers (each step and each prefill runs one launch per layer), with the
+    fraction of the HBM roofline.  Seeded device-side N(0,1) K/V/q; scores
+    drawn as the workload states.  Prefill inputs are generated one layer at
+    a time (the 131k workload needs 19 GB of them in all).
+    """
+    import torch
+    from fixed_budget_learned_amd import abi
+    from fixed_budget_learned_amd.inputs import T_SCORES, draw_scores, rng_for
+    L, Hq, Hkv, D = w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim
+    P = w.prompt_len or 0
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2000 + w.wid)
+    # the decode graph below is replayed reps times after one eager pass and
+    # the cache keeps advancing on the device: P + steps * (reps + 1) positions
+    cache = abi.KVpopCache(abi.make_config(L, 1, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
+                                           max_positions=P + steps * (reps + 2) + 1))
+    stream = torch.cuda.Stream()
+    pre_ms = 0.0
+    if P > 0:
+        for layer in range(L):
+            k = torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16)
+            v = torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16)
+            sc = torch.from_numpy(draw_scores(rng_for(w.wid, layer, 0, T_SCORES), w.score_dist,
+                                              (Hkv, P))).to("cuda")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                cache.prefill_compact(layer, 0, k, v, sc)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            pre_ms += e0.elapsed_time(e1)
+            del k, v, sc
+    q = torch.randn((steps, L, 1, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    kn = torch.randn((steps, L, 1, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((steps, L, 1, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+    sl = torch.from_numpy(draw_scores(rng_for(w.wid, 0, 1, T_SCORES), w.score_dist,
+                                      (steps, L, 1, Hkv))).to("cuda")
+    out = torch.empty((L, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
+
+    def dec():
+        for i in range(steps):
+            for layer in range(L):
+                cache.decode_step(layer, q[i, layer], kn[i, layer], vn[i, layer], sl[i, layer],
+                                  out[layer])
+
+    with torch.cuda.stream(stream):
+        dec()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        dec()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1)
+    cache.close()
+    us = dec_ms * 1e3 / (reps * steps)
+    # decode bytes per step: every layer reads its kept rows; a cache started
+    # empty holds at least P + steps rows during the timed replays
+    kept = min(w.budget, P + steps + 1)
+    dbytes = L * decode_bytes_per_launch(w, kept)
+    res = {"workload": w.name, "layers": L, "batch": 1, "budget": w.budget, "prompt_len": P,
+           "decode_us_per_step": us, "decode_steps_per_s": 1e6 / us,
+           "decode_GBps": dbytes / (us * 1e-6) / 1e9,
+           "decode_frac": dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+           "decode_bytes_per_step": dbytes, "decode_steps_timed": reps * steps}
+    if P > 0:
+        pbytes = L * prefill_bytes(w, P)
+        res.update({"prefill_us_all_layers": pre_ms * 1e3,
+                    "prefill_tokens_per_s": P / (pre_ms / 1e3),
+                    "prefill_GBps": pbytes / (pre_ms / 1e3) / 1e9,
+                    "prefill_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                    "prefill_bytes": pbytes})
+    return res
+
+
+def decode_cold(w, steps: int):
+    """Decode launch time of the one-layer workload when its cache is not
+    resident in any cache level: a 1 GiB buffer is written between steps
+    (more than the 256 MB last-level cache), then one decode launch is timed
+    alone with events around it."""
+    import torch
+    from fixed_budget_learned_amd import abi
+    Hq, Hkv, D, P = w.n_q_heads, w.n_kv_heads, w.head_dim, w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3000 + w.wid)
+    cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
+                                           max_positions=P + steps + 1))
+    k = torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16)
+    sc = torch.randn((Hkv, P), generator=gen, device="cuda")
+    cache.prefill_compact(0, 0, k, v, sc)
+    q = torch.randn((steps, 1, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    kn = torch.randn((steps, 1, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((steps, 1, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+    sl = torch.randn((steps, 1, Hkv), generator=gen, device="cuda")
+    out = torch.empty((1, Hq, D), dtype=torch.bfloat16, device="cuda")
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(steps):
+        scratch.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.decode_step(0, q[i], kn[i], vn[i], sl[i], out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    cache.close()
+    ms.sort()
+    us = ms[len(ms) // 2] * 1e3
+    bpl = decode_bytes_per_launch(w, w.budget)
+    return {"decode_us_per_launch_median": us, "GBps": bpl / (us * 1e-6) / 1e9,
+            "frac": bpl / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "launches": steps,
+            "note": "1 GiB written between steps; events around each single launch "
+                    "(includes its launch latency)"}
+
+
 def batched_serving(steps: int, reps: int, mode: str = "graph"):
     """Batched serving: 64 sequences of the Qwen3-8B layer shape with 4,032
     slots per KV head, prompts uniform in [4096, 32768] (seeded), scores
@@ -289,6 +414,8 @@ def main():
                     help="decode steps per pass (default: the workload's); for short profiles")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batch-64 serving measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, 36-layer and 131k-token workloads and the cold-cache line")
     ap.add_argument("--batched-only", action="store_true",
                     help="run only the batch-64 serving measurement (for profiles)")
     ap.add_argument("--no-dense-sweep", action="store_true",
@@ -450,6 +577,12 @@ def main():
     }
     if not args.no_batched:
         result["batched_serving"] = batched_serving(64, 3, args.mode)
+    if not args.no_configs:
+        from fixed_budget_learned_amd.configs import (LONG_131K_8X, QWEN3_8B_36L_4X, TINY)
+        result["decode_cold_cache"] = decode_cold(w, 32)
+        result["configs"] = [layered_config(TINY, 512, 2),
+                             layered_config(QWEN3_8B_36L_4X, 32, 2),
+                             layered_config(LONG_131K_8X, 32, 2)]
     if not args.no_dense_sweep:
         result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
     if not args.no_cpu_baseline:

@@ -41,6 +41,11 @@ notes of the repository):
 7. A NaN score is a caller error (the oracle raises).
 8. At prefill the scores of positions [s, P - W) are used; the scores of
    window positions arrive later, one per decode step.
+9. The prefix top-k thresholds the model card's cache-backends section names
+   are read as: for every position n of a prompt, the key of the k-th most
+   important member of Cand(n) (0 while there are fewer than k, KEY_NONE
+   when k = 0), so that the kept set at n is the sinks, the window and the
+   candidates whose key reaches it.
 
 All arithmetic is float64 on exactly decoded bfloat16 values.
 """
@@ -124,6 +129,65 @@ def masked_dense_attention(q, K_all, V_all, kept, scale: float) -> np.ndarray:
     m = logits[mask].max()
     w = np.where(mask, np.exp(logits - m), 0.0)
     return (w / w.sum()) @ V_all
+
+
+# ---------------------------------------------------------------------------
+# Prefix top-k thresholds (every position of a prompt)
+# ---------------------------------------------------------------------------
+
+KEY_NONE = (1 << 64) - 1
+
+
+def score_key(score, pos: int) -> int:
+    """64-bit key of a scored token: order code of the float32 score in the
+    high half, position in the low half.
+
+    The code flips every bit of a negative float and sets the sign bit of a
+    non-negative one, so unsigned order of codes is float order; -0 is taken
+    as +0 first.  Comparing keys as integers is comparing (score, position)
+    lexicographically (reading 3).
+    """
+    u = int(np.array([score], dtype=np.float32).view(np.uint32)[0])
+    if u == 0x80000000:
+        u = 0
+    code = (~u & 0xFFFFFFFF) if (u & 0x80000000) else (u | 0x80000000)
+    return (code << 32) | int(pos)
+
+
+def prefix_thresholds(scores_g, n_tokens: int, n_sink: int, n_scored: int, n_recent: int):
+    """Threshold key of every position n of a prompt, for one KV head.
+
+    thr(n) is the key of the k-th most important member of Cand(n) =
+    {s .. n - W}, so that Kept(n) = Sink(n) | Win(n) | {t in Cand(n) :
+    key(t) >= thr(n)}; it is 0 (every candidate kept) while Cand(n) has fewer
+    than k members, and KEY_NONE (no candidate kept) when k = 0.  The model
+    card names a prefix top-k thresholds kernel among its cache backends; its
+    exact contract is not on the pages, and this is the reading taken.
+
+    Computed the plain way: Cand grows by one position per step, and the k-th
+    largest key of a growing set is the root of a min-heap holding the k
+    largest so far.  Returns a list of n_tokens Python ints.
+    """
+    import heapq
+    s, k, W = n_sink, n_scored, n_recent
+    out = []
+    heap = []
+    nxt = s                                    # next position to enter Cand
+    for n in range(n_tokens):
+        while nxt <= n - W:                     # positions that left the window
+            key = score_key(_check_score(scores_g[nxt]), nxt)
+            if len(heap) < k:
+                heapq.heappush(heap, key)
+            elif k > 0 and key > heap[0]:
+                heapq.heapreplace(heap, key)
+            nxt += 1
+        if k == 0:
+            out.append(KEY_NONE)
+        elif len(heap) < k:
+            out.append(0)
+        else:
+            out.append(heap[0])
+    return out
 
 
 # ---------------------------------------------------------------------------

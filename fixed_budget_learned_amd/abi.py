@@ -22,7 +22,8 @@ KVPOP_FLAG_NAN_SCORE = 1
 
 EXPORTED = ("kvpop_cache_required_bytes", "kvpop_cache_create", "kvpop_cache_destroy",
             "kvpop_cache_reset", "kvpop_prefill_compact", "kvpop_decode_step",
-            "kvpop_cache_state", "kvpop_strerror")
+            "kvpop_cache_state", "kvpop_strerror",
+            "kvpop_prefix_thresholds")
 
 
 class KVpopLibraryMissing(RuntimeError):
@@ -75,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.kvpop_decode_step.restype = ctypes.c_int
     lib.kvpop_cache_state.argtypes = [vp, i32, i32, ctypes.POINTER(State), vp, vp, vp]
     lib.kvpop_cache_state.restype = ctypes.c_int
+    lib.kvpop_prefix_thresholds.argtypes = [vp, i32, vp, vp, vp]
+    lib.kvpop_prefix_thresholds.restype = ctypes.c_int
     lib.kvpop_strerror.argtypes = [ctypes.c_int]
     lib.kvpop_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -187,6 +190,18 @@ class KVpopCache:
         op = _dev_ptr(out, torch.bfloat16, (B, c.n_q_heads, c.head_dim), "out")
         _check(load().kvpop_decode_step(self._h, layer, qp, kp, vp, sp, op, _stream_ptr(stream)),
                "kvpop_decode_step")
+
+    def prefix_thresholds(self, scores, thr, stream=None):
+        """Threshold key of every prompt position per KV head (see the
+        header): scores float32 [Hkv][P] in, thr int64 [Hkv][P] out (the
+        uint64 keys' bits)."""
+        import torch
+        c = self.cfg
+        P = int(scores.shape[1]) if scores is not None and scores.dim() == 2 else 0
+        sp = _dev_ptr(scores, torch.float32, (c.n_kv_heads, P), "scores")
+        tp = _dev_ptr(thr, torch.int64, (c.n_kv_heads, P), "thr")
+        _check(load().kvpop_prefix_thresholds(self._h, P, sp, tp, _stream_ptr(stream)),
+               "kvpop_prefix_thresholds")
 
     def state(self, layer: int, seq: int, stream=None) -> HeadState:
         c = self.cfg

@@ -302,6 +302,26 @@ int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_
   return KVPOP_OK;
 }
 
+int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, const float* scores,
+                            uint64_t* thr, void* stream) {
+  if (cache == nullptr || n_tokens < 0) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (c.n_scored > kvpop::THR_KMAX) return KVPOP_EINVAL;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  if (n_tokens > c.max_positions) return KVPOP_ESTATE;
+  if (n_tokens == 0) return KVPOP_OK;
+  if (scores == nullptr || thr == nullptr) return KVPOP_EINVAL;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  hipError_t e = kvpop::launch_prefix_thresholds(cache->geo(), n_tokens, scores, thr,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  return KVPOP_OK;
+}
+
 int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, const float* score_leaving, uint16_t* out,
                       void* stream) {

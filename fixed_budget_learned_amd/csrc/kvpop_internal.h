@@ -79,6 +79,11 @@ struct PrefillWork {
 hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
                           const uint16_t* k, const uint16_t* v, const float* scores,
                           const PrefillWork& pw, hipStream_t stream);
+// Prefix top-k thresholds of a prompt ([Hkv][n_tokens] keys), n_scored <=
+// THR_KMAX.
+constexpr int THR_KMAX = 4096;
+hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const float* scores,
+                                    uint64_t* thr, hipStream_t stream);
 // Largest split count the decode kernel accepts, and whether a launch shape
 // (head_dim, group size, workgroup size, rows per thread) is compiled.
 int decode_max_splits();

@@ -159,6 +159,25 @@ KVPOP_API int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_
 KVPOP_API int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, kvpop_state* st,
                       int32_t* counts, int32_t* kept_pos, void* stream);
 
+/* Prefix top-k thresholds of a prompt (the "prefix top-k thresholds" kernel
+ * that the "Qwen3-8B-KVpop-4x" model card lists among its cache backends;
+ * the exact contract there is not given, this is the reading taken).  With
+ * the cache's geometry (n_kv_heads, n_sink, n_scored, n_recent) and no
+ * access to its state:
+ *   scores  device [Hkv][n_tokens] float32, the score of every position
+ *   thr     device [Hkv][n_tokens] uint64 (output): for position n, the key
+ *           ((order code of the score) << 32 | position) of the n_scored-th
+ *           most important candidate among positions n_sink .. n-n_recent;
+ *           0 while there are fewer than n_scored of them, and ~0 when
+ *           n_scored == 0.
+ * The kept set after position n is then the sinks, the window and the
+ * candidates whose key is >= thr[g][n]: the set a cache streamed through
+ * position n holds.  Stream-ordered and asynchronous; the caller owns both
+ * buffers.  Errors: KVPOP_EINVAL (NULL pointers, n_tokens < 0, n_scored >
+ * 4096), KVPOP_ESTATE (n_tokens > max_positions), KVPOP_EHIP. */
+KVPOP_API int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, const float* scores,
+                                      uint64_t* thr, void* stream);
+
 /* Static description of a return code. */
 KVPOP_API const char* kvpop_strerror(int code);
 

@@ -107,6 +107,7 @@ def test_null_cache_handle_everywhere(lib):
     assert lib.kvpop_decode_step(None, 0, 1, 1, 1, 1, 1, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_cache_state(None, 0, 0, ctypes.byref(st), None, None, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_cache_reset(None, 0, 0, None) == abi.KVPOP_EINVAL
+    assert lib.kvpop_prefix_thresholds(None, 4, 1, 1, None) == abi.KVPOP_EINVAL
     lib.kvpop_cache_destroy(None)
 
 

@@ -308,6 +308,35 @@ def decode_cold(w, steps: int):
                     "(includes its launch latency)"}
 
 
+def prefix_thresholds_rate(w, reps: int):
+    """Time kvpop_prefix_thresholds on one prompt of the workload (all KV
+    heads): positions per second, and the bytes it must move (scores in,
+    8-byte thresholds out) against the HBM roofline."""
+    import torch
+    from fixed_budget_learned_amd import abi
+    from fixed_budget_learned_amd.inputs import T_SCORES, draw_scores, rng_for
+    Hkv, P = w.n_kv_heads, w.prompt_len
+    sc = torch.from_numpy(draw_scores(rng_for(w.wid, 0, 0, T_SCORES), w.score_dist,
+                                      (Hkv, P))).to("cuda")
+    thr = torch.empty((Hkv, P), dtype=torch.int64, device="cuda")
+    cache = abi.KVpopCache(abi.make_config(1, 1, w.n_q_heads, Hkv, w.head_dim, w.n_sink,
+                                           w.n_scored, w.n_recent, max_positions=P))
+    cache.prefix_thresholds(sc, thr)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        cache.prefix_thresholds(sc, thr)
+    e1.record()
+    torch.cuda.synchronize()
+    cache.close()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = Hkv * (P - w.n_sink - w.n_recent) * 4 + Hkv * P * 8
+    return {"workload": w.name, "prompt_len": P, "us_per_call": us,
+            "positions_per_s": P / (us * 1e-6), "GBps": nbytes / (us * 1e-6) / 1e9,
+            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "bytes": nbytes}
+
+
 def batched_serving(steps: int, reps: int, mode: str = "graph"):
     """Batched serving: 64 sequences of the Qwen3-8B layer shape with 4,032
     slots per KV head, prompts uniform in [4096, 32768] (seeded), scores
@@ -580,6 +609,8 @@ def main():
     if not args.no_configs:
         from fixed_budget_learned_amd.configs import (LONG_131K_8X, QWEN3_8B_36L_4X, TINY)
         result["decode_cold_cache"] = decode_cold(w, 32)
+        result["prefix_thresholds"] = [prefix_thresholds_rate(w, 5),
+                                       prefix_thresholds_rate(LONG_131K_8X, 3)]
         result["configs"] = [layered_config(TINY, 512, 2),
                              layered_config(QWEN3_8B_36L_4X, 32, 2),
                              layered_config(LONG_131K_8X, 32, 2)]

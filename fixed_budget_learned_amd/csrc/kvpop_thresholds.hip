@@ -68,28 +68,101 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
 
   uint64_t* R = Rbuf[0];
   uint64_t* R2 = Rbuf[1];
-  for (int32_t i = tid; i < k; i += THR_THREADS) R[i] = 0ull;
-  __syncthreads();
+  // ---- warm-up: until k candidates have left the window every one is kept
+  // (threshold 0); R = the first min(k, C) keys sorted, then zero keys ------
+  const int32_t w0 = min(k, C);
+  {
+    int32_t p2 = 1;
+    while (p2 < k) p2 <<= 1;
+    for (int32_t i = tid; i < p2; i += THR_THREADS) {
+      uint64_t v = 0ull;
+      if (i < w0) {
+        const int32_t pos = s + i;
+        v = make_key(score_code(sc[pos]), pos);
+        if (i < w0 - 1 || w0 < k) out[s + W + i] = 0ull;  // fewer than k after it
+      } else if (i >= k) {
+        v = ~0ull;                                        // sorts past R
+      }
+      R2[i] = v;
+    }
+    __syncthreads();
+    for (int32_t size = 2; size <= p2; size <<= 1) {
+      for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int32_t i = tid; i < p2 / 2; i += THR_THREADS) {
+          const int32_t lo = 2 * i - (i & (stride - 1));
+          const int32_t hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t a = R2[lo], b = R2[hi];
+          if ((a > b) == up) {
+            R2[lo] = b;
+            R2[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    uint64_t* t = R;
+    R = R2;
+    R2 = t;
+    if (w0 == k && tid == 0) out[s + W + k - 1] = R[0];  // the k-th candidate completes R
+  }
 
-  for (int32_t c0 = 0; c0 < C; c0 += THR_CHUNK) {
-    const int32_t len = min(THR_CHUNK, C - c0);
-    // ---- 1. this thread's candidate and the entrants --------------------
-    const bool valid = tid < len;
-    uint64_t key = 0ull;
-    if (valid) {
-      const int32_t pos = s + c0 + tid;
-      key = make_key(score_code(sc[pos]), pos);
+  // Chunks: each thread takes a run of V consecutive candidates, V = 1, 2 or
+  // 4; about 1024 * V * k / m candidates of a chunk beat its threshold after
+  // m candidates, so V grows with m while the entrants still fit the
+  // arrays (expected 1024 * V * k / m <= 683; a chunk that overflows them
+  // is redone with V = 1).
+  auto pick_v = [&](int32_t m) { return m >= 6 * k ? 4 : (m >= 3 * k ? 2 : 1); };
+  float xs[4];  // scores of this thread's run, loaded one chunk ahead
+  auto load_run = [&](int32_t c0, int V) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int32_t i = min(c0 + tid * V + v, C - 1);
+      xs[v] = (v < V) ? sc[s + i] : 0.f;
     }
+  };
+  int V = pick_v(w0);
+  if (w0 < C) load_run(w0, V);
+  for (int32_t c0 = w0; c0 < C;) {
+    // ---- 1. this thread's candidates and the entrants ---------------------
     const uint64_t T0 = R[0];
-    const bool ent = valid && key > T0;
-    uint32_t e;
-    const uint32_t before = block_exclusive_scan_u32<THR_THREADS>(ent ? 1u : 0u, scan_buf, &e);
-    const uint32_t q_here = before + (ent ? 1u : 0u);  // entrants up to and including tid
-    if (ent) {
-      arr[before] = key;
-      ak[before] = key;
-      aq[before] = before + 1;
+    uint64_t key[4];
+    uint32_t own;    // entrants in this thread's run
+    uint32_t e, before;
+    int32_t len;
+    for (;;) {
+      len = min(THR_CHUNK * V, C - c0);
+      own = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int32_t i = tid * V + v;  // chunk-relative
+        const bool valid = v < V && i < len;
+        key[v] = valid ? make_key(score_code(xs[v]), s + c0 + i) : 0ull;
+        own += (valid && key[v] > T0) ? 1u : 0u;
+      }
+      before = block_exclusive_scan_u32<THR_THREADS>(own, scan_buf, &e);
+      if (e <= THR_CHUNK) break;
+      V = 1;  // too many entrants for the arrays: redo with one per thread
+      load_run(c0, V);
     }
+    // next chunk's scores go out now; their latency overlaps this chunk
+    const int32_t c_next = c0 + len;
+    const int V_next = pick_v(c_next);
+    uint32_t qv[4];  // entrants up to and including each of this run
+    {
+      uint32_t q = before;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (key[v] > T0) {
+          arr[q] = key[v];
+          ak[q] = key[v];
+          aq[q] = q + 1;
+          ++q;
+        }
+        qv[v] = q;
+      }
+    }
+    if (c_next < C) load_run(c_next, V_next);
     // pad the sort to a power of two with keys above every real key
     uint32_t p2 = 1;
     while (p2 < e) p2 <<= 1;
@@ -99,22 +172,54 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
     }
     __syncthreads();
     // ---- sort the entrants ascending (bitonic, pairs) ---------------------
-    for (uint32_t size = 2; size <= p2; size <<= 1) {
-      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = tid; i < p2 / 2; i += THR_THREADS) {
-          const uint32_t lo = 2 * i - (i & (stride - 1));
-          const uint32_t hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const uint64_t a = ak[lo], b = ak[hi];
-          if ((a > b) == up) {
-            ak[lo] = b;
-            ak[hi] = a;
-            const uint32_t t = aq[lo];
-            aq[lo] = aq[hi];
-            aq[hi] = t;
+    if (p2 <= WAVE) {
+      // one wavefront, in registers: no workgroup barrier per stage
+      if (tid < WAVE) {
+        const int lane = tid;
+        uint64_t kx = ak[lane < static_cast<int>(p2) ? lane : 0];
+        uint32_t qx = aq[lane < static_cast<int>(p2) ? lane : 0];
+        if (lane >= static_cast<int>(p2)) {
+          kx = ~0ull;
+          qx = 0u;
+        }
+        for (uint32_t size = 2; size <= p2; size <<= 1) {
+          for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t ko = __shfl_xor(kx, static_cast<int>(stride), WAVE);
+            const uint32_t qo = __shfl_xor(qx, static_cast<int>(stride), WAVE);
+            const bool up = (lane & size) == 0;
+            const bool lower = (lane & stride) == 0;
+            const bool take_min = (lower == up);
+            const bool other_smaller = ko < kx;
+            if (take_min == other_smaller) {
+              kx = ko;
+              qx = qo;
+            }
           }
         }
-        __syncthreads();
+        if (lane < static_cast<int>(p2)) {
+          ak[lane] = kx;
+          aq[lane] = qx;
+        }
+      }
+      __syncthreads();
+    } else {
+      for (uint32_t size = 2; size <= p2; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+          for (uint32_t i = tid; i < p2 / 2; i += THR_THREADS) {
+            const uint32_t lo = 2 * i - (i & (stride - 1));
+            const uint32_t hi = lo + stride;
+            const bool up = (lo & size) == 0;
+            const uint64_t a = ak[lo], b = ak[hi];
+            if ((a > b) == up) {
+              ak[lo] = b;
+              ak[hi] = a;
+              const uint32_t t = aq[lo];
+              aq[lo] = aq[hi];
+              aq[hi] = t;
+            }
+          }
+          __syncthreads();
+        }
       }
     }
     // ---- 2. threshold after every entrant --------------------------------
@@ -141,18 +246,31 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
         rank = static_cast<int32_t>(j) + below_r;
       }
       if (rank > static_cast<int32_t>(e)) continue;
-      // g(q) = below_r + #(arrivals 1..q below val) - q, non-increasing
-      int32_t cnt = 0;
-      for (uint32_t q = 0; q <= e; ++q) {
-        if (q > 0 && arr[q - 1] < val) ++cnt;
-        const int32_t gq = below_r + cnt - static_cast<int32_t>(q);
-        if (gq < 0) break;
-        if (gq == 0 && q >= avail) tq[q] = val;
+      // g(q) = below_r + #(arrivals 1..q below val) - q never increases;
+      // val is the threshold on the steps q >= avail where g(q) = 0
+      int32_t gq = below_r;  // g(0)
+      uint32_t q = 0;
+      while (gq > 0 && q < e) {
+        gq += (arr[q] < val) ? 0 : -1;  // arrival q + 1
+        ++q;
+      }
+      // now g(q) = 0 (or q = e with g > 0: never the threshold)
+      if (gq == 0) {
+        while (q <= e) {
+          if (q >= avail) tq[q] = val;
+          if (q == e) break;
+          if (!(arr[q] < val)) break;  // g drops below 0 at q + 1
+          ++q;
+        }
       }
     }
     __syncthreads();
     // ---- 3. per-position thresholds ---------------------------------------
-    if (valid) out[s + W + c0 + tid] = tq[q_here];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int32_t i = tid * V + v;
+      if (v < V && i < len) out[s + W + c0 + i] = tq[qv[v]];
+    }
     // ---- 4. R <- the k largest of R and the entrants ----------------------
     for (int32_t i = tid; i < k; i += THR_THREADS) {
       const uint64_t v = R[i];
@@ -168,6 +286,8 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
     uint64_t* t = R;
     R = R2;
     R2 = t;
+    c0 = c_next;
+    V = V_next;
   }
 }
 

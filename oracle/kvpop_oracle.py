@@ -46,6 +46,11 @@ notes of the repository):
    important member of Cand(n) (0 while there are fewer than k, KEY_NONE
    when k = 0), so that the kept set at n is the sinks, the window and the
    candidates whose key reaches it.
+10. The future-attention target (the scorer's training target) sums, for
+    each key, the causal softmax weight that every query of the KV head's
+    group puts on it after the key has left the window; the pages do not say
+    how query heads combine or whether it is normalised (summed here, not
+    normalised).
 
 All arithmetic is float64 on exactly decoded bfloat16 values.
 """
@@ -188,6 +193,50 @@ def prefix_thresholds(scores_g, n_tokens: int, n_sink: int, n_scored: int, n_rec
         else:
             out.append(heap[0])
     return out
+
+
+# ---------------------------------------------------------------------------
+# Future-attention target (the scorer's training target)
+# ---------------------------------------------------------------------------
+
+def future_attention_target(q_bits, k_bits, n_recent: int, scale: float) -> np.ndarray:
+    """Attention mass each key receives from queries that come after it has
+    left the recent window, per KV head.
+
+    y[g][j] = sum over query heads h of group g, and over queries i >= j + W,
+    of softmax_j'(scale * <q_h,i, k_g,j'>) over the causal keys j' <= i,
+    taken at j' = j.  The English aiweekly article (its paragraph on how
+    KVpop defines the right answer) and the French one (second paragraph)
+    define the scorer's target as the attention mass a token will receive
+    from queries that come after it has left the protected recent window,
+    computed in training by a transposed-attention pass (KVpop abstract: no
+    dense attention map is materialised).  How the query heads of a group
+    combine and whether the sum is normalised is not on the pages (reading:
+    summed over the group's query heads and over those queries, not
+    normalised).
+
+    q_bits [Hq][T][D], k_bits [Hkv][T][D] bfloat16 bit patterns; returns
+    float64 [Hkv][T].
+    """
+    Q = bf16_to_f64(q_bits)
+    K = bf16_to_f64(k_bits)
+    Hq, T, _ = Q.shape
+    Hkv = K.shape[0]
+    W = n_recent
+    y = np.zeros((Hkv, T))
+    i_idx = np.arange(T)[:, None]
+    j_idx = np.arange(T)[None, :]
+    causal = j_idx <= i_idx
+    future = i_idx >= j_idx + W
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        logits = scale * (Q[h] @ K[g].T)                  # [i][j]
+        logits = np.where(causal, logits, -np.inf)
+        logits = logits - logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        p = p / p.sum(axis=1, keepdims=True)
+        y[g] += np.where(future, p, 0.0).sum(axis=0)
+    return y
 
 
 # ---------------------------------------------------------------------------

@@ -23,7 +23,7 @@ KVPOP_FLAG_NAN_SCORE = 1
 EXPORTED = ("kvpop_cache_required_bytes", "kvpop_cache_create", "kvpop_cache_destroy",
             "kvpop_cache_reset", "kvpop_prefill_compact", "kvpop_decode_step",
             "kvpop_cache_state", "kvpop_strerror",
-            "kvpop_prefix_thresholds")
+            "kvpop_prefix_thresholds", "kvpop_future_attention_target")
 
 
 class KVpopLibraryMissing(RuntimeError):
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.kvpop_cache_state.restype = ctypes.c_int
     lib.kvpop_prefix_thresholds.argtypes = [vp, i32, vp, vp, vp]
     lib.kvpop_prefix_thresholds.restype = ctypes.c_int
+    lib.kvpop_future_attention_target.argtypes = [vp, i32, vp, vp, vp, vp, vp]
+    lib.kvpop_future_attention_target.restype = ctypes.c_int
     lib.kvpop_strerror.argtypes = [ctypes.c_int]
     lib.kvpop_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -201,7 +203,22 @@ class KVpopCache:
         sp = _dev_ptr(scores, torch.float32, (c.n_kv_heads, P), "scores")
         tp = _dev_ptr(thr, torch.int64, (c.n_kv_heads, P), "thr")
         _check(load().kvpop_prefix_thresholds(self._h, P, sp, tp, _stream_ptr(stream)),
-               "kvpop_prefix_thresholds")
+               "kvpop_prefix_thresholds", "kvpop_future_attention_target")
+
+    def future_attention_target(self, q, k, lse, y, stream=None):
+        """Future-attention target (see the header): q bf16 [Hq][T][D],
+        k bf16 [Hkv][T][D], lse float32 [Hq][T] workspace, y float32
+        [Hkv][T] out."""
+        import torch
+        c = self.cfg
+        T = int(q.shape[1]) if q is not None and q.dim() == 3 else 0
+        qp = _dev_ptr(q, torch.bfloat16, (c.n_q_heads, T, c.head_dim), "q")
+        kp = _dev_ptr(k, torch.bfloat16, (c.n_kv_heads, T, c.head_dim), "k")
+        lp = _dev_ptr(lse, torch.float32, (c.n_q_heads, T), "lse")
+        yp = _dev_ptr(y, torch.float32, (c.n_kv_heads, T), "y")
+        _check(load().kvpop_future_attention_target(self._h, T, qp, kp, lp, yp,
+                                                    _stream_ptr(stream)),
+               "kvpop_future_attention_target")
 
     def state(self, layer: int, seq: int, stream=None) -> HeadState:
         c = self.cfg

@@ -1,0 +1,270 @@
+// Future-attention target for gfx950: for every KV head g and key j,
+//   y[g][j] = sum over the query heads h of g's group and the queries
+//             i >= j + W of the causal softmax weight of query i on key j,
+// the attention mass a token receives after it has left the protected
+// recent window (English and French aiweekly articles: the scorer's
+// training target, computed with a transposed-attention pass so that no
+// dense attention map is materialised; summing over the group's query heads,
+// unnormalised, is the reading taken).
+//
+// Two passes, FlashAttention-backward style, on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   pass 1  per (query head, 128-query tile): S^T = K . Q^T over the causal
+//           key tiles, online row log-sum-exp in the log2 domain -> lse[h][i].
+//   pass 2  per (KV head, 128-key tile): for each query head of the group and
+//           each 64-query tile with queries >= key + W, P = 2^(c S - lse),
+//           summed over the queries -> y[g][j].
+// S^T puts keys on the MFMA rows and queries on its columns: a lane holds 16
+// keys of one query, so the row reductions of pass 1 are in-lane plus one
+// swap of wave halves, and pass 2 sums columns in-lane until one final
+// reduction.  Operand layouts (checked on the hardware): A row l%32, k
+// 8*(l/32)+0..7; B k 8*(l/32)+0..7, column l%32; C column l%32, row
+// 8*(r/4) + 4*(l/32) + r%4.
+#include <hip/hip_runtime.h>
+
+#include "kvpop_device.h"
+#include "kvpop_internal.h"
+
+namespace kvpop {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int FT_THREADS = 256;   // 4 waves
+constexpr int FT_ROWS = 128;      // queries (pass 1) or keys (pass 2) per workgroup
+constexpr int FT_TILE = 64;       // keys (pass 1) or queries (pass 2) per LDS tile
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One 64-row tile of a [rows][D] bf16 matrix into LDS (row stride D + 8
+// elements: neighbouring rows start 4 banks apart).  Rows past `nrows` read
+// the last valid row (their results are masked).  Coalesced 16-byte pieces.
+template <int D>
+struct TileLoader {
+  static constexpr int PIECES = D / 8;                       // 16-byte pieces per row
+  static constexpr int PER_THREAD = FT_TILE * PIECES / FT_THREADS;
+  uint4 buf[PER_THREAD];
+  __device__ __forceinline__ void load(const uint16_t* src, int32_t row0, int32_t nrows) {
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int p = threadIdx.x + u * FT_THREADS;
+      const int32_t r = min(row0 + p / PIECES, nrows - 1);
+      buf[u] = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r) * D)[p % PIECES];
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int p = threadIdx.x + u * FT_THREADS;
+      *reinterpret_cast<uint4*>(lds + (p / PIECES) * (D + 8) + (p % PIECES) * 8) = buf[u];
+    }
+  }
+};
+
+// The 32-row operand of one wave held in registers: lane l keeps row
+// row0 + l%32, elements 16*ks + 8*(l/32) .. +7 for every k-step ks.
+template <int D>
+__device__ __forceinline__ void load_operand_rows(const uint16_t* src, int32_t row0, int32_t nrows,
+                                                  uint4 (&op)[D / 16]) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int32_t r = min(row0 + (lane & 31), nrows - 1);
+  const uint16_t* p = src + static_cast<int64_t>(r) * D + 8 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) op[ks] = *reinterpret_cast<const uint4*>(p + 16 * ks);
+}
+
+// S^T block (32 LDS rows x 32 register columns): acc += A(LDS rows) . B(regs)
+template <int D>
+__device__ __forceinline__ void mfma_block(const uint16_t* lds_rows, const uint4 (&breg)[D / 16],
+                                           f32x16_t& acc) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const uint16_t* a = lds_rows + (lane & 31) * (D + 8) + 8 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint4 av = *reinterpret_cast<const uint4*>(a + 16 * ks);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(breg[ks]), acc, 0, 0, 0);
+  }
+}
+
+// ---- pass 1: log2-domain log-sum-exp of every query row --------------------
+template <int D>
+__global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int32_t T, int32_t Hq,
+    int32_t Hkv, float c2, float* __restrict__ lse) {
+  __shared__ __align__(16) uint16_t ktile[2][FT_TILE * (D + 8)];
+  const int h = blockIdx.y;
+  const int g = (h * Hkv) / Hq;
+  // largest tiles (most keys) first
+  const int32_t i0 = (static_cast<int32_t>(gridDim.x - 1 - blockIdx.x)) * FT_ROWS;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  const uint16_t* qh = q + static_cast<int64_t>(h) * T * D;
+  const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
+  const int32_t iw = i0 + 32 * wid;          // this wave's first query
+  const int32_t my_q = iw + (lane & 31);     // this lane's query (column)
+  uint4 qreg[D / 16];
+  load_operand_rows<D>(qh, iw, T, qreg);
+  const int32_t ilast = min(i0 + FT_ROWS, T) - 1;
+  const int ntile = ilast / FT_TILE + 1;      // key tiles 0 .. ilast/64
+  TileLoader<D> ld;
+  ld.load(kg, 0, T);
+  ld.store(ktile[0]);
+  __syncthreads();
+  float m = -INFINITY, ssum = 0.f;
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 1 < ntile) ld.load(kg, (t + 1) * FT_TILE, T);
+    const uint16_t* kt = ktile[t & 1];
+    if (iw <= ilast && t * FT_TILE <= iw + 31) {  // the wave has unmasked work
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16_t acc = {};
+        mfma_block<D>(kt + 32 * kb * (D + 8), qreg, acc);
+        const int32_t key0 = t * FT_TILE + 32 * kb + 4 * (lane >> 5);
+        float x[16], mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
+          x[r] = (key <= my_q && key < T) ? acc[r] * c2 : -INFINITY;
+          mx = fmaxf(mx, x[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float mnew = fmaxf(m, mx);
+        if (mnew != -INFINITY) {
+          float part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part += __builtin_amdgcn_exp2f(x[r] - mnew);
+          part += __shfl_xor(part, 32, WAVE);
+          ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
+          m = mnew;
+        }
+      }
+    }
+    if (t + 1 < ntile) {
+      ld.store(ktile[(t + 1) & 1]);
+    }
+    __syncthreads();
+  }
+  if (lane < 32 && my_q < T) lse[static_cast<int64_t>(h) * T + my_q] = m + __log2f(ssum);
+}
+
+// ---- pass 2: column sums of the probabilities of queries past the window --
+template <int D>
+__global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
+    int32_t T, int32_t Hq, int32_t Hkv, int32_t W, float c2, float* __restrict__ y) {
+  __shared__ __align__(16) uint16_t qtile[2][FT_TILE * (D + 8)];
+  __shared__ float ltile[2][FT_TILE];
+  const int g = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int32_t j0 = static_cast<int32_t>(blockIdx.x) * FT_ROWS;  // earliest keys: most queries
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
+  const int32_t jw = j0 + 32 * wid;          // this wave's first key
+  uint4 kreg[D / 16];
+  load_operand_rows<D>(kg, jw, T, kreg);
+  // this lane's 16 keys: jw + 8*(r/4) + 4*(lane/32) + r%4
+  float col[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) col[r] = 0.f;
+  const int32_t qfirst = j0 + W;              // first query any key of the tile counts
+  const int t0 = qfirst / FT_TILE;
+  const int ntile = (qfirst < T) ? (T - 1) / FT_TILE + 1 - t0 : 0;
+  const int nsteps = ntile * G;               // (head, query tile) pairs
+  TileLoader<D> ld;
+  float lreg = 0.f;
+  auto fetch = [&](int step) {
+    const int hh = g * G + step / ntile;
+    const int32_t qrow0 = (t0 + step % ntile) * FT_TILE;
+    ld.load(q + static_cast<int64_t>(hh) * T * D, qrow0, T);
+    if (tid < FT_TILE) lreg = lse[static_cast<int64_t>(hh) * T + min(qrow0 + tid, T - 1)];
+  };
+  if (nsteps > 0) {
+    fetch(0);
+    ld.store(qtile[0]);
+    if (tid < FT_TILE) ltile[0][tid] = lreg;
+  }
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    if (step + 1 < nsteps) fetch(step + 1);
+    const int buf = step & 1;
+    const int32_t qrow0 = (t0 + step % ntile) * FT_TILE;
+    if (jw < T && qrow0 + FT_TILE - 1 >= jw + W) {  // some query of the tile counts
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // B operand: 32 queries of the tile, from LDS
+        const uint16_t* bq = qtile[buf] + (32 * qb + (lane & 31)) * (D + 8) + 8 * (lane >> 5);
+        uint4 breg[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) breg[ks] = *reinterpret_cast<const uint4*>(bq + 16 * ks);
+        // S^T = K (rows: this wave's keys, registers) . Q^T (columns)
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(breg[ks]),
+                                                        acc, 0, 0, 0);
+        const int32_t qi = qrow0 + 32 * qb + (lane & 31);  // this lane's query
+        const float l2 = ltile[buf][32 * qb + (lane & 31)];
+        const int32_t key0 = jw + 4 * (lane >> 5);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
+          const bool live = qi < T && key < T && qi >= key + W;
+          col[r] += live ? __builtin_amdgcn_exp2f(acc[r] * c2 - l2) : 0.f;
+        }
+      }
+    }
+    if (step + 1 < nsteps) {
+      ld.store(qtile[buf ^ 1]);
+      if (tid < FT_TILE) ltile[buf ^ 1][tid] = lreg;
+    }
+    __syncthreads();
+  }
+  // every key's sum is spread over the 32 query lanes of its wave half
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = col[r];
+    v += __shfl_xor(v, 1, WAVE);
+    v += __shfl_xor(v, 2, WAVE);
+    v += __shfl_xor(v, 4, WAVE);
+    v += __shfl_xor(v, 8, WAVE);
+    v += __shfl_xor(v, 16, WAVE);
+    col[r] = v;
+  }
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t key = jw + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
+      if (key < T) y[static_cast<int64_t>(g) * T + key] = col[r];
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_future_d(int32_t T, int32_t Hq, int32_t Hkv, int32_t W, float c2,
+                           const uint16_t* q, const uint16_t* k, float* lse, float* y,
+                           hipStream_t stream) {
+  const uint32_t tiles = static_cast<uint32_t>((T + FT_ROWS - 1) / FT_ROWS);
+  hipLaunchKernelGGL(future_lse_kernel<D>, dim3(tiles, static_cast<uint32_t>(Hq)), dim3(FT_THREADS),
+                     0, stream, q, k, T, Hq, Hkv, c2, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(future_colsum_kernel<D>, dim3(tiles, static_cast<uint32_t>(Hkv)),
+                     dim3(FT_THREADS), 0, stream, q, k, lse, T, Hq, Hkv, W, c2, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uint16_t* q,
+                                const uint16_t* k, float scale, float* lse, float* y,
+                                hipStream_t stream) {
+  if (n_tokens <= 0) return hipSuccess;
+  const float c2 = scale * 1.4426950408889634f;
+  if (geo.head_dim == 128)
+    return launch_future_d<128>(n_tokens, geo.n_q_heads, geo.n_kv_heads, geo.n_recent, c2, q, k,
+                                lse, y, stream);
+  return launch_future_d<64>(n_tokens, geo.n_q_heads, geo.n_kv_heads, geo.n_recent, c2, q, k, lse,
+                             y, stream);
+}
+
+}  // namespace kvpop

@@ -84,6 +84,11 @@ hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq,
 constexpr int THR_KMAX = 4096;
 hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const float* scores,
                                     uint64_t* thr, hipStream_t stream);
+// Future-attention target of one sequence: lse [Hq][n_tokens] f32 workspace
+// (log2-domain row log-sum-exp), y [Hkv][n_tokens] f32 output.
+hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uint16_t* q,
+                                const uint16_t* k, float scale, float* lse, float* y,
+                                hipStream_t stream);
 // Largest split count the decode kernel accepts, and whether a launch shape
 // (head_dim, group size, workgroup size, rows per thread) is compiled.
 int decode_max_splits();

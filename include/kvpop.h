@@ -178,6 +178,27 @@ KVPOP_API int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, 
 KVPOP_API int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, const float* scores,
                                       uint64_t* thr, void* stream);
 
+/* Future-attention target of one sequence: the attention mass each key
+ * receives from queries that come after it has left the protected recent
+ * window (the target the scorer is trained against: English and French
+ * aiweekly articles, KVpop abstract; computed, as they describe, by a
+ * transposed-attention pass that never materialises the attention map).
+ * With the cache's geometry and softmax scale c, and no access to its state:
+ *   q    device [Hq][n_tokens][D] bf16, the queries of every position
+ *   k    device [Hkv][n_tokens][D] bf16, the keys of every position
+ *   lse  device [Hq][n_tokens] float32 workspace (receives each query's
+ *        causal log-sum-exp in log2 units)
+ *   y    device [Hkv][n_tokens] float32 (output):
+ *        y[g][j] = sum over the query heads h of g's group and the queries
+ *        i >= j + n_recent of softmax over j' <= i of c <q_h,i, k_g,j'>, at
+ *        j' = j.  Summed over the group's query heads, not normalised (the
+ *        pages leave both open; this is the reading taken).
+ * Stream-ordered and asynchronous; the caller owns every buffer.  Errors:
+ * KVPOP_EINVAL (NULL pointers, n_tokens < 0), KVPOP_ESTATE (n_tokens >
+ * max_positions or poisoned), KVPOP_EHIP. */
+KVPOP_API int kvpop_future_attention_target(kvpop_cache* cache, int32_t n_tokens, const uint16_t* q,
+                                            const uint16_t* k, float* lse, float* y, void* stream);
+
 /* Static description of a return code. */
 KVPOP_API const char* kvpop_strerror(int code);
 

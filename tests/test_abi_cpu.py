@@ -108,6 +108,7 @@ def test_null_cache_handle_everywhere(lib):
     assert lib.kvpop_cache_state(None, 0, 0, ctypes.byref(st), None, None, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_cache_reset(None, 0, 0, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_prefix_thresholds(None, 4, 1, 1, None) == abi.KVPOP_EINVAL
+    assert lib.kvpop_future_attention_target(None, 4, 1, 1, 1, 1, None) == abi.KVPOP_EINVAL
     lib.kvpop_cache_destroy(None)
 
 

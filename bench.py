@@ -337,6 +337,40 @@ def prefix_thresholds_rate(w, reps: int):
             "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "bytes": nbytes}
 
 
+def future_target_rate(w, reps: int):
+    """Time kvpop_future_attention_target over one prompt of the workload
+    (both passes): the algorithmic flops are the two causal products
+    (2 * D per (query, key) pair: every causal pair in the log-sum-exp pass,
+    the pairs with query >= key + W in the column pass) per query head."""
+    import torch
+    from fixed_budget_learned_amd import abi
+    Hq, Hkv, D, W, T = w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_recent, w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4000 + w.wid)
+    q = torch.randn((Hq, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((Hkv, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    y = torch.empty((Hkv, T), dtype=torch.float32, device="cuda")
+    cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, w.n_scored, W,
+                                           max_positions=T))
+    cache.future_attention_target(q, k, lse, y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        cache.future_attention_target(q, k, lse, y)
+    e1.record()
+    torch.cuda.synchronize()
+    cache.close()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    pairs = T * (T + 1) / 2 + max(0, T - W) * (T - W + 1) / 2
+    flops = Hq * pairs * 2 * D
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": w.name, "tokens": T, "us_per_call": us, "TFLOPs": tf,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": tf / 2500.0, "flops_per_call": flops}}
+
+
 def batched_serving(steps: int, reps: int, mode: str = "graph"):
     """Batched serving: 64 sequences of the Qwen3-8B layer shape with 4,032
     slots per KV head, prompts uniform in [4096, 32768] (seeded), scores
@@ -609,6 +643,7 @@ def main():
     if not args.no_configs:
         from fixed_budget_learned_amd.configs import (LONG_131K_8X, QWEN3_8B_36L_4X, TINY)
         result["decode_cold_cache"] = decode_cold(w, 32)
+        result["future_attention_target"] = future_target_rate(w, 3)
         result["prefix_thresholds"] = [prefix_thresholds_rate(w, 5),
                                        prefix_thresholds_rate(LONG_131K_8X, 3)]
         result["configs"] = [layered_config(TINY, 512, 2),

@@ -203,7 +203,7 @@ class KVpopCache:
         sp = _dev_ptr(scores, torch.float32, (c.n_kv_heads, P), "scores")
         tp = _dev_ptr(thr, torch.int64, (c.n_kv_heads, P), "thr")
         _check(load().kvpop_prefix_thresholds(self._h, P, sp, tp, _stream_ptr(stream)),
-               "kvpop_prefix_thresholds", "kvpop_future_attention_target")
+               "kvpop_prefix_thresholds")
 
     def future_attention_target(self, q, k, lse, y, stream=None):
         """Future-attention target (see the header): q bf16 [Hq][T][D],

@@ -30,12 +30,13 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int FT_THREADS = 256;   // 4 waves
 constexpr int FT_ROWS = 128;      // queries (pass 1) or keys (pass 2) per workgroup
 constexpr int FT_TILE = 64;       // keys (pass 1) or queries (pass 2) per LDS tile
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // One 64-row tile of a [rows][D] bf16 matrix into LDS (row stride D + 8
 // elements: neighbouring rows start 4 banks apart).  Rows past `nrows` read
@@ -44,20 +45,20 @@ template <int D>
 struct TileLoader {
   static constexpr int PIECES = D / 8;                       // 16-byte pieces per row
   static constexpr int PER_THREAD = FT_TILE * PIECES / FT_THREADS;
-  uint4 buf[PER_THREAD];
+  u32x4_t buf[PER_THREAD];
   __device__ __forceinline__ void load(const uint16_t* src, int32_t row0, int32_t nrows) {
 #pragma unroll
     for (int u = 0; u < PER_THREAD; ++u) {
       const int p = threadIdx.x + u * FT_THREADS;
       const int32_t r = min(row0 + p / PIECES, nrows - 1);
-      buf[u] = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r) * D)[p % PIECES];
+      buf[u] = reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(r) * D)[p % PIECES];
     }
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
     for (int u = 0; u < PER_THREAD; ++u) {
       const int p = threadIdx.x + u * FT_THREADS;
-      *reinterpret_cast<uint4*>(lds + (p / PIECES) * (D + 8) + (p % PIECES) * 8) = buf[u];
+      *reinterpret_cast<u32x4_t*>(lds + (p / PIECES) * (D + 8) + (p % PIECES) * 8) = buf[u];
     }
   }
 };
@@ -66,25 +67,22 @@ struct TileLoader {
 // row0 + l%32, elements 16*ks + 8*(l/32) .. +7 for every k-step ks.
 template <int D>
 __device__ __forceinline__ void load_operand_rows(const uint16_t* src, int32_t row0, int32_t nrows,
-                                                  uint4 (&op)[D / 16]) {
+                                                  u32x4_t (&op)[D / 16]) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int32_t r = min(row0 + (lane & 31), nrows - 1);
   const uint16_t* p = src + static_cast<int64_t>(r) * D + 8 * (lane >> 5);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) op[ks] = *reinterpret_cast<const uint4*>(p + 16 * ks);
+  for (int ks = 0; ks < D / 16; ++ks) op[ks] = *reinterpret_cast<const u32x4_t*>(p + 16 * ks);
 }
 
-// S^T block (32 LDS rows x 32 register columns): acc += A(LDS rows) . B(regs)
-template <int D>
-__device__ __forceinline__ void mfma_block(const uint16_t* lds_rows, const uint4 (&breg)[D / 16],
-                                           f32x16_t& acc) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const uint16_t* a = lds_rows + (lane & 31) * (D + 8) + 8 * (lane >> 5);
+// An empty register-to-register statement that reads and rewrites the
+// operand: the compiler completes its loads here and can neither sink them
+// into the main loop nor count them among that loop's outstanding loads
+// (whose waits would then also hold back the next tile's prefetch).
+template <int N>
+__device__ __forceinline__ void settle(u32x4_t (&op)[N]) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const uint4 av = *reinterpret_cast<const uint4*>(a + 16 * ks);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(breg[ks]), acc, 0, 0, 0);
-  }
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(op[i]));
 }
 
 // ---- pass 1: log2-domain log-sum-exp of every query row --------------------
@@ -102,43 +100,66 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
   const int32_t iw = i0 + 32 * wid;          // this wave's first query
   const int32_t my_q = iw + (lane & 31);     // this lane's query (column)
-  uint4 qreg[D / 16];
+  u32x4_t qreg[D / 16];
   load_operand_rows<D>(qh, iw, T, qreg);
+  __builtin_amdgcn_sched_barrier(0);
   const int32_t ilast = min(i0 + FT_ROWS, T) - 1;
   const int ntile = ilast / FT_TILE + 1;      // key tiles 0 .. ilast/64
   TileLoader<D> ld;
   ld.load(kg, 0, T);
   ld.store(ktile[0]);
+  settle(qreg);
   __syncthreads();
   float m = -INFINITY, ssum = 0.f;
   for (int t = 0; t < ntile; ++t) {
     if (t + 1 < ntile) ld.load(kg, (t + 1) * FT_TILE, T);
+    // keep the next tile's LDS stores after this tile's math, so that its
+    // loads stay in flight meanwhile
+    __builtin_amdgcn_sched_barrier(0);
     const uint16_t* kt = ktile[t & 1];
     if (iw <= ilast && t * FT_TILE <= iw + 31) {  // the wave has unmasked work
+      // both 32-key blocks of the tile as two independent MFMA chains
+      f32x16_t acc0 = {}, acc1 = {};
+      {
+        const uint16_t* a0 = kt + (lane & 31) * (D + 8) + 8 * (lane >> 5);
+        const uint16_t* a1 = a0 + 32 * (D + 8);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t acc = {};
-        mfma_block<D>(kt + 32 * kb * (D + 8), qreg, acc);
-        const int32_t key0 = t * FT_TILE + 32 * kb + 4 * (lane >> 5);
-        float x[16], mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
-          x[r] = (key <= my_q && key < T) ? acc[r] * c2 : -INFINITY;
-          mx = fmaxf(mx, x[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float mnew = fmaxf(m, mx);
-        if (mnew != -INFINITY) {
-          float part = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) part += __builtin_amdgcn_exp2f(x[r] - mnew);
-          part += __shfl_xor(part, 32, WAVE);
-          ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
-          m = mnew;
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4_t av0 = *reinterpret_cast<const u32x4_t*>(a0 + 16 * ks);
+          const u32x4_t av1 = *reinterpret_cast<const u32x4_t*>(a1 + 16 * ks);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av0), as_bf16x8(qreg[ks]),
+                                                         acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av1), as_bf16x8(qreg[ks]),
+                                                         acc1, 0, 0, 0);
         }
       }
+      // keys of the tile past this wave's first query need the causal mask
+      const bool diag = t * FT_TILE + FT_TILE - 1 > iw || t * FT_TILE + FT_TILE > T;
+      const int32_t key0 = t * FT_TILE + 4 * (lane >> 5);
+      float x[32], mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const float v = (r < 16 ? acc0[r] : acc1[r - 16]) * c2;
+        if (diag) {
+          const int32_t key = key0 + 32 * (r >> 4) + 8 * ((r & 15) >> 2) + (r & 3);
+          x[r] = (key <= my_q && key < T) ? v : -INFINITY;
+        } else {
+          x[r] = v;
+        }
+        mx = fmaxf(mx, x[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float mnew = fmaxf(m, mx);
+      if (mnew != -INFINITY) {
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) part += __builtin_amdgcn_exp2f(x[r] - mnew);
+        part += __shfl_xor(part, 32, WAVE);
+        ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
+        m = mnew;
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < ntile) {
       ld.store(ktile[(t + 1) & 1]);
     }
@@ -160,8 +181,9 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
   const int32_t jw = j0 + 32 * wid;          // this wave's first key
-  uint4 kreg[D / 16];
+  u32x4_t kreg[D / 16];
   load_operand_rows<D>(kg, jw, T, kreg);
+  __builtin_amdgcn_sched_barrier(0);
   // this lane's 16 keys: jw + 8*(r/4) + 4*(lane/32) + r%4
   float col[16];
 #pragma unroll
@@ -183,36 +205,52 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
     ld.store(qtile[0]);
     if (tid < FT_TILE) ltile[0][tid] = lreg;
   }
+  settle(kreg);
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) fetch(step + 1);
+    // keep the next tile's LDS stores after this tile's math, so that its
+    // loads stay in flight meanwhile
+    __builtin_amdgcn_sched_barrier(0);
     const int buf = step & 1;
     const int32_t qrow0 = (t0 + step % ntile) * FT_TILE;
     if (jw < T && qrow0 + FT_TILE - 1 >= jw + W) {  // some query of the tile counts
+      // both 32-query blocks of the tile as two independent MFMA chains
+      f32x16_t acc0 = {}, acc1 = {};
+      {
+        const uint16_t* b0 = qtile[buf] + (lane & 31) * (D + 8) + 8 * (lane >> 5);
+        const uint16_t* b1 = b0 + 32 * (D + 8);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4_t bv0 = *reinterpret_cast<const u32x4_t*>(b0 + 16 * ks);
+          const u32x4_t bv1 = *reinterpret_cast<const u32x4_t*>(b1 + 16 * ks);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(bv0),
+                                                         acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(bv1),
+                                                         acc1, 0, 0, 0);
+        }
+      }
+      // every (query, key) pair of the tile counts when its first query is
+      // at least W past this wave's last key and the tile ends before T
+      const bool full = qrow0 >= jw + 31 + W && qrow0 + FT_TILE <= T && jw + 32 <= T;
+      const int32_t key0 = jw + 4 * (lane >> 5);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        // B operand: 32 queries of the tile, from LDS
-        const uint16_t* bq = qtile[buf] + (32 * qb + (lane & 31)) * (D + 8) + 8 * (lane >> 5);
-        uint4 breg[D / 16];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) breg[ks] = *reinterpret_cast<const uint4*>(bq + 16 * ks);
-        // S^T = K (rows: this wave's keys, registers) . Q^T (columns)
-        f32x16_t acc = {};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(breg[ks]),
-                                                        acc, 0, 0, 0);
         const int32_t qi = qrow0 + 32 * qb + (lane & 31);  // this lane's query
         const float l2 = ltile[buf][32 * qb + (lane & 31)];
-        const int32_t key0 = jw + 4 * (lane >> 5);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
-          const bool live = qi < T && key < T && qi >= key + W;
-          col[r] += live ? __builtin_amdgcn_exp2f(acc[r] * c2 - l2) : 0.f;
+          const float p = __builtin_amdgcn_exp2f((qb == 0 ? acc0[r] : acc1[r]) * c2 - l2);
+          if (full) {
+            col[r] += p;
+          } else {
+            const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
+            col[r] += (qi < T && key < T && qi >= key + W) ? p : 0.f;
+          }
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (step + 1 < nsteps) {
       ld.store(qtile[buf ^ 1]);
       if (tid < FT_TILE) ltile[buf ^ 1][tid] = lreg;

@@ -30,6 +30,11 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
+# Per-file additions.  The MFMA kernels keep their accumulators in ordinary
+# VGPRs: the softmax reads every accumulator element, and from AGPRs each
+# read would be one more VALU instruction.
+FILE_FLAGS = {"kvpop_future.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -59,7 +64,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        jobs.append([hipcc] + COMMON_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc] + COMMON_FLAGS + FILE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()

@@ -95,7 +95,10 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
   const int g = (h * Hkv) / Hq;
   // largest tiles (most keys) first
   const int32_t i0 = (static_cast<int32_t>(gridDim.x - 1 - blockIdx.x)) * FT_ROWS;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  // the wave index is uniform across the wave: said so, the per-wave tests
+  // below become scalar branches instead of per-lane masks
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const uint16_t* qh = q + static_cast<int64_t>(h) * T * D;
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
   const int32_t iw = i0 + 32 * wid;          // this wave's first query
@@ -133,27 +136,28 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
                                                          acc1, 0, 0, 0);
         }
       }
-      // keys of the tile past this wave's first query need the causal mask
-      const bool diag = t * FT_TILE + FT_TILE - 1 > iw || t * FT_TILE + FT_TILE > T;
-      const int32_t key0 = t * FT_TILE + 4 * (lane >> 5);
-      float x[32], mx = -INFINITY;
+      float x[32];
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const float v = (r < 16 ? acc0[r] : acc1[r - 16]) * c2;
-        if (diag) {
+      for (int r = 0; r < 32; ++r) x[r] = r < 16 ? acc0[r] : acc1[r - 16];
+      // keys of the tile past this wave's first query need the causal mask
+      if (t * FT_TILE + FT_TILE - 1 > iw || t * FT_TILE + FT_TILE > T) {
+        const int32_t key0 = t * FT_TILE + 4 * (lane >> 5);
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
           const int32_t key = key0 + 32 * (r >> 4) + 8 * ((r & 15) >> 2) + (r & 3);
-          x[r] = (key <= my_q && key < T) ? v : -INFINITY;
-        } else {
-          x[r] = v;
+          x[r] = (key <= my_q && key < T) ? x[r] : -INFINITY;
         }
-        mx = fmaxf(mx, x[r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      // the scale is positive: the largest scaled logit is the scaled maximum
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * c2;
       const float mnew = fmaxf(m, mx);
       if (mnew != -INFINITY) {
         float part = 0.f;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) part += __builtin_amdgcn_exp2f(x[r] - mnew);
+        for (int r = 0; r < 32; ++r) part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -mnew));
         part += __shfl_xor(part, 32, WAVE);
         ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
         m = mnew;
@@ -178,7 +182,8 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
   const int g = blockIdx.y;
   const int G = Hq / Hkv;
   const int32_t j0 = static_cast<int32_t>(blockIdx.x) * FT_ROWS;  // earliest keys: most queries
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
   const int32_t jw = j0 + 32 * wid;          // this wave's first key
   u32x4_t kreg[D / 16];

@@ -349,16 +349,16 @@ def future_target_rate(w, reps: int):
     gen.manual_seed(4000 + w.wid)
     q = torch.randn((Hq, T, D), generator=gen, device="cuda").to(torch.bfloat16)
     k = torch.randn((Hkv, T, D), generator=gen, device="cuda").to(torch.bfloat16)
-    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    work = torch.empty((2, Hq, T), dtype=torch.float32, device="cuda")
     y = torch.empty((Hkv, T), dtype=torch.float32, device="cuda")
     cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, w.n_scored, W,
                                            max_positions=T))
-    cache.future_attention_target(q, k, lse, y)
+    cache.future_attention_target(q, k, work, y)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        cache.future_attention_target(q, k, lse, y)
+        cache.future_attention_target(q, k, work, y)
     e1.record()
     torch.cuda.synchronize()
     cache.close()

@@ -205,18 +205,19 @@ class KVpopCache:
         _check(load().kvpop_prefix_thresholds(self._h, P, sp, tp, _stream_ptr(stream)),
                "kvpop_prefix_thresholds")
 
-    def future_attention_target(self, q, k, lse, y, stream=None):
+    def future_attention_target(self, q, k, work, y, stream=None):
         """Future-attention target (see the header): q bf16 [Hq][T][D],
-        k bf16 [Hkv][T][D], lse float32 [Hq][T] workspace, y float32
-        [Hkv][T] out."""
+        k bf16 [Hkv][T][D], work float32 [2][Hq][T] workspace (work[0]
+        receives the log2-domain log-sum-exps, work[1] each query head's
+        share), y float32 [Hkv][T] out."""
         import torch
         c = self.cfg
         T = int(q.shape[1]) if q is not None and q.dim() == 3 else 0
         qp = _dev_ptr(q, torch.bfloat16, (c.n_q_heads, T, c.head_dim), "q")
         kp = _dev_ptr(k, torch.bfloat16, (c.n_kv_heads, T, c.head_dim), "k")
-        lp = _dev_ptr(lse, torch.float32, (c.n_q_heads, T), "lse")
+        wp = _dev_ptr(work, torch.float32, (2, c.n_q_heads, T), "work")
         yp = _dev_ptr(y, torch.float32, (c.n_kv_heads, T), "y")
-        _check(load().kvpop_future_attention_target(self._h, T, qp, kp, lp, yp,
+        _check(load().kvpop_future_attention_target(self._h, T, qp, kp, wp, yp,
                                                     _stream_ptr(stream)),
                "kvpop_future_attention_target")
 

@@ -323,18 +323,17 @@ int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, const float* s
 }
 
 int kvpop_future_attention_target(kvpop_cache* cache, int32_t n_tokens, const uint16_t* q,
-                                  const uint16_t* k, float* lse, float* y, void* stream) {
+                                  const uint16_t* k, float* work, float* y, void* stream) {
   if (cache == nullptr || n_tokens < 0) return KVPOP_EINVAL;
   const kvpop_config& c = cache->cfg;
   if (cache->poisoned) return KVPOP_ESTATE;
   if (n_tokens > c.max_positions) return KVPOP_ESTATE;
   if (n_tokens == 0) return KVPOP_OK;
-  if (q == nullptr || k == nullptr || lse == nullptr || y == nullptr) return KVPOP_EINVAL;
+  if (q == nullptr || k == nullptr || work == nullptr || y == nullptr) return KVPOP_EINVAL;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
-  const float scale = cache->scale_log2e / 1.4426950408889634f;
-  hipError_t e = kvpop::launch_future_target(cache->geo(), n_tokens, q, k, scale, lse, y,
-                                             static_cast<hipStream_t>(stream));
+  hipError_t e = kvpop::launch_future_target(cache->geo(), n_tokens, q, k, cache->scale_log2e,
+                                             work, y, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;
     return KVPOP_EHIP;

@@ -8,12 +8,18 @@
 // unnormalised, is the reading taken).
 //
 // Two passes, FlashAttention-backward style, on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate), and a group sum:
 //   pass 1  per (query head, 128-query tile): S^T = K . Q^T over the causal
 //           key tiles, online row log-sum-exp in the log2 domain -> lse[h][i].
-//   pass 2  per (KV head, 128-key tile): for each query head of the group and
-//           each 64-query tile with queries >= key + W, P = 2^(c S - lse),
-//           summed over the queries -> y[g][j].
+//   pass 2  per (query head, 128-key tile): for each 64-query tile with
+//           queries >= key + W, P = 2^(c S - lse), summed over the queries
+//           -> part[h][j].
+//   sum     y[g][j] = sum of part[h][j] over the group's heads, in head order.
+// Splitting pass 2 by query head rather than by KV head keeps its longest
+// workgroup to one head's queries (the first key tile sees every query), and
+// the fixed-order group sum keeps the result deterministic.
+// Both passes launch the largest tiles (most work) first: the grid's x is the
+// head, its y the tile.
 // S^T puts keys on the MFMA rows and queries on its columns: a lane holds 16
 // keys of one query, so the row reductions of pass 1 are in-lane plus one
 // swap of wave halves, and pass 2 sums columns in-lane until one final
@@ -91,10 +97,10 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int32_t T, int32_t Hq,
     int32_t Hkv, float c2, float* __restrict__ lse) {
   __shared__ __align__(16) uint16_t ktile[2][FT_TILE * (D + 8)];
-  const int h = blockIdx.y;
+  const int h = blockIdx.x;
   const int g = (h * Hkv) / Hq;
   // largest tiles (most keys) first
-  const int32_t i0 = (static_cast<int32_t>(gridDim.x - 1 - blockIdx.x)) * FT_ROWS;
+  const int32_t i0 = (static_cast<int32_t>(gridDim.y - 1 - blockIdx.y)) * FT_ROWS;
   // the wave index is uniform across the wave: said so, the per-wave tests
   // below become scalar branches instead of per-lane masks
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
@@ -176,12 +182,12 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
 template <int D>
 __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
-    int32_t T, int32_t Hq, int32_t Hkv, int32_t W, float c2, float* __restrict__ y) {
+    int32_t T, int32_t Hq, int32_t Hkv, int32_t W, float c2, float* __restrict__ part) {
   __shared__ __align__(16) uint16_t qtile[2][FT_TILE * (D + 8)];
   __shared__ float ltile[2][FT_TILE];
-  const int g = blockIdx.y;
-  const int G = Hq / Hkv;
-  const int32_t j0 = static_cast<int32_t>(blockIdx.x) * FT_ROWS;  // earliest keys: most queries
+  const int h = blockIdx.x;
+  const int g = (h * Hkv) / Hq;
+  const int32_t j0 = static_cast<int32_t>(blockIdx.y) * FT_ROWS;  // earliest keys: most queries
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
@@ -195,15 +201,15 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
   for (int r = 0; r < 16; ++r) col[r] = 0.f;
   const int32_t qfirst = j0 + W;              // first query any key of the tile counts
   const int t0 = qfirst / FT_TILE;
-  const int ntile = (qfirst < T) ? (T - 1) / FT_TILE + 1 - t0 : 0;
-  const int nsteps = ntile * G;               // (head, query tile) pairs
+  const int nsteps = (qfirst < T) ? (T - 1) / FT_TILE + 1 - t0 : 0;  // query tiles
+  const uint16_t* qh = q + static_cast<int64_t>(h) * T * D;
+  const float* lh = lse + static_cast<int64_t>(h) * T;
   TileLoader<D> ld;
   float lreg = 0.f;
   auto fetch = [&](int step) {
-    const int hh = g * G + step / ntile;
-    const int32_t qrow0 = (t0 + step % ntile) * FT_TILE;
-    ld.load(q + static_cast<int64_t>(hh) * T * D, qrow0, T);
-    if (tid < FT_TILE) lreg = lse[static_cast<int64_t>(hh) * T + min(qrow0 + tid, T - 1)];
+    const int32_t qrow0 = (t0 + step) * FT_TILE;
+    ld.load(qh, qrow0, T);
+    if (tid < FT_TILE) lreg = lh[min(qrow0 + tid, T - 1)];
   };
   if (nsteps > 0) {
     fetch(0);
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
     // loads stay in flight meanwhile
     __builtin_amdgcn_sched_barrier(0);
     const int buf = step & 1;
-    const int32_t qrow0 = (t0 + step % ntile) * FT_TILE;
+    const int32_t qrow0 = (t0 + step) * FT_TILE;
     if (jw < T && qrow0 + FT_TILE - 1 >= jw + W) {  // some query of the tile counts
       // both 32-query blocks of the tile as two independent MFMA chains
       f32x16_t acc0 = {}, acc1 = {};
@@ -277,37 +283,57 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int32_t key = jw + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
-      if (key < T) y[static_cast<int64_t>(g) * T + key] = col[r];
+      if (key < T) part[static_cast<int64_t>(h) * T + key] = col[r];
     }
   }
 }
 
+// ---- the group sum: y[g][j] = sum over the group's heads of part[h][j] ------
+__global__ __launch_bounds__(256) void future_group_sum_kernel(const float* __restrict__ part,
+                                                               int32_t T, int32_t G,
+                                                               float* __restrict__ y) {
+  const int g = blockIdx.y;
+  const int32_t j = static_cast<int32_t>(blockIdx.x) * 256 + static_cast<int32_t>(threadIdx.x);
+  if (j >= T) return;
+  const float* p = part + static_cast<int64_t>(g) * G * T + j;
+  float acc = 0.f;
+  for (int u = 0; u < G; ++u) acc += p[static_cast<int64_t>(u) * T];
+  y[static_cast<int64_t>(g) * T + j] = acc;
+}
+
 template <int D>
 hipError_t launch_future_d(int32_t T, int32_t Hq, int32_t Hkv, int32_t W, float c2,
-                           const uint16_t* q, const uint16_t* k, float* lse, float* y,
+                           const uint16_t* q, const uint16_t* k, float* work, float* y,
                            hipStream_t stream) {
   const uint32_t tiles = static_cast<uint32_t>((T + FT_ROWS - 1) / FT_ROWS);
-  hipLaunchKernelGGL(future_lse_kernel<D>, dim3(tiles, static_cast<uint32_t>(Hq)), dim3(FT_THREADS),
+  float* lse = work;
+  float* part = work + static_cast<int64_t>(Hq) * T;
+  hipLaunchKernelGGL(future_lse_kernel<D>, dim3(static_cast<uint32_t>(Hq), tiles), dim3(FT_THREADS),
                      0, stream, q, k, T, Hq, Hkv, c2, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(future_colsum_kernel<D>, dim3(tiles, static_cast<uint32_t>(Hkv)),
-                     dim3(FT_THREADS), 0, stream, q, k, lse, T, Hq, Hkv, W, c2, y);
+  hipLaunchKernelGGL(future_colsum_kernel<D>, dim3(static_cast<uint32_t>(Hq), tiles),
+                     dim3(FT_THREADS), 0, stream, q, k, lse, T, Hq, Hkv, W, c2, part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(future_group_sum_kernel,
+                     dim3(static_cast<uint32_t>((T + 255) / 256), static_cast<uint32_t>(Hkv)),
+                     dim3(256), 0, stream, part, T, Hq / Hkv, y);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uint16_t* q,
-                                const uint16_t* k, float scale, float* lse, float* y,
+                                const uint16_t* k, float scale_log2e, float* work, float* y,
                                 hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
-  const float c2 = scale * 1.4426950408889634f;
+  const float c2 = scale_log2e;
   if (geo.head_dim == 128)
     return launch_future_d<128>(n_tokens, geo.n_q_heads, geo.n_kv_heads, geo.n_recent, c2, q, k,
-                                lse, y, stream);
-  return launch_future_d<64>(n_tokens, geo.n_q_heads, geo.n_kv_heads, geo.n_recent, c2, q, k, lse,
-                             y, stream);
+                                work, y, stream);
+  return launch_future_d<64>(n_tokens, geo.n_q_heads, geo.n_kv_heads, geo.n_recent, c2, q, k,
+                             work, y, stream);
 }
 
 }  // namespace kvpop

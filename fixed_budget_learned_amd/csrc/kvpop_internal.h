@@ -86,8 +86,11 @@ hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const
                                     uint64_t* thr, hipStream_t stream);
 // Future-attention target of one sequence: lse [Hq][n_tokens] f32 workspace
 // (log2-domain row log-sum-exp), y [Hkv][n_tokens] f32 output.
+// work: [2][Hq][n_tokens] fp32 (each query's log2-domain log-sum-exp, then
+// each query head's share of the target); scale_log2e: the softmax scale
+// times log2(e).
 hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uint16_t* q,
-                                const uint16_t* k, float scale, float* lse, float* y,
+                                const uint16_t* k, float scale_log2e, float* work, float* y,
                                 hipStream_t stream);
 // Largest split count the decode kernel accepts, and whether a launch shape
 // (head_dim, group size, workgroup size, rows per thread) is compiled.

@@ -186,8 +186,9 @@ KVPOP_API int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, cons
  * With the cache's geometry and softmax scale c, and no access to its state:
  *   q    device [Hq][n_tokens][D] bf16, the queries of every position
  *   k    device [Hkv][n_tokens][D] bf16, the keys of every position
- *   lse  device [Hq][n_tokens] float32 workspace (receives each query's
- *        causal log-sum-exp in log2 units)
+ *   work device [2][Hq][n_tokens] float32 workspace: work[0][h][i]
+ *        receives query i of head h's causal log-sum-exp in log2 units,
+ *        work[1][h][j] head h's share of y[g][j]
  *   y    device [Hkv][n_tokens] float32 (output):
  *        y[g][j] = sum over the query heads h of g's group and the queries
  *        i >= j + n_recent of softmax over j' <= i of c <q_h,i, k_g,j'>, at
@@ -197,7 +198,7 @@ KVPOP_API int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, cons
  * KVPOP_EINVAL (NULL pointers, n_tokens < 0), KVPOP_ESTATE (n_tokens >
  * max_positions or poisoned), KVPOP_EHIP. */
 KVPOP_API int kvpop_future_attention_target(kvpop_cache* cache, int32_t n_tokens, const uint16_t* q,
-                                            const uint16_t* k, float* lse, float* y, void* stream);
+                                            const uint16_t* k, float* work, float* y, void* stream);
 
 /* Static description of a return code. */
 KVPOP_API const char* kvpop_strerror(int code);

@@ -26,14 +26,16 @@ def _gpu():
     torch.cuda.init()
 
 
-def _run(Hq, Hkv, D, W, T, q, k):
+def _run(Hq, Hkv, D, W, T, q, k, with_work=False):
     geo = Geo(Hq, Hkv, D, 4, 16, W)
     cache = make_cache(geo, max_positions=max(T, 1))
-    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    work = torch.full((2, Hq, T), float("nan"), dtype=torch.float32, device="cuda")
     y = torch.full((Hkv, T), float("nan"), dtype=torch.float32, device="cuda")
-    cache.future_attention_target(to_dev_bf16(q), to_dev_bf16(k), lse, y)
+    cache.future_attention_target(to_dev_bf16(q), to_dev_bf16(k), work, y)
     got = y.cpu().numpy().astype(np.float64)
     cache.close()
+    if with_work:
+        return got, work.cpu().numpy().astype(np.float64)
     return got
 
 
@@ -61,6 +63,31 @@ def test_future_target_matches_oracle(Hq, Hkv, D, W, T, sd):
     assert np.all(np.isfinite(got))
     assert np.all(err <= 1e-3 * (1.0 + np.abs(want))), \
         f"max err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}"
+
+
+def test_per_head_shares_and_lse():
+    """work[1][h] is head h's own target (the oracle on that head alone), and
+    work[0][h][i] the log2 of the causal softmax denominator of query i."""
+    Hq, Hkv, D, W, T = 8, 2, 64, 9, 400
+    rng = np.random.default_rng(21)
+    q = bf16_bits_rne((1.5 * rng.standard_normal((Hq, T, D))).astype(np.float32))
+    k = bf16_bits_rne(rng.standard_normal((Hkv, T, D)).astype(np.float32))
+    y, work = _run(Hq, Hkv, D, W, T, q, k, with_work=True)
+    scale = 1.0 / math.sqrt(D)
+    G = Hq // Hkv
+    for h in range(Hq):
+        want = future_attention_target(q[h:h + 1], k[h // G:h // G + 1], W, scale)[0]
+        assert np.all(np.abs(work[1][h] - want) <= 1e-3 * (1.0 + np.abs(want))), h
+    # lse of a few queries of head 3, from the definition in fp64
+    qf = q.astype(np.uint32) << 16
+    kf = k.astype(np.uint32) << 16
+    qf = qf.view(np.float32).astype(np.float64)
+    kf = kf.view(np.float32).astype(np.float64)
+    for i in (0, 1, 63, 64, 200, T - 1):
+        s = scale * (kf[0, :i + 1] @ qf[3, i])
+        want = (s.max() + np.log(np.exp(s - s.max()).sum())) / math.log(2.0)
+        assert abs(work[0][3][i] - want) <= 1e-3 * (1.0 + abs(want)), i
+    assert np.allclose(y, work[1].reshape(Hkv, G, T).sum(axis=1), rtol=1e-6, atol=1e-6)
 
 
 def test_uniform_attention_harmonic_sums_on_gpu():

@@ -51,6 +51,13 @@ notes of the repository):
     group puts on it after the key has left the window; the pages do not say
     how query heads combine or whether it is normalised (summed here, not
     normalised).
+11. The Dynamic backend the model card lists beside the Static one ("Cache
+    backends": it grows, then prunes, under the same budget) is read as:
+    every token leaving the window is held (the scored region grows without
+    a comparison), and a prune cuts each head's scored region back to its
+    top-k by key.  When it prunes is not on the pages; the prune is an
+    explicit step here, and a cache that prunes after every step is the
+    Static one.
 
 All arithmetic is float64 on exactly decoded bfloat16 values.
 """
@@ -105,6 +112,27 @@ def kept_by_definition(scores_g, n: int, n_sink: int, n_scored: int, n_recent: i
     cand = range(s, n - W + 1)
     ranked = sorted(cand, key=lambda t: (_check_score(scores_g[t]), t), reverse=True)
     return sorted(sink | win | set(ranked[:k]))
+
+
+def held_dynamic_by_definition(scores_g, n: int, n_pruned: int, n_sink: int, n_scored: int,
+                               n_recent: int):
+    """Rows a Dynamic-backend head holds after position n, when its scored
+    region was last cut back at position n_pruned (-1: never; a prefill of P
+    tokens counts as a cut at P - 1), written from the definition (reading
+    11): the sinks and the window of n, the top-k of Cand(n_pruned), and
+    every token that has left the window since, i.e. Cand(n) minus
+    Cand(n_pruned).  Returns a sorted list.
+    """
+    s, k, W = n_sink, n_scored, n_recent
+    if n < 0:
+        return []
+    sink = set(range(0, min(s, n + 1)))
+    win = set(range(max(s, n - W + 1), n + 1))
+    cand_pruned = range(s, n_pruned - W + 1)
+    ranked = sorted(cand_pruned, key=lambda t: (_check_score(scores_g[t]), t), reverse=True)
+    old = set(ranked[:k])                       # TopK(Cand(n_pruned))
+    new = set(range(max(s, n_pruned - W + 1), n - W + 1))
+    return sorted(sink | win | old | new)
 
 
 # ---------------------------------------------------------------------------
@@ -249,12 +277,17 @@ class KVpopOracle:
     prefill(k, v, scores)          fill from a P-token prompt
     decode(q, k_new, v_new, sl)    process one new token; returns the
                                    attention output of every query head
+    prune()                        Dynamic backend: cut every head's scored
+                                   region back to its top-k (reading 11)
     kept(g)                        sorted kept positions of KV head g
+
+    dynamic=False is the Static backend (fixed buffers, online replacement);
+    dynamic=True holds every leaving token until the next prune().
     """
 
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  n_sink: int, n_scored: int, n_recent: int,
-                 softmax_scale: float | None = None):
+                 softmax_scale: float | None = None, dynamic: bool = False):
         if n_q_heads % n_kv_heads:
             raise ValueError("n_q_heads must be a multiple of n_kv_heads")
         if n_recent < 1 or n_sink < 0 or n_scored < 0:
@@ -263,6 +296,7 @@ class KVpopOracle:
         self.s, self.k, self.W = n_sink, n_scored, n_recent
         self.scale = (1.0 / math.sqrt(head_dim)) if not softmax_scale or softmax_scale <= 0 \
             else float(softmax_scale)
+        self.dynamic = bool(dynamic)
         self.n = -1                       # newest processed position
         self._cap = 0
         self._K = np.zeros((self.Hkv, 0, self.D))
@@ -307,6 +341,9 @@ class KVpopOracle:
     def _admit_leaving(self, g: int, t: int, score: float):
         """Token t has just left the window with ``score`` (delayed scoring)."""
         S = self.S[g]
+        if self.dynamic:                          # reading 11: grow until the prune
+            S[t] = score
+            return
         if len(S) < self.k:                       # reading 4
             S[t] = score
             return
@@ -317,6 +354,15 @@ class KVpopOracle:
             del S[m]                              # evicted for good
             S[t] = score
         # else: t is dropped for good
+
+    def prune(self):
+        """Dynamic backend: keep only the k most important members of every
+        head's scored region (by (score, position), reading 3); the rest are
+        evicted for good."""
+        for g in range(self.Hkv):
+            S = self.S[g]
+            ranked = sorted(S, key=lambda p: (S[p], p), reverse=True)
+            self.S[g] = {p: S[p] for p in ranked[:self.k]}
 
     def decode(self, q_bits, k_new_bits, v_new_bits, score_leaving, attend: bool = True):
         """Process token n = self.n + 1 and return out [Hq][D] (float64).

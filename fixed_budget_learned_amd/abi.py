@@ -23,7 +23,7 @@ KVPOP_FLAG_NAN_SCORE = 1
 EXPORTED = ("kvpop_cache_required_bytes", "kvpop_cache_create", "kvpop_cache_destroy",
             "kvpop_cache_reset", "kvpop_prefill_compact", "kvpop_decode_step",
             "kvpop_cache_state", "kvpop_strerror",
-            "kvpop_prefix_thresholds", "kvpop_future_attention_target")
+            "kvpop_prefix_thresholds", "kvpop_future_attention_target", "kvpop_cache_prune")
 
 
 class KVpopLibraryMissing(RuntimeError):
@@ -42,7 +42,7 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_sink", ctypes.c_int32),
                 ("n_scored", ctypes.c_int32), ("n_recent", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("decode_splits", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("prune_interval", ctypes.c_int32)]
 
 
 class State(ctypes.Structure):
@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.kvpop_prefix_thresholds.restype = ctypes.c_int
     lib.kvpop_future_attention_target.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.kvpop_future_attention_target.restype = ctypes.c_int
+    lib.kvpop_cache_prune.argtypes = [vp, i32, vp]
+    lib.kvpop_cache_prune.restype = ctypes.c_int
     lib.kvpop_strerror.argtypes = [ctypes.c_int]
     lib.kvpop_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -91,10 +93,13 @@ def strerror(code: int) -> str:
 
 
 def make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_sink, n_scored, n_recent,
-                max_positions=1 << 30, decode_splits=0, softmax_scale=0.0) -> Config:
+                max_positions=1 << 30, decode_splits=0, softmax_scale=0.0,
+                prune_interval=0) -> Config:
+    """prune_interval 0: Static backend; P >= 1: Dynamic backend pruned after
+    every P-th decode step of a layer (see the header)."""
     return Config(int(n_layers), int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim),
                   int(n_sink), int(n_scored), int(n_recent), int(max_positions),
-                  int(decode_splits), float(softmax_scale))
+                  int(decode_splits), float(softmax_scale), int(prune_interval))
 
 
 def required_bytes(cfg: Config) -> int:
@@ -143,6 +148,7 @@ class KVpopCache:
         lib = load()
         self.cfg = cfg
         self.budget = cfg.n_sink + cfg.n_scored + cfg.n_recent
+        self.capacity = self.budget + cfg.prune_interval   # rows per KV head
         self._arena = arena
         h = ctypes.c_void_p()
         ptr, nbytes = None, 0
@@ -193,6 +199,10 @@ class KVpopCache:
         _check(load().kvpop_decode_step(self._h, layer, qp, kp, vp, sp, op, _stream_ptr(stream)),
                "kvpop_decode_step")
 
+    def prune(self, layer: int, stream=None):
+        """Dynamic backend: prune every head of `layer` back to the budget now."""
+        _check(load().kvpop_cache_prune(self._h, layer, _stream_ptr(stream)), "kvpop_cache_prune")
+
     def prefix_thresholds(self, scores, thr, stream=None):
         """Threshold key of every prompt position per KV head (see the
         header): scores float32 [Hkv][P] in, thr int64 [Hkv][P] out (the
@@ -225,7 +235,7 @@ class KVpopCache:
         c = self.cfg
         st = State()
         counts = np.zeros(c.n_kv_heads, dtype=np.int32)
-        kept = np.zeros((c.n_kv_heads, self.budget), dtype=np.int32)
+        kept = np.zeros((c.n_kv_heads, self.capacity), dtype=np.int32)
         _check(load().kvpop_cache_state(self._h, layer, seq, ctypes.byref(st),
                                         counts.ctypes.data, kept.ctypes.data,
                                         _stream_ptr(stream)), "kvpop_cache_state")

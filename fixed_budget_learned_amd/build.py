@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkvpop.so")
 ARCH = "gfx950"
 
-SOURCES = ["kvpop_abi.cpp", "kvpop_prefill.hip", "kvpop_decode.hip", "kvpop_thresholds.hip", "kvpop_future.hip"]
+SOURCES = ["kvpop_abi.cpp", "kvpop_prefill.hip", "kvpop_decode.hip", "kvpop_thresholds.hip",
+           "kvpop_future.hip", "kvpop_prune.hip"]
 
 # Packed-FP32 instructions are disabled for all device code.
 COMMON_FLAGS = [

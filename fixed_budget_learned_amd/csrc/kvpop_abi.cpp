@@ -31,6 +31,11 @@ bool mul_ok(size_t a, size_t b, size_t* r) {
   return true;
 }
 
+// Rows per head: the budget plus the Dynamic backend's growth room.
+int64_t capacity_of(const kvpop_config& c) {
+  return int64_t(c.n_sink) + c.n_scored + c.n_recent + c.prune_interval;
+}
+
 bool config_valid(const kvpop_config* c) {
   if (c == nullptr) return false;
   if (c->n_layers < 1 || c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1) return false;
@@ -39,8 +44,8 @@ bool config_valid(const kvpop_config* c) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (c->head_dim != 64 && c->head_dim != 128) return false;
   if (c->n_sink < 0 || c->n_scored < 0 || c->n_recent < 1) return false;
-  const int64_t budget = int64_t(c->n_sink) + c->n_scored + c->n_recent;
-  if (budget > (1 << 20)) return false;
+  if (c->prune_interval < 0 || c->prune_interval > kvpop::PRUNE_SLACK_MAX) return false;
+  if (capacity_of(*c) > (1 << 20)) return false;
   if (c->max_positions < 1 || c->max_positions > (1 << 30)) return false;
   if (c->decode_splits < 0 || c->decode_splits > kvpop::decode_max_splits()) return false;
   if (std::isnan(c->softmax_scale) || std::isinf(c->softmax_scale)) return false;
@@ -57,7 +62,7 @@ bool config_valid(const kvpop_config* c) {
 // then stalls the stream.  Every split keeps at least 128 slots.
 void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
                          int32_t* threads, int32_t* rows_per_thread) {
-  const int64_t budget = int64_t(c.n_sink) + c.n_scored + c.n_recent;
+  const int64_t budget = capacity_of(c);
   const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
   const int nt = 256, np = 2;
   const int64_t rpp = nt / (c.head_dim / 16);
@@ -77,7 +82,7 @@ void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_p
 }
 
 bool compute_layout(const kvpop_config& c, Layout* L) {
-  const size_t budget = size_t(c.n_sink) + c.n_scored + c.n_recent;
+  const size_t budget = size_t(capacity_of(c));
   const size_t heads_all = size_t(c.n_layers) * c.batch * c.n_kv_heads;
   const size_t heads = size_t(c.batch) * c.n_kv_heads;
   const size_t G = size_t(c.n_q_heads / c.n_kv_heads);
@@ -136,6 +141,7 @@ struct kvpop_cache {
   char* base = nullptr;
   float scale_log2e = 0.f;
   std::vector<int32_t> n_host;  // [L][B], newest processed position
+  std::vector<int64_t> steps;   // [L] decode steps taken (the Dynamic backend's prune clock)
 
   kvpop::Geometry geo() const {
     kvpop::Geometry g;
@@ -146,12 +152,13 @@ struct kvpop_cache {
     g.n_sink = cfg.n_sink;
     g.n_scored = cfg.n_scored;
     g.n_recent = cfg.n_recent;
-    g.budget = cfg.n_sink + cfg.n_scored + cfg.n_recent;
+    g.slack = cfg.prune_interval;
+    g.budget = int32_t(capacity_of(cfg));
     return g;
   }
   kvpop::LayerView layer(int32_t l) const {
     const size_t heads = size_t(cfg.batch) * cfg.n_kv_heads;
-    const size_t budget = size_t(cfg.n_sink) + cfg.n_scored + cfg.n_recent;
+    const size_t budget = size_t(capacity_of(cfg));
     const size_t h0 = size_t(l) * heads;
     kvpop::LayerView v;
     v.kc = reinterpret_cast<uint16_t*>(base + lay.kc) + h0 * budget * cfg.head_dim;
@@ -205,6 +212,7 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
   if (c == nullptr) return KVPOP_ENOMEM;
   try {
     c->n_host.assign(size_t(cfg->n_layers) * cfg->batch, -1);
+    c->steps.assign(size_t(cfg->n_layers), 0);
   } catch (...) {
     delete c;
     return KVPOP_ENOMEM;
@@ -364,6 +372,32 @@ int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, cons
     return KVPOP_EHIP;
   }
   for (int32_t b = 0; b < c.batch; ++b) nh[b] += 1;
+  // Dynamic backend: after every prune_interval-th step of the layer, cut
+  // every head back to the budget
+  if (c.prune_interval > 0 && ++cache->steps[size_t(layer)] % c.prune_interval == 0) {
+    e = kvpop::launch_prune(cache->geo(), cache->layer(layer), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      cache->poisoned = true;
+      return KVPOP_EHIP;
+    }
+  }
+  return KVPOP_OK;
+}
+
+int kvpop_cache_prune(kvpop_cache* cache, int32_t layer, void* stream) {
+  if (cache == nullptr) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (layer < 0 || layer >= c.n_layers) return KVPOP_EINVAL;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  if (c.prune_interval == 0) return KVPOP_OK;  // Static: never above the budget
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  hipError_t e =
+      kvpop::launch_prune(cache->geo(), cache->layer(layer), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
   return KVPOP_OK;
 }
 
@@ -375,7 +409,7 @@ int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, kvpop_stat
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
   const int32_t Hkv = c.n_kv_heads;
-  const size_t budget = size_t(c.n_sink) + c.n_scored + c.n_recent;
+  const size_t budget = size_t(capacity_of(c));
   std::vector<kvpop::HeadCtl> ctl;
   std::vector<int32_t> pos;
   try {

@@ -752,7 +752,7 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
   prm.n_heads = geo.batch * geo.n_kv_heads;
   prm.budget = geo.budget;
   prm.n_sink = geo.n_sink;
-  prm.n_scored = geo.n_scored;
+  prm.n_scored = geo.n_scored + geo.slack;  // the Dynamic backend grows into its slack
   prm.n_recent = geo.n_recent;
   prm.nsplit = work.nsplit;
   prm.rows_per_split = work.rows_per_split;

@@ -1,5 +1,5 @@
 // Internal layout and launcher declarations shared by the C-ABI host code
-// (kvpop_abi.cpp) and the HIP kernels (kvpop_prefill.hip, kvpop_decode.hip).
+// (kvpop_abi.cpp) and the HIP kernels (kvpop_*.hip).
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -37,6 +37,7 @@ struct MinPart {
 static_assert(sizeof(MinPart) == 16, "MinPart layout");
 
 // Device views of one layer of the cache.  Head index = seq * Hkv + g.
+// `budget` below is the row capacity of a head (Geometry::budget).
 struct LayerView {
   uint16_t* kc;     // [B][Hkv][budget][D] bf16
   uint16_t* vc;     // [B][Hkv][budget][D] bf16
@@ -46,9 +47,14 @@ struct LayerView {
   HeadCtl* ctl;     // [B][Hkv]
 };
 
+// n_scored is k, the scored top-k the cache keeps.  slack is the growth room
+// of the Dynamic backend (0: Static): its scored region holds up to
+// k + slack tokens between prunes.  budget is the row capacity of a head,
+// n_sink + n_scored + n_recent + slack.
 struct Geometry {
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
   int32_t n_sink, n_scored, n_recent, budget;
+  int32_t slack;
 };
 
 // Decode workspace, shared by every layer (calls are stream-ordered).
@@ -84,10 +90,9 @@ hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq,
 constexpr int THR_KMAX = 4096;
 hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const float* scores,
                                     uint64_t* thr, hipStream_t stream);
-// Future-attention target of one sequence: lse [Hq][n_tokens] f32 workspace
-// (log2-domain row log-sum-exp), y [Hkv][n_tokens] f32 output.
-// work: [2][Hq][n_tokens] fp32 (each query's log2-domain log-sum-exp, then
-// each query head's share of the target); scale_log2e: the softmax scale
+// Future-attention target of one sequence: work [2][Hq][n_tokens] fp32
+// (each query's log2-domain log-sum-exp, then each query head's share of the
+// target), y [Hkv][n_tokens] fp32 output; scale_log2e: the softmax scale
 // times log2(e).
 hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uint16_t* q,
                                 const uint16_t* k, float scale_log2e, float* work, float* y,
@@ -101,5 +106,10 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
                          const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                          const float* score_leaving, uint16_t* out, float scale_log2e,
                          hipStream_t stream);
+// Dynamic backend: cut every head of the layer whose scored region holds
+// more than n_scored tokens back to its top n_scored, compacting the rows
+// into [0, count).  slack <= PRUNE_SLACK_MAX.
+constexpr int PRUNE_SLACK_MAX = 4096;
+hipError_t launch_prune(const Geometry& geo, const LayerView& lv, hipStream_t stream);
 
 }  // namespace kvpop

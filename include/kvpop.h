@@ -89,12 +89,27 @@ typedef struct kvpop_config {
   int32_t decode_splits; /* slot ranges per head in decode attention;
                             0 = chosen by the library, else 1 .. 256 */
   float softmax_scale;   /* <= 0: 1/sqrt(head_dim) */
+  int32_t prune_interval; /* cache backend ("Qwen3-8B-KVpop-4x" model card,
+                            "Cache backends"; when to prune is not given
+                            there, this is the reading taken):
+                            0 = Static: fixed buffers of n_sink + n_scored +
+                                n_recent rows, the leaving token replaces the
+                                least important scored one or is dropped;
+                            P in 1 .. 4096 = Dynamic: n_scored + P scored
+                                rows; every token leaving the window is held,
+                                and after every P-th decode step of a layer
+                                each of its heads is pruned back to its top
+                                n_scored (also on demand, kvpop_cache_prune).
+                            Both hold the same rows right after a prune. */
 } kvpop_config;
 
 typedef struct kvpop_state {
   int32_t n;     /* newest processed position of the sequence; -1 when empty */
   int32_t flags; /* KVPOP_FLAG_* bits, OR over the KV heads */
 } kvpop_state;
+
+/* Rows per KV head, the "capacity" below: n_sink + n_scored + n_recent +
+ * prune_interval. */
 
 /* Device bytes the cache needs for `cfg` (K/V rows, slot metadata and the
  * decode workspace), or 0 if `cfg` is invalid.  Pure host arithmetic. */
@@ -144,16 +159,30 @@ KVPOP_API int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t s
  *                (the new token included)
  * The new token enters the window; the leaving token takes a scored slot
  * (free, or the least important one's, which is evicted) or is dropped.
+ * Dynamic backend: the leaving token is held while the scored region has
+ * fewer than n_scored + prune_interval tokens, and after every
+ * prune_interval-th call for this layer (counted since the cache was
+ * created; resets do not restart the count) the call also prunes every head
+ * of the layer, as kvpop_cache_prune does.
  * Errors: KVPOP_EINVAL (NULL pointers, bad layer), KVPOP_ESTATE (poisoned or
  * a sequence would reach max_positions), KVPOP_EHIP (launch failed). */
 KVPOP_API int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, const float* score_leaving, uint16_t* out,
                       void* stream);
 
+/* Dynamic backend: prune every sequence's heads of `layer` now.  A head whose
+ * scored region holds more than n_scored tokens keeps its n_scored most
+ * important ones (by score, then position: the newer wins a tie) and evicts
+ * the rest for good; its rows are compacted into [0, count).  Afterwards
+ * every head holds exactly the rows the Static backend would keep.
+ * Stream-ordered.  A no-op for the Static backend.  Errors: KVPOP_EINVAL
+ * (NULL cache, bad layer), KVPOP_ESTATE (poisoned), KVPOP_EHIP. */
+KVPOP_API int kvpop_cache_prune(kvpop_cache* cache, int32_t layer, void* stream);
+
 /* Read back the state of (layer, seq).  Synchronises `stream` first.
  *   st        host, receives n and flags
  *   counts    host [Hkv] or NULL: kept rows per KV head
- *   kept_pos  host [Hkv][budget] or NULL: kept positions of each head in
+ *   kept_pos  host [Hkv][capacity] or NULL: kept positions of each head in
  *             ascending order, padded with -1
  * The caller owns the host buffers.  Errors: KVPOP_EINVAL, KVPOP_EHIP. */
 KVPOP_API int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, kvpop_state* st,

@@ -75,16 +75,18 @@ class Geo:
     n_recent: int
 
 
-def make_cache(geo: Geo, n_layers=1, batch=1, decode_splits=0, max_positions=1 << 30):
+def make_cache(geo: Geo, n_layers=1, batch=1, decode_splits=0, max_positions=1 << 30,
+               prune_interval=0):
     cfg = abi.make_config(n_layers, batch, geo.n_q_heads, geo.n_kv_heads, geo.head_dim,
                           geo.n_sink, geo.n_scored, geo.n_recent,
-                          max_positions=max_positions, decode_splits=decode_splits)
+                          max_positions=max_positions, decode_splits=decode_splits,
+                          prune_interval=prune_interval)
     return abi.KVpopCache(cfg)
 
 
-def make_oracle(geo: Geo) -> KVpopOracle:
+def make_oracle(geo: Geo, dynamic: bool = False) -> KVpopOracle:
     return KVpopOracle(geo.n_q_heads, geo.n_kv_heads, geo.head_dim, geo.n_sink,
-                       geo.n_scored, geo.n_recent)
+                       geo.n_scored, geo.n_recent, dynamic=dynamic)
 
 
 class Stream:

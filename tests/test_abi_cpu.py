@@ -72,6 +72,10 @@ def test_required_bytes_layout(lib):
     assert nb % 256 == 0
     # K/V storage grows linearly with layers and sequences
     assert abi.required_bytes(_cfg(n_layers=36)) - nb >= 35 * (kv + 8 * 4032 * 12)
+    # the Dynamic backend holds prune_interval more rows per head
+    grow = abi.required_bytes(_cfg(prune_interval=256)) - nb
+    assert grow >= 8 * 256 * (2 * 128 * 2 + 12)
+    assert abi.required_bytes(_cfg(prune_interval=4096)) > 0
 
 
 @pytest.mark.parametrize("bad", [
@@ -79,6 +83,7 @@ def test_required_bytes_layout(lib):
     dict(n_recent=0), dict(n_sink=-1), dict(n_scored=-2), dict(n_layers=0),
     dict(batch=0), dict(max_positions=0), dict(decode_splits=257),
     dict(softmax_scale=float("nan")), dict(n_kv_heads=0),
+    dict(prune_interval=-1), dict(prune_interval=4097),
 ])
 def test_invalid_configs_rejected(lib, bad):
     c = _cfg(**bad)
@@ -109,6 +114,7 @@ def test_null_cache_handle_everywhere(lib):
     assert lib.kvpop_cache_reset(None, 0, 0, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_prefix_thresholds(None, 4, 1, 1, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_future_attention_target(None, 4, 1, 1, 1, 1, None) == abi.KVPOP_EINVAL
+    assert lib.kvpop_cache_prune(None, 0, None) == abi.KVPOP_EINVAL
     lib.kvpop_cache_destroy(None)
 
 

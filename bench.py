@@ -183,6 +183,96 @@ def dense_vs_kvpop(contexts, steps: int, reps: int):
     return rows
 
 
+def dynamic_backend(steps: int, reps: int, every: int = 256):
+    """The Dynamic backend (grow into `every` rows of slack, prune after
+    every `every`-th step) against the Static one on the one-layer Qwen3-8B
+    4x workload: prefill 16,384, then `steps` decode steps, both captured in
+    graphs; plus the prune kernel alone after `every` steps of growth.
+    Inputs: seeded device-side N(0,1) K/V/q and scores."""
+    import torch
+    from fixed_budget_learned_amd import abi
+    from fixed_budget_learned_amd.configs import QWEN3_8B_LAYER_4X as w
+    D, Hq, Hkv, W, P = w.head_dim, w.n_q_heads, w.n_kv_heads, w.n_recent, w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5000)
+    T = P + steps
+    k = torch.randn((Hkv, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((Hkv, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+    sc = torch.randn((Hkv, T), generator=gen, device="cuda")
+    q = torch.randn((steps, 1, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    kn = k[:, P:].transpose(0, 1).contiguous().view(steps, 1, Hkv, D)
+    vn = v[:, P:].transpose(0, 1).contiguous().view(steps, 1, Hkv, D)
+    sl = sc[:, P - W:T - W].transpose(0, 1).contiguous().view(steps, 1, Hkv)
+    pk, pv, ps = k[:, :P].contiguous(), v[:, :P].contiguous(), sc[:, :P].contiguous()
+    out = torch.empty((1, Hq, D), dtype=torch.bfloat16, device="cuda")
+    res = {"workload": w.name, "prune_interval": every, "decode_steps": steps}
+    stream = torch.cuda.Stream()
+    for mode, interval in (("static", 0), ("dynamic", every)):
+        cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, w.n_scored, W,
+                                               max_positions=T, prune_interval=interval))
+
+        def pre():
+            cache.reset(0, 0)
+            cache.prefill_compact(0, 0, pk, pv, ps)
+
+        def dec():
+            for i in range(steps):
+                cache.decode_step(0, q[i], kn[i], vn[i], sl[i], out)
+
+        with torch.cuda.stream(stream):
+            pre()
+            dec()
+        torch.cuda.synchronize()
+        gp, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gp, stream=stream):
+            pre()
+        with torch.cuda.graph(gd, stream=stream):
+            dec()
+        ms = 0.0
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                gp.replay()
+                e0.record(stream)
+                gd.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                ms += e0.elapsed_time(e1)
+        res[f"{mode}_us_per_step"] = ms * 1e3 / (reps * steps)
+        res[f"{mode}_steps_per_s"] = reps * steps / (ms / 1e3)
+        st = cache.state(0, 0)
+        res[f"{mode}_rows_after"] = int(max(st.counts))
+        cache.close()
+        del gp, gd
+    res["dynamic_over_static"] = res["dynamic_us_per_step"] / res["static_us_per_step"]
+    # the prune alone: grow `every` steps with no scheduled prune, then prune
+    cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, w.n_scored, W,
+                                           max_positions=T, prune_interval=4096))
+    us = []
+    for r in range(reps + 1):
+        with torch.cuda.stream(stream):
+            cache.reset(0, 0)
+            cache.prefill_compact(0, 0, pk, pv, ps)
+            for i in range(every):
+                cache.decode_step(0, q[i], kn[i], vn[i], sl[i], out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cache.prune(0)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            us.append(e0.elapsed_time(e1) * 1e3)
+    st = cache.state(0, 0)
+    assert all(int(c) == w.budget for c in st.counts), "prune left more than the budget"
+    cache.close()
+    res["prune_us"] = sum(us) / len(us)
+    res["prune_us_per_step_amortised"] = res["prune_us"] / every
+    del k, v, sc, q, kn, vn, sl, pk, pv, ps
+    torch.cuda.empty_cache()
+    return res
+
+
 def layered_config(w, steps: int, reps: int):
     """Decode steps/s and prefill tokens/s of a batch-1 workload over all its
     layers (each step and each prefill runs one launch per layer), with the
@@ -651,6 +741,7 @@ def main():
                              layered_config(LONG_131K_8X, 32, 2)]
     if not args.no_dense_sweep:
         result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
+        result["dynamic_backend"] = dynamic_backend(1024, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_steps)
     print(json.dumps(result), flush=True)

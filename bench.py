@@ -104,7 +104,19 @@ def cpu_baseline(w, sample_steps: int):
                   f"{w.decode_steps} decode steps (all 8 KV heads, 32 query heads), fp64",
         "prefill_tokens_per_s": P / (t1 - t0),
         "host_cores_visible": len(os.sched_getaffinity(0)),
+        "host_cpu": _cpu_model(),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def dense_vs_kvpop(contexts, steps: int, reps: int):

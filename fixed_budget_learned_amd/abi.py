@@ -23,7 +23,8 @@ KVPOP_FLAG_NAN_SCORE = 1
 EXPORTED = ("kvpop_cache_required_bytes", "kvpop_cache_create", "kvpop_cache_destroy",
             "kvpop_cache_reset", "kvpop_prefill_compact", "kvpop_decode_step",
             "kvpop_cache_state", "kvpop_strerror",
-            "kvpop_prefix_thresholds", "kvpop_future_attention_target", "kvpop_cache_prune")
+            "kvpop_prefix_thresholds", "kvpop_future_attention_target", "kvpop_cache_prune",
+            "kvpop_prefill_compact_batch")
 
 
 class KVpopLibraryMissing(RuntimeError):
@@ -43,6 +44,12 @@ class Config(ctypes.Structure):
                 ("n_scored", ctypes.c_int32), ("n_recent", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("decode_splits", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("prune_interval", ctypes.c_int32)]
+
+
+class PrefillItem(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int32), ("seq", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("scores", ctypes.c_void_p)]
 
 
 class State(ctypes.Structure):
@@ -80,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.kvpop_prefix_thresholds.restype = ctypes.c_int
     lib.kvpop_future_attention_target.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.kvpop_future_attention_target.restype = ctypes.c_int
+    lib.kvpop_prefill_compact_batch.argtypes = [vp, i32, ctypes.POINTER(PrefillItem), vp]
+    lib.kvpop_prefill_compact_batch.restype = ctypes.c_int
     lib.kvpop_cache_prune.argtypes = [vp, i32, vp]
     lib.kvpop_cache_prune.restype = ctypes.c_int
     lib.kvpop_strerror.argtypes = [ctypes.c_int]
@@ -186,6 +195,21 @@ class KVpopCache:
         sp = _dev_ptr(scores, torch.float32, (c.n_kv_heads, P), "scores")
         _check(load().kvpop_prefill_compact(self._h, layer, seq, P, kp, vp, sp,
                                             _stream_ptr(stream)), "kvpop_prefill_compact")
+
+    def prefill_compact_batch(self, items, stream=None):
+        """Compact several prompts at once: items is a sequence of
+        (layer, seq, k, v, scores) with the tensors of prefill_compact."""
+        import torch
+        c = self.cfg
+        arr = (PrefillItem * max(1, len(items)))()
+        for i, (layer, seq, k, v, scores) in enumerate(items):
+            P = int(k.shape[1]) if k is not None and k.dim() == 3 else 0
+            arr[i].layer, arr[i].seq, arr[i].n_tokens, arr[i].pad = int(layer), int(seq), P, 0
+            arr[i].k = _dev_ptr(k, torch.bfloat16, (c.n_kv_heads, P, c.head_dim), "k")
+            arr[i].v = _dev_ptr(v, torch.bfloat16, (c.n_kv_heads, P, c.head_dim), "v")
+            arr[i].scores = _dev_ptr(scores, torch.float32, (c.n_kv_heads, P), "scores")
+        _check(load().kvpop_prefill_compact_batch(self._h, len(items), arr, _stream_ptr(stream)),
+               "kvpop_prefill_compact_batch")
 
     def decode_step(self, layer: int, q, k_new, v_new, score_leaving, out, stream=None):
         import torch

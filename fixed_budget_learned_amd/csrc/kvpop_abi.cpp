@@ -23,6 +23,7 @@ struct Layout {
   size_t kc, vc, keys, pos, ring, ctl, sel, slice_keys, slice_nan, part_acc, part_ml, part_min,
       tickets, total;
   int32_t nsplit, rows_per_split, threads, rows_per_thread;
+  int32_t sel_items;  // prompts one batched prefill launch can select at once
 };
 
 bool mul_ok(size_t a, size_t b, size_t* r) {
@@ -103,7 +104,11 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   ok = ok && mul_ok(rows, 4, &tmp) && take(tmp, &L->pos);
   ok = ok && mul_ok(heads_all, size_t(c.n_recent) * 4, &tmp) && take(tmp, &L->ring);
   ok = ok && mul_ok(heads_all, sizeof(kvpop::HeadCtl), &tmp) && take(tmp, &L->ctl);
-  ok = ok && take(size_t(c.n_kv_heads) * size_t(std::max(c.n_scored, 1)) * 4, &L->sel);
+  // selection buffer: up to PREFILL_NB prompts per launch, within 16 MiB
+  const size_t sel_one = size_t(c.n_kv_heads) * size_t(std::max(c.n_scored, 1)) * 4;
+  L->sel_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
+                                                              (size_t(16) << 20) / sel_one)));
+  ok = ok && take(sel_one * size_t(L->sel_items), &L->sel);
   ok = ok && take(size_t(c.n_kv_heads) * kvpop::SLICE_MAX * size_t(std::max(c.n_scored, 1)) * 8,
                   &L->slice_keys);
   ok = ok && take(size_t(c.n_kv_heads) * kvpop::SLICE_MAX * 4, &L->slice_nan);
@@ -168,6 +173,14 @@ struct kvpop_cache {
     v.ring = reinterpret_cast<int32_t*>(base + lay.ring) + h0 * cfg.n_recent;
     v.ctl = reinterpret_cast<kvpop::HeadCtl*>(base + lay.ctl) + h0;
     return v;
+  }
+  kvpop::PrefillWork prefill_work() const {
+    kvpop::PrefillWork pw;
+    pw.sel = reinterpret_cast<int32_t*>(base + lay.sel);
+    pw.sel_items = lay.sel_items;
+    pw.slice_keys = reinterpret_cast<uint64_t*>(base + lay.slice_keys);
+    pw.slice_nan = reinterpret_cast<int32_t*>(base + lay.slice_nan);
+    return pw;
   }
   kvpop::DecodeWork work() const {
     kvpop::DecodeWork w;
@@ -296,17 +309,71 @@ int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_
   if (k == nullptr || v == nullptr || scores == nullptr) return KVPOP_EINVAL;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
-  kvpop::PrefillWork pw;
-  pw.sel = reinterpret_cast<int32_t*>(cache->base + cache->lay.sel);
-  pw.slice_keys = reinterpret_cast<uint64_t*>(cache->base + cache->lay.slice_keys);
-  pw.slice_nan = reinterpret_cast<int32_t*>(cache->base + cache->lay.slice_nan);
-  hipError_t e = kvpop::launch_prefill(cache->geo(), cache->layer(layer), seq, n_tokens, k, v,
-                                       scores, pw, static_cast<hipStream_t>(stream));
+  kvpop::PrefillItem it;
+  it.k = k;
+  it.v = v;
+  it.scores = scores;
+  it.n_tokens = n_tokens;
+  it.seq = seq;
+  it.lv = cache->layer(layer);
+  hipError_t e = kvpop::launch_prefill_batch(cache->geo(), &it, 1, cache->prefill_work(),
+                                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;
     return KVPOP_EHIP;
   }
   nh = n_tokens - 1;
+  return KVPOP_OK;
+}
+
+int kvpop_prefill_compact_batch(kvpop_cache* cache, int32_t n_items,
+                                const kvpop_prefill_item* items, void* stream) {
+  if (cache == nullptr || n_items < 0 || (n_items > 0 && items == nullptr)) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  // validate everything before anything is enqueued
+  for (int32_t i = 0; i < n_items; ++i) {
+    const kvpop_prefill_item& x = items[i];
+    if (x.layer < 0 || x.layer >= c.n_layers || x.seq < 0 || x.seq >= c.batch || x.n_tokens < 0)
+      return KVPOP_EINVAL;
+    if (x.n_tokens > 0 && (x.k == nullptr || x.v == nullptr || x.scores == nullptr))
+      return KVPOP_EINVAL;
+  }
+  if (cache->poisoned) return KVPOP_ESTATE;
+  std::vector<kvpop::PrefillItem> its;
+  std::vector<size_t> slots;
+  try {
+    its.reserve(size_t(n_items));
+    slots.reserve(size_t(n_items));
+  } catch (...) {
+    return KVPOP_ENOMEM;
+  }
+  for (int32_t i = 0; i < n_items; ++i) {
+    const kvpop_prefill_item& x = items[i];
+    const size_t slot = size_t(x.layer) * c.batch + x.seq;
+    if (cache->n_host[slot] != -1 || x.n_tokens > c.max_positions) return KVPOP_ESTATE;
+    if (std::find(slots.begin(), slots.end(), slot) != slots.end()) return KVPOP_EINVAL;
+    slots.push_back(slot);
+    kvpop::PrefillItem it;
+    it.k = x.k;
+    it.v = x.v;
+    it.scores = x.scores;
+    it.n_tokens = x.n_tokens;
+    it.seq = x.seq;
+    it.lv = cache->layer(x.layer);
+    its.push_back(it);
+  }
+  if (n_items == 0) return KVPOP_OK;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  hipError_t e = kvpop::launch_prefill_batch(cache->geo(), its.data(), n_items,
+                                             cache->prefill_work(),
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  for (int32_t i = 0; i < n_items; ++i)
+    if (items[i].n_tokens > 0) cache->n_host[slots[size_t(i)]] = items[i].n_tokens - 1;
   return KVPOP_OK;
 }
 

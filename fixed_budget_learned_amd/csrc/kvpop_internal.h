@@ -77,14 +77,25 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
 // select in two levels: up to SLICE_MAX slices per head first keep their own
 // top k, then one workgroup per head selects from the union.
 constexpr int SLICE_MAX = 16;
+// A batch of prompts shares launches, up to PREFILL_NB prompts per launch.
+constexpr int PREFILL_NB = 32;
 struct PrefillWork {
-  int32_t* sel;          // [Hkv][k] kept candidate positions of the call
+  int32_t* sel;          // [sel_items][Hkv][k] kept candidate positions
+  int32_t sel_items;     // prompts the selection buffer holds (1 .. PREFILL_NB)
   uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level keys
   int32_t* slice_nan;    // [Hkv][SLICE_MAX] first-level NaN flags
 };
-hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
-                          const uint16_t* k, const uint16_t* v, const float* scores,
-                          const PrefillWork& pw, hipStream_t stream);
+// One prompt to compact into an empty (layer, sequence).
+struct PrefillItem {
+  const uint16_t* k;      // [Hkv][n_tokens][D]
+  const uint16_t* v;
+  const float* scores;    // [Hkv][n_tokens]
+  int32_t n_tokens;
+  int32_t seq;
+  LayerView lv;           // the destination layer
+};
+hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, int32_t n,
+                                const PrefillWork& pw, hipStream_t stream);
 // Prefix top-k thresholds of a prompt ([Hkv][n_tokens] keys), n_scored <=
 // THR_KMAX.
 constexpr int THR_KMAX = 4096;

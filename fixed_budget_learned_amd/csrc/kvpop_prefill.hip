@@ -10,16 +10,19 @@
 // Two kernels per call:
 //   select  one 1024-thread workgroup per KV head; each thread owns a
 //           contiguous block of candidate positions (kept in registers when
-//           it is at most 32 long).  A 4 x 8-bit radix select over the
-//           order-preserving score codes (one LDS histogram per wave) finds
-//           the threshold code and how many tokens carrying it survive; one
-//           workgroup scan of per-thread (greater, equal) counts then places
-//           every code above the threshold and the newest of the tied ones,
-//           writing the kept positions in ascending order plus the head's
-//           control block (count, min key and its slot).
+//           it is at most 32 long).  A radix select with 12, 12 and 8-bit
+//           digits over the order-preserving score codes (one 4096-bin LDS
+//           histogram) finds the threshold code and how many tokens carrying
+//           it survive; one workgroup scan of per-thread (greater, equal)
+//           counts then places every code above the threshold and the newest
+//           of the tied ones, writing the kept positions in ascending order
+//           plus the head's control block (count, min key and its slot).
 //   gather  many 256-thread workgroups per head copy the kept K/V rows into
 //           slots [0, count) with 16-byte coalesced loads/stores and write
 //           per-slot position and key, and the window ring.
+// A batch of (layer, sequence) prompts shares one select and one gather
+// launch: the grid's z is the prompt, each reading its own descriptor from
+// the kernel arguments (up to PREFILL_NB per launch).
 // Slot layout after prefill: sinks, then selected candidates in ascending
 // position, then the window in ascending position.
 #include <hip/hip_runtime.h>
@@ -169,7 +172,7 @@ __device__ __forceinline__ void radix_pass(Visit&& visit, uint32_t prefix, uint3
 constexpr int SEL_HEAD = 0, SEL_SLICE = 1, SEL_LIST = 2;
 
 struct SelectArgs {
-  const float* scores;   // [Hkv][P] of this sequence
+  const float* scores;   // [Hkv][P] of this prompt
   PrefillShape sh;
   int32_t k;             // scored slots (stride of the selection buffers)
   int32_t* sel;          // [Hkv][k] kept candidate positions, ascending
@@ -179,8 +182,15 @@ struct SelectArgs {
   int32_t n_slices, slice_len;
 };
 
-template <int VPT, int MODE>
-__global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectArgs a) {
+// Descriptors of the prompts of one launch (grid z = prompt).
+template <int NB>
+struct SelectBatch {
+  SelectArgs item[NB];
+};
+
+template <int VPT, int MODE, int NB>
+__global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch<NB> batch) {
+  const SelectArgs& a = batch.item[blockIdx.z];
   static_assert(MODE != SEL_LIST || VPT == 16, "list mode stages 64-bit keys: at most 16 per thread");
   static_assert(MODE == SEL_HEAD || VPT > 0, "slice and list modes keep codes in registers");
   constexpr int NWAVE = SEL_THREADS / WAVE;
@@ -456,22 +466,49 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectArgs 
   }
 }
 
+// One prompt of a gather launch: its inputs, selection and destination
+// (the cache rows of its (layer, sequence), head 0).
+struct GatherItem {
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* scores;
+  PrefillShape sh;
+  const int32_t* sel;
+  uint16_t* kc;
+  uint16_t* vc;
+  uint64_t* keys;
+  int32_t* pos;
+  int32_t* ring;
+};
+
+template <int NB>
+struct GatherBatch {
+  GatherItem item[NB];
+};
+
 // Rows per gather workgroup: 256 threads move 16 bytes each per pass.
-template <int D>
+template <int D, int NB>
 __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ scores, PrefillShape sh, int32_t kcap, int32_t budget, int32_t W,
-    int32_t rows_per_block, const int32_t* __restrict__ sel, uint16_t* __restrict__ kc,
-    uint16_t* __restrict__ vc, uint64_t* __restrict__ keys, int32_t* __restrict__ pos,
-    int32_t* __restrict__ ring) {
+    GatherBatch<NB> batch, int32_t kcap, int32_t budget, int32_t W, int32_t rows_per_block) {
   constexpr int LPR = D / 8;                   // lanes per row (16 B each)
   constexpr int RPP = GATHER_THREADS / LPR;    // rows per pass
+  const GatherItem& it = batch.item[blockIdx.z];
+  const PrefillShape& sh = it.sh;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int rg = tid / LPR;
   const int c = tid % LPR;
   const int32_t r0 = blockIdx.x * rows_per_block;
-  const int32_t r1 = min(r0 + rows_per_block, sh.count);
+  const int32_t r1 = min(r0 + rows_per_block, sh.count);  // empty past this prompt's rows
+  const uint16_t* __restrict__ k = it.k;
+  const uint16_t* __restrict__ v = it.v;
+  const float* __restrict__ scores = it.scores;
+  const int32_t* __restrict__ sel = it.sel;
+  uint16_t* __restrict__ kc = it.kc;
+  uint16_t* __restrict__ vc = it.vc;
+  uint64_t* __restrict__ keys = it.keys;
+  int32_t* __restrict__ pos = it.pos;
+  int32_t* __restrict__ ring = it.ring;
 
   const uint4* ksrc = reinterpret_cast<const uint4*>(k + static_cast<int64_t>(g) * sh.P * D);
   const uint4* vsrc = reinterpret_cast<const uint4*>(v + static_cast<int64_t>(g) * sh.P * D);
@@ -555,84 +592,171 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const Geometry& geo, const LayerView& lv, int32_t seq, int32_t n_tokens,
-                          const uint16_t* k, const uint16_t* v, const float* scores,
-                          const PrefillWork& pw, hipStream_t stream) {
-  const PrefillShape sh = prefill_shape(n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
-  const int64_t head0 = static_cast<int64_t>(seq) * geo.n_kv_heads;
-  const int32_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
-  int32_t* sel = pw.sel;
+namespace {
+
+SelectArgs select_args(const Geometry& geo, const PrefillItem& it, int32_t* sel,
+                       const PrefillWork& pw) {
   SelectArgs sa;
-  sa.scores = scores;
-  sa.sh = sh;
+  sa.scores = it.scores;
+  sa.sh = prefill_shape(it.n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
   sa.k = geo.n_scored;
   sa.sel = sel;
-  sa.ctl = lv.ctl + head0;
+  sa.ctl = it.lv.ctl + static_cast<int64_t>(it.seq) * geo.n_kv_heads;
   sa.slice_keys = pw.slice_keys;
   sa.slice_nan = pw.slice_nan;
   sa.n_slices = 1;
   sa.slice_len = 0;
+  return sa;
+}
+
+GatherItem gather_item(const Geometry& geo, const PrefillItem& it, const int32_t* sel) {
+  const int64_t head0 = static_cast<int64_t>(it.seq) * geo.n_kv_heads;
+  const int64_t row0 = head0 * geo.budget;
+  const int64_t el0 = row0 * geo.head_dim;
+  GatherItem g;
+  g.k = it.k;
+  g.v = it.v;
+  g.scores = it.scores;
+  g.sh = prefill_shape(it.n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
+  g.sel = sel;
+  g.kc = it.lv.kc + el0;
+  g.vc = it.lv.vc + el0;
+  g.keys = it.lv.keys + row0;
+  g.pos = it.lv.pos + row0;
+  g.ring = it.lv.ring + head0 * geo.n_recent;
+  return g;
+}
+
+constexpr int32_t GATHER_ROWS = 64;  // rows per gather workgroup
+
+// Gather of m prompts whose selections are complete.
+template <int NB>
+hipError_t launch_gather(const Geometry& geo, const GatherBatch<NB>& gb, int32_t m,
+                         hipStream_t stream) {
+  int32_t maxc = 0;
+  for (int32_t i = 0; i < m; ++i) maxc = gb.item[i].sh.count > maxc ? gb.item[i].sh.count : maxc;
+  if (maxc == 0) return hipSuccess;
+  const int32_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
+  const dim3 grid(static_cast<uint32_t>((maxc + GATHER_ROWS - 1) / GATHER_ROWS),
+                  static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(m));
+  if (geo.head_dim == 128)
+    hipLaunchKernelGGL((prefill_gather_kernel<128, NB>), grid, dim3(GATHER_THREADS), 0, stream, gb,
+                       kcap, geo.budget, geo.n_recent, GATHER_ROWS);
+  else
+    hipLaunchKernelGGL((prefill_gather_kernel<64, NB>), grid, dim3(GATHER_THREADS), 0, stream, gb,
+                       kcap, geo.budget, geo.n_recent, GATHER_ROWS);
+  return hipGetLastError();
+}
+
+// Prompts whose candidates fit VPT per thread, up to NB per launch pair.
+template <int VPT, int NB>
+hipError_t launch_head_batch(const Geometry& geo, const PrefillItem* const* its, int32_t m,
+                             const PrefillWork& pw, hipStream_t stream) {
+  const int64_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
+  SelectBatch<NB> sb;
+  GatherBatch<NB> gb;
+  for (int32_t i = 0; i < m; ++i) {
+    int32_t* sel = pw.sel + i * static_cast<int64_t>(geo.n_kv_heads) * kcap;
+    sb.item[i] = select_args(geo, *its[i], sel, pw);
+    gb.item[i] = gather_item(geo, *its[i], sel);
+  }
+  const dim3 grid(static_cast<uint32_t>(geo.n_kv_heads), 1u, static_cast<uint32_t>(m));
+  hipLaunchKernelGGL((prefill_select_kernel<VPT, SEL_HEAD, NB>), grid, dim3(SEL_THREADS), 0,
+                     stream, sb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gather<NB>(geo, gb, m, stream);
+}
+
+template <int VPT>
+hipError_t launch_head_class(const Geometry& geo, const PrefillItem* const* its, int32_t m,
+                             const PrefillWork& pw, hipStream_t stream) {
+  if (m == 1) return launch_head_batch<VPT, 1>(geo, its, 1, pw, stream);
+  return launch_head_batch<VPT, PREFILL_NB>(geo, its, m, pw, stream);
+}
+
+// A prompt longer than 32 candidates per thread, alone: two-level select
+// when the union of its slices' top-k fits one workgroup's registers (at
+// most 16 per thread), else the streaming select; then its gather.
+hipError_t launch_long(const Geometry& geo, const PrefillItem& it, const PrefillWork& pw,
+                       hipStream_t stream) {
+  SelectBatch<1> sb;
+  sb.item[0] = select_args(geo, it, pw.sel, pw);
+  SelectArgs& sa = sb.item[0];
+  const PrefillShape& sh = sa.sh;
   const int32_t C = sh.c1 - sh.c0;
-  const int32_t per_thread = (C + SEL_THREADS - 1) / SEL_THREADS;
-  const dim3 heads(geo.n_kv_heads);
-  if (per_thread <= 16) {
-    hipLaunchKernelGGL((prefill_select_kernel<16, SEL_HEAD>), heads, dim3(SEL_THREADS), 0, stream,
-                       sa);
-  } else if (per_thread <= 32) {
-    hipLaunchKernelGGL((prefill_select_kernel<32, SEL_HEAD>), heads, dim3(SEL_THREADS), 0, stream,
-                       sa);
+  const int64_t k64 = geo.n_scored;
+  const int32_t ns16 = (C + 16383) / 16384, ns32 = (C + 32767) / 32768;
+  int vpt = 0;
+  if (sh.kk < C && ns16 <= SLICE_MAX && ns16 * k64 <= 16384) {
+    vpt = 16;
+    sa.n_slices = ns16;
+    sa.slice_len = 16384;
+  } else if (sh.kk < C && ns32 <= SLICE_MAX && ns32 * k64 <= 16384) {
+    vpt = 32;
+    sa.n_slices = ns32;
+    sa.slice_len = 32768;
+  }
+  const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads));
+  if (vpt == 0) {
+    hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD, 1>), heads, dim3(SEL_THREADS), 0, stream,
+                       sb);
   } else {
-    // Long prompts: two levels when the union of the slices' top-k fits one
-    // workgroup's registers (at most 16 per thread), else the streaming path.
-    const int64_t k64 = geo.n_scored;
-    const int32_t ns16 = (C + 16383) / 16384, ns32 = (C + 32767) / 32768;
-    int vpt = 0;
-    if (sh.kk < C && ns16 <= SLICE_MAX && ns16 * k64 <= 16384) {
-      vpt = 16;
-      sa.n_slices = ns16;
-      sa.slice_len = 16384;
-    } else if (sh.kk < C && ns32 <= SLICE_MAX && ns32 * k64 <= 16384) {
-      vpt = 32;
-      sa.n_slices = ns32;
-      sa.slice_len = 32768;
-    }
-    if (vpt == 0) {
-      hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD>), heads, dim3(SEL_THREADS), 0, stream,
-                         sa);
-    } else {
-      const dim3 slices(geo.n_kv_heads, sa.n_slices);
-      if (vpt == 16)
-        hipLaunchKernelGGL((prefill_select_kernel<16, SEL_SLICE>), slices, dim3(SEL_THREADS), 0,
-                           stream, sa);
-      else
-        hipLaunchKernelGGL((prefill_select_kernel<32, SEL_SLICE>), slices, dim3(SEL_THREADS), 0,
-                           stream, sa);
-      hipError_t e1 = hipGetLastError();
-      if (e1 != hipSuccess) return e1;
-      hipLaunchKernelGGL((prefill_select_kernel<16, SEL_LIST>), heads, dim3(SEL_THREADS), 0, stream,
-                         sa);
-    }
+    const dim3 slices(static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(sa.n_slices));
+    if (vpt == 16)
+      hipLaunchKernelGGL((prefill_select_kernel<16, SEL_SLICE, 1>), slices, dim3(SEL_THREADS), 0,
+                         stream, sb);
+    else
+      hipLaunchKernelGGL((prefill_select_kernel<32, SEL_SLICE, 1>), slices, dim3(SEL_THREADS), 0,
+                         stream, sb);
+    hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+    hipLaunchKernelGGL((prefill_select_kernel<16, SEL_LIST, 1>), heads, dim3(SEL_THREADS), 0,
+                       stream, sb);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (sh.count == 0) return hipSuccess;
-  const int32_t rows_per_block = 64;
-  const uint32_t nblk = static_cast<uint32_t>((sh.count + rows_per_block - 1) / rows_per_block);
-  const int64_t row0 = head0 * geo.budget;
-  const int64_t el0 = row0 * geo.head_dim;
-  const dim3 grid(nblk, geo.n_kv_heads);
-  if (geo.head_dim == 128) {
-    hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, dim3(GATHER_THREADS), 0, stream, k, v,
-                       scores, sh, kcap, geo.budget, geo.n_recent, rows_per_block, sel,
-                       lv.kc + el0, lv.vc + el0, lv.keys + row0, lv.pos + row0,
-                       lv.ring + head0 * geo.n_recent);
-  } else {
-    hipLaunchKernelGGL(prefill_gather_kernel<64>, grid, dim3(GATHER_THREADS), 0, stream, k, v,
-                       scores, sh, kcap, geo.budget, geo.n_recent, rows_per_block, sel,
-                       lv.kc + el0, lv.vc + el0, lv.keys + row0, lv.pos + row0,
-                       lv.ring + head0 * geo.n_recent);
+  GatherBatch<1> gb;
+  gb.item[0] = gather_item(geo, it, pw.sel);
+  return launch_gather<1>(geo, gb, 1, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, int32_t n,
+                                const PrefillWork& pw, hipStream_t stream) {
+  const int32_t chunk = pw.sel_items < PREFILL_NB ? pw.sel_items : PREFILL_NB;
+  if (chunk < 1) return hipErrorInvalidValue;
+  const PrefillItem* cls16[PREFILL_NB];
+  const PrefillItem* cls32[PREFILL_NB];
+  int32_t m16 = 0, m32 = 0;
+  auto flush = [&](const PrefillItem** its, int32_t& m, int vpt) -> hipError_t {
+    if (m == 0) return hipSuccess;
+    hipError_t e = vpt == 16 ? launch_head_class<16>(geo, its, m, pw, stream)
+                             : launch_head_class<32>(geo, its, m, pw, stream);
+    m = 0;
+    return e;
+  };
+  for (int32_t i = 0; i < n; ++i) {
+    const PrefillItem& it = items[i];
+    if (it.n_tokens <= 0) continue;
+    const PrefillShape sh = prefill_shape(it.n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
+    const int32_t per_thread = (sh.c1 - sh.c0 + SEL_THREADS - 1) / SEL_THREADS;
+    hipError_t e = hipSuccess;
+    if (per_thread <= 16) {
+      cls16[m16++] = &it;
+      if (m16 == chunk) e = flush(cls16, m16, 16);
+    } else if (per_thread <= 32) {
+      cls32[m32++] = &it;
+      if (m32 == chunk) e = flush(cls32, m32, 32);
+    } else {
+      e = launch_long(geo, it, pw, stream);  // uses selection slot 0: stream-ordered
+    }
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  hipError_t e = flush(cls16, m16, 16);
+  if (e != hipSuccess) return e;
+  return flush(cls32, m32, 32);
 }
 
 }  // namespace kvpop

@@ -148,6 +148,30 @@ KVPOP_API int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t s
                           const uint16_t* k, const uint16_t* v, const float* scores,
                           void* stream);
 
+/* Prefill compaction of several prompts at once: items[i] fills the empty
+ * (layer, seq) it names exactly as kvpop_prefill_compact would (same
+ * layouts for k, v and scores; n_tokens == 0 leaves it empty).  The prompts
+ * share kernel launches (up to 32 per launch; prompts longer than 32,768
+ * candidates per head run one at a time), which is how a serving batch, or
+ * every layer of one prompt, is compacted without one launch pair per
+ * prompt.  Stream-ordered and asynchronous; `items` is read during the call
+ * only; the device buffers it points to must stay alive until the stream
+ * passes the call.  Every item is checked before anything is enqueued.
+ * Errors: KVPOP_EINVAL (NULL pointers, bad indices, n_tokens < 0, the same
+ * (layer, seq) twice), KVPOP_ESTATE (an item's (layer, seq) is not empty,
+ * n_tokens > max_positions, or the cache is poisoned), KVPOP_EHIP. */
+typedef struct kvpop_prefill_item {
+  int32_t layer;
+  int32_t seq;
+  int32_t n_tokens;
+  int32_t pad;          /* unused */
+  const uint16_t* k;    /* device [Hkv][n_tokens][D] bf16 */
+  const uint16_t* v;    /* device [Hkv][n_tokens][D] bf16 */
+  const float* scores;  /* device [Hkv][n_tokens] float32 */
+} kvpop_prefill_item;
+KVPOP_API int kvpop_prefill_compact_batch(kvpop_cache* cache, int32_t n_items,
+                                          const kvpop_prefill_item* items, void* stream);
+
 /* One decode step of every sequence of `layer`: sequence b processes position
  * n_b + 1 (position 0 if empty).
  *   q            device [batch][Hq][D] bf16, the query of the new token

@@ -115,6 +115,7 @@ def test_null_cache_handle_everywhere(lib):
     assert lib.kvpop_prefix_thresholds(None, 4, 1, 1, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_future_attention_target(None, 4, 1, 1, 1, 1, None) == abi.KVPOP_EINVAL
     assert lib.kvpop_cache_prune(None, 0, None) == abi.KVPOP_EINVAL
+    assert lib.kvpop_prefill_compact_batch(None, 1, None, None) == abi.KVPOP_EINVAL
     lib.kvpop_cache_destroy(None)
 
 

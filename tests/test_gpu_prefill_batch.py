@@ -1,0 +1,121 @@
+"""Batched prefill compaction (kvpop_prefill_compact_batch) through the C ABI.
+
+Every prompt of a batch must end exactly as a single kvpop_prefill_compact
+of it would: the kept sets against the oracle and, bit for bit, against a
+cache filled one prompt at a time; the following decode steps must then
+produce identical outputs.  Batches mix every prompt class (inside the
+sinks or the window, up to 16 and 32 candidates per thread, long prompts on
+the two-level path, empty prompts), span layers, exceed one launch's 32
+prompts, and run with a selection buffer smaller than 32 prompts.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import (Geo, Stream, check_output, log, make_cache, make_oracle, out_to_f64,
+                         to_dev_bf16, to_dev_f32)
+from fixed_budget_learned_amd import abi
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    abi.load()
+    torch.cuda.init()
+
+
+def _run(geo, n_layers, batch, prompts, steps, seed, kind="normal", check_oracle=True):
+    """prompts: {(layer, seq): P}.  Fills one cache with a single batched call
+    and another one prompt at a time, decodes `steps` steps on every layer
+    of both, and compares."""
+    streams = {key: Stream(geo, P + steps, seed + 97 * i, kind)
+               for i, (key, P) in enumerate(sorted(prompts.items()))}
+    dev = {key: (to_dev_bf16(s.k[:, :prompts[key]]), to_dev_bf16(s.v[:, :prompts[key]]),
+                 to_dev_f32(s.scores[:, :prompts[key]])) for key, s in streams.items()}
+    log(f"batch prefill geo={geo} layers={n_layers} batch={batch} prompts={sorted(prompts.values())}")
+    cb = make_cache(geo, n_layers=n_layers, batch=batch)
+    cs = make_cache(geo, n_layers=n_layers, batch=batch)
+    cb.prefill_compact_batch([(l, b, *dev[(l, b)]) for (l, b) in sorted(prompts)])
+    for (l, b) in sorted(prompts):
+        cs.prefill_compact(l, b, *dev[(l, b)])
+    torch.cuda.synchronize()
+    for (l, b), P in prompts.items():
+        sb, ss = cb.state(l, b), cs.state(l, b)
+        assert sb.n == ss.n == P - 1, ((l, b), sb.n, ss.n)
+        for g in range(geo.n_kv_heads):
+            assert sb.kept[g].tolist() == ss.kept[g].tolist(), ((l, b), g)
+        if check_oracle and P > 0:
+            s = streams[(l, b)]
+            orc = make_oracle(geo)
+            orc.prefill(s.k[:, :P], s.v[:, :P], s.scores[:, :P])
+            for g in range(geo.n_kv_heads):
+                assert sb.kept[g].tolist() == orc.kept(g), ((l, b), g)
+    # decode every sequence of every layer a few steps: identical outputs
+    Hq, Hkv, D = geo.n_q_heads, geo.n_kv_heads, geo.head_dim
+    for l in range(n_layers):
+        if not any(key[0] == l for key in prompts):
+            continue
+        out_b = torch.empty((batch, Hq, D), dtype=torch.bfloat16, device="cuda")
+        out_s = torch.empty_like(out_b)
+        for i in range(steps):
+            q = np.zeros((batch, Hq, D), np.uint16)
+            kn = np.zeros((batch, Hkv, D), np.uint16)
+            vn = np.zeros((batch, Hkv, D), np.uint16)
+            sl = np.zeros((batch, Hkv), np.float32)
+            for b in range(batch):
+                if (l, b) in prompts:
+                    s, P = streams[(l, b)], prompts[(l, b)]
+                    q[b], kn[b], vn[b], sl[b] = s.q[P + i], s.k[:, P + i], s.v[:, P + i], s.leaving(P + i)
+            args = (to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn), to_dev_f32(sl))
+            cb.decode_step(l, *args, out_b)
+            cs.decode_step(l, *args, out_s)
+            assert torch.equal(out_b.view(torch.int16), out_s.view(torch.int16)), (l, i)
+    cb.close()
+    cs.close()
+
+
+def test_every_prompt_class_in_one_batch():
+    geo = Geo(8, 2, 128, 4, 700, 64)
+    prompts = {(0, 0): 0, (0, 1): 3, (0, 2): 60, (0, 3): 900, (0, 4): 12000,
+               (1, 0): 20000, (1, 1): 40000, (1, 2): 5, (1, 3): 16500, (1, 4): 1}
+    _run(geo, 2, 5, prompts, 6, seed=3)
+
+
+def test_more_prompts_than_one_launch_holds():
+    geo = Geo(4, 1, 64, 4, 120, 16)
+    rng = np.random.default_rng(5)
+    prompts = {(l, b): int(rng.integers(0, 3000)) for l in range(3) for b in range(15)}
+    _run(geo, 3, 15, prompts, 3, seed=11, kind="ties")
+
+
+def test_small_selection_buffer():
+    """A scored region this large leaves room for only a few prompts per launch."""
+    geo = Geo(8, 8, 64, 4, 120000, 16)
+    prompts = {(0, b): 3000 + 1500 * b for b in range(9)}
+    _run(geo, 1, 9, prompts, 2, seed=17, check_oracle=False)
+
+
+def test_batch_errors_change_nothing():
+    geo = Geo(4, 1, 64, 4, 50, 16)
+    cache = make_cache(geo, n_layers=2, batch=2)
+    s = Stream(geo, 300, 1)
+    k, v, sc = to_dev_bf16(s.k[:, :300]), to_dev_bf16(s.v[:, :300]), to_dev_f32(s.scores[:, :300])
+    with pytest.raises(abi.KVpopError) as e:
+        cache.prefill_compact_batch([(0, 0, k, v, sc), (0, 0, k, v, sc)])
+    assert e.value.code == abi.KVPOP_EINVAL
+    with pytest.raises(abi.KVpopError) as e:
+        cache.prefill_compact_batch([(0, 1, k, v, sc), (2, 0, k, v, sc)])
+    assert e.value.code == abi.KVPOP_EINVAL
+    assert cache.state(0, 1).n == -1  # nothing happened
+    cache.prefill_compact(1, 1, k, v, sc)
+    with pytest.raises(abi.KVpopError) as e:
+        cache.prefill_compact_batch([(0, 0, k, v, sc), (1, 1, k, v, sc)])
+    assert e.value.code == abi.KVPOP_ESTATE
+    assert cache.state(0, 0).n == -1
+    cache.prefill_compact_batch([])
+    cache.prefill_compact_batch([(0, 0, k, v, sc)])
+    assert cache.state(0, 0).n == 299
+    cache.close()

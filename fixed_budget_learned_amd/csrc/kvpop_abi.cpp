@@ -23,7 +23,8 @@ struct Layout {
   size_t kc, vc, keys, pos, ring, ctl, sel, slice_keys, slice_nan, part_acc, part_ml, part_min,
       tickets, total;
   int32_t nsplit, rows_per_split, threads, rows_per_thread;
-  int32_t sel_items;  // prompts one batched prefill launch can select at once
+  int32_t sel_items;    // prompts one batched prefill launch can select at once
+  int32_t slice_items;  // long prompts one batched two-level select can hold
 };
 
 bool mul_ok(size_t a, size_t b, size_t* r) {
@@ -109,9 +110,13 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   L->sel_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
                                                               (size_t(16) << 20) / sel_one)));
   ok = ok && take(sel_one * size_t(L->sel_items), &L->sel);
-  ok = ok && take(size_t(c.n_kv_heads) * kvpop::SLICE_MAX * size_t(std::max(c.n_scored, 1)) * 8,
-                  &L->slice_keys);
-  ok = ok && take(size_t(c.n_kv_heads) * kvpop::SLICE_MAX * 4, &L->slice_nan);
+  // first-level keys of long prompts: up to PREFILL_NB prompts, within 64 MiB
+  const size_t slice_one = size_t(c.n_kv_heads) * kvpop::SLICE_MAX *
+                           size_t(std::max(c.n_scored, 1)) * 8;
+  L->slice_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
+                                                                (size_t(64) << 20) / slice_one)));
+  ok = ok && take(slice_one * size_t(L->slice_items), &L->slice_keys);
+  ok = ok && take(size_t(L->slice_items) * c.n_kv_heads * kvpop::SLICE_MAX * 4, &L->slice_nan);
   const size_t parts = heads * size_t(L->nsplit);
   ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
   ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
@@ -180,6 +185,7 @@ struct kvpop_cache {
     pw.sel_items = lay.sel_items;
     pw.slice_keys = reinterpret_cast<uint64_t*>(base + lay.slice_keys);
     pw.slice_nan = reinterpret_cast<int32_t*>(base + lay.slice_nan);
+    pw.slice_items = lay.slice_items;
     return pw;
   }
   kvpop::DecodeWork work() const {

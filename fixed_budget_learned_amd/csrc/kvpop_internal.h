@@ -82,8 +82,9 @@ constexpr int PREFILL_NB = 32;
 struct PrefillWork {
   int32_t* sel;          // [sel_items][Hkv][k] kept candidate positions
   int32_t sel_items;     // prompts the selection buffer holds (1 .. PREFILL_NB)
-  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level keys
-  int32_t* slice_nan;    // [Hkv][SLICE_MAX] first-level NaN flags
+  uint64_t* slice_keys;  // [slice_items][Hkv][SLICE_MAX][k] first-level keys
+  int32_t* slice_nan;    // [slice_items][Hkv][SLICE_MAX] first-level NaN flags
+  int32_t slice_items;   // long prompts the first-level buffers hold (1 .. PREFILL_NB)
 };
 // One prompt to compact into an empty (layer, sequence).
 struct PrefillItem {

@@ -191,6 +191,8 @@ struct SelectBatch {
 template <int VPT, int MODE, int NB>
 __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch<NB> batch) {
   const SelectArgs& a = batch.item[blockIdx.z];
+  // a batch launch covers its longest prompt's slices: shorter ones have none here
+  if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= a.n_slices) return;
   static_assert(MODE != SEL_LIST || VPT == 16, "list mode stages 64-bit keys: at most 16 per thread");
   static_assert(MODE == SEL_HEAD || VPT > 0, "slice and list modes keep codes in registers");
   constexpr int NWAVE = SEL_THREADS / WAVE;
@@ -675,45 +677,75 @@ hipError_t launch_head_class(const Geometry& geo, const PrefillItem* const* its,
   return launch_head_batch<VPT, PREFILL_NB>(geo, its, m, pw, stream);
 }
 
-// A prompt longer than 32 candidates per thread, alone: two-level select
-// when the union of its slices' top-k fits one workgroup's registers (at
-// most 16 per thread), else the streaming select; then its gather.
-hipError_t launch_long(const Geometry& geo, const PrefillItem& it, const PrefillWork& pw,
-                       hipStream_t stream) {
-  SelectBatch<1> sb;
-  sb.item[0] = select_args(geo, it, pw.sel, pw);
-  SelectArgs& sa = sb.item[0];
-  const PrefillShape& sh = sa.sh;
+// How a prompt longer than 32 candidates per thread selects: two levels
+// with 16k or 32k-candidate slices when the union of its slices' top-k fits
+// one workgroup's registers (at most 16 per thread), else (vpt 0) the
+// streaming select.
+struct LongPlan {
+  int vpt;
+  int32_t n_slices, slice_len;
+};
+
+LongPlan long_plan(const Geometry& geo, const PrefillShape& sh) {
   const int32_t C = sh.c1 - sh.c0;
   const int64_t k64 = geo.n_scored;
   const int32_t ns16 = (C + 16383) / 16384, ns32 = (C + 32767) / 32768;
-  int vpt = 0;
-  if (sh.kk < C && ns16 <= SLICE_MAX && ns16 * k64 <= 16384) {
-    vpt = 16;
-    sa.n_slices = ns16;
-    sa.slice_len = 16384;
-  } else if (sh.kk < C && ns32 <= SLICE_MAX && ns32 * k64 <= 16384) {
-    vpt = 32;
-    sa.n_slices = ns32;
-    sa.slice_len = 32768;
+  if (sh.kk < C && ns16 <= SLICE_MAX && ns16 * k64 <= 16384) return {16, ns16, 16384};
+  if (sh.kk < C && ns32 <= SLICE_MAX && ns32 * k64 <= 16384) return {32, ns32, 32768};
+  return {0, 1, 0};
+}
+
+// Two-level selects of m prompts with the same slice length, then their
+// gather; each prompt uses selection and slice slot i of the workspace.
+template <int VPT, int NB>
+hipError_t launch_two_level(const Geometry& geo, const PrefillItem* const* its, int32_t m,
+                            const PrefillWork& pw, hipStream_t stream) {
+  const int64_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
+  const int64_t slice_one = static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX * kcap;
+  SelectBatch<NB> sb;
+  GatherBatch<NB> gb;
+  int32_t max_slices = 1;
+  for (int32_t i = 0; i < m; ++i) {
+    int32_t* sel = pw.sel + i * static_cast<int64_t>(geo.n_kv_heads) * kcap;
+    SelectArgs& sa = sb.item[i];
+    sa = select_args(geo, *its[i], sel, pw);
+    const LongPlan lp = long_plan(geo, sa.sh);
+    sa.n_slices = lp.n_slices;
+    sa.slice_len = lp.slice_len;
+    sa.slice_keys = pw.slice_keys + i * slice_one;
+    sa.slice_nan = pw.slice_nan + i * static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX;
+    max_slices = lp.n_slices > max_slices ? lp.n_slices : max_slices;
+    gb.item[i] = gather_item(geo, *its[i], sel);
   }
+  const dim3 slices(static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(max_slices),
+                    static_cast<uint32_t>(m));
+  hipLaunchKernelGGL((prefill_select_kernel<VPT, SEL_SLICE, NB>), slices, dim3(SEL_THREADS), 0,
+                     stream, sb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads), 1u, static_cast<uint32_t>(m));
+  hipLaunchKernelGGL((prefill_select_kernel<16, SEL_LIST, NB>), heads, dim3(SEL_THREADS), 0,
+                     stream, sb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gather<NB>(geo, gb, m, stream);
+}
+
+template <int VPT>
+hipError_t launch_two_level_class(const Geometry& geo, const PrefillItem* const* its, int32_t m,
+                                  const PrefillWork& pw, hipStream_t stream) {
+  if (m == 1) return launch_two_level<VPT, 1>(geo, its, 1, pw, stream);
+  return launch_two_level<VPT, PREFILL_NB>(geo, its, m, pw, stream);
+}
+
+// A prompt for which even two levels do not fit: the streaming select, alone.
+hipError_t launch_streaming(const Geometry& geo, const PrefillItem& it, const PrefillWork& pw,
+                            hipStream_t stream) {
+  SelectBatch<1> sb;
+  sb.item[0] = select_args(geo, it, pw.sel, pw);
   const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads));
-  if (vpt == 0) {
-    hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD, 1>), heads, dim3(SEL_THREADS), 0, stream,
-                       sb);
-  } else {
-    const dim3 slices(static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(sa.n_slices));
-    if (vpt == 16)
-      hipLaunchKernelGGL((prefill_select_kernel<16, SEL_SLICE, 1>), slices, dim3(SEL_THREADS), 0,
-                         stream, sb);
-    else
-      hipLaunchKernelGGL((prefill_select_kernel<32, SEL_SLICE, 1>), slices, dim3(SEL_THREADS), 0,
-                         stream, sb);
-    hipError_t e1 = hipGetLastError();
-    if (e1 != hipSuccess) return e1;
-    hipLaunchKernelGGL((prefill_select_kernel<16, SEL_LIST, 1>), heads, dim3(SEL_THREADS), 0,
-                       stream, sb);
-  }
+  hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD, 1>), heads, dim3(SEL_THREADS), 0, stream,
+                     sb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GatherBatch<1> gb;
@@ -723,40 +755,59 @@ hipError_t launch_long(const Geometry& geo, const PrefillItem& it, const Prefill
 
 }  // namespace
 
+// Prompts are grouped by how they select (up to 16 or 32 candidates per
+// thread; two levels with 16k or 32k slices; streaming) and each group runs
+// in launches of up to `chunk` prompts.  Launches share the workspace, which
+// is safe because they are ordered on the stream.
 hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, int32_t n,
                                 const PrefillWork& pw, hipStream_t stream) {
-  const int32_t chunk = pw.sel_items < PREFILL_NB ? pw.sel_items : PREFILL_NB;
-  if (chunk < 1) return hipErrorInvalidValue;
-  const PrefillItem* cls16[PREFILL_NB];
-  const PrefillItem* cls32[PREFILL_NB];
-  int32_t m16 = 0, m32 = 0;
-  auto flush = [&](const PrefillItem** its, int32_t& m, int vpt) -> hipError_t {
+  int32_t chunk = pw.sel_items < PREFILL_NB ? pw.sel_items : PREFILL_NB;
+  const int32_t chunk_long = pw.slice_items < chunk ? pw.slice_items : chunk;
+  if (chunk < 1 || chunk_long < 1) return hipErrorInvalidValue;
+  enum { C16, C32, L16, L32, NCLS };
+  const PrefillItem* grp[NCLS][PREFILL_NB];
+  int32_t cnt[NCLS] = {0, 0, 0, 0};
+  auto flush = [&](int c) -> hipError_t {
+    const int32_t m = cnt[c];
+    cnt[c] = 0;
     if (m == 0) return hipSuccess;
-    hipError_t e = vpt == 16 ? launch_head_class<16>(geo, its, m, pw, stream)
-                             : launch_head_class<32>(geo, its, m, pw, stream);
-    m = 0;
-    return e;
+    switch (c) {
+      case C16: return launch_head_class<16>(geo, grp[c], m, pw, stream);
+      case C32: return launch_head_class<32>(geo, grp[c], m, pw, stream);
+      case L16: return launch_two_level_class<16>(geo, grp[c], m, pw, stream);
+      default: return launch_two_level_class<32>(geo, grp[c], m, pw, stream);
+    }
   };
   for (int32_t i = 0; i < n; ++i) {
     const PrefillItem& it = items[i];
     if (it.n_tokens <= 0) continue;
     const PrefillShape sh = prefill_shape(it.n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
     const int32_t per_thread = (sh.c1 - sh.c0 + SEL_THREADS - 1) / SEL_THREADS;
-    hipError_t e = hipSuccess;
+    int c;
     if (per_thread <= 16) {
-      cls16[m16++] = &it;
-      if (m16 == chunk) e = flush(cls16, m16, 16);
+      c = C16;
     } else if (per_thread <= 32) {
-      cls32[m32++] = &it;
-      if (m32 == chunk) e = flush(cls32, m32, 32);
+      c = C32;
     } else {
-      e = launch_long(geo, it, pw, stream);  // uses selection slot 0: stream-ordered
+      const LongPlan lp = long_plan(geo, sh);
+      if (lp.vpt == 0) {
+        hipError_t e = launch_streaming(geo, it, pw, stream);
+        if (e != hipSuccess) return e;
+        continue;
+      }
+      c = lp.vpt == 16 ? L16 : L32;
     }
+    grp[c][cnt[c]++] = &it;
+    if (cnt[c] == (c >= L16 ? chunk_long : chunk)) {
+      hipError_t e = flush(c);
+      if (e != hipSuccess) return e;
+    }
+  }
+  for (int c = 0; c < NCLS; ++c) {
+    hipError_t e = flush(c);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = flush(cls16, m16, 16);
-  if (e != hipSuccess) return e;
-  return flush(cls32, m32, 32);
+  return hipSuccess;
 }
 
 }  // namespace kvpop

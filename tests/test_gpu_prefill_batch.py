@@ -5,15 +5,15 @@ of it would: the kept sets against the oracle and, bit for bit, against a
 cache filled one prompt at a time; the following decode steps must then
 produce identical outputs.  Batches mix every prompt class (inside the
 sinks or the window, up to 16 and 32 candidates per thread, long prompts on
-the two-level path, empty prompts), span layers, exceed one launch's 32
-prompts, and run with a selection buffer smaller than 32 prompts.
+the two-level path with different slice counts, the streaming path, empty
+prompts), span layers, exceed one launch's 32 prompts, and run with
+selection and first-level buffers smaller than 32 prompts.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_harness import (Geo, Stream, check_output, log, make_cache, make_oracle, out_to_f64,
-                         to_dev_bf16, to_dev_f32)
+from gpu_harness import Geo, Stream, log, make_cache, make_oracle, to_dev_bf16, to_dev_f32
 from fixed_budget_learned_amd import abi
 
 pytestmark = pytest.mark.gpu
@@ -119,3 +119,21 @@ def test_batch_errors_change_nothing():
     cache.prefill_compact_batch([(0, 0, k, v, sc)])
     assert cache.state(0, 0).n == 299
     cache.close()
+
+
+def test_long_prompts_two_level_batched():
+    """Several long prompts (two-level select, 3 to 7 slices each) share launches."""
+    geo = Geo(4, 2, 64, 4, 700, 32)
+    prompts = {(0, 0): 33000, (0, 1): 40000, (0, 2): 70000, (0, 3): 100000, (0, 4): 17000,
+               (0, 5): 0}
+    _run(geo, 1, 6, prompts, 3, seed=23)
+
+
+def test_long_prompts_small_slice_buffer_and_streaming():
+    """Two-level prompts beyond what the first-level buffer holds at once (7),
+    and, in another cache, a prompt only the streaming select can take."""
+    geo = Geo(8, 8, 64, 4, 8000, 16)
+    prompts = {(0, b): 40000 + 2500 * b for b in range(9)}
+    _run(geo, 1, 9, prompts, 2, seed=29, check_oracle=False)
+    geo = Geo(4, 1, 64, 4, 9000, 16)
+    _run(geo, 1, 3, {(0, 0): 70000, (0, 1): 20000, (0, 2): 41000}, 2, seed=31)

@@ -304,22 +304,48 @@ def layered_config(w, steps: int, reps: int):
     cache = abi.KVpopCache(abi.make_config(L, 1, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
                                            max_positions=P + steps * (reps + 2) + 1))
     stream = torch.cuda.Stream()
-    pre_ms = 0.0
+    pre_ms = pre_batch_ms = 0.0
     if P > 0:
+        # every layer's prompt (19 GB for the 131k workload) resident at once
+        ks, vs, scs = [], [], []
         for layer in range(L):
-            k = torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16)
-            v = torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16)
-            sc = torch.from_numpy(draw_scores(rng_for(w.wid, layer, 0, T_SCORES), w.score_dist,
-                                              (Hkv, P))).to("cuda")
-            torch.cuda.synchronize()
+            ks.append(torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16))
+            vs.append(torch.randn((Hkv, P, D), generator=gen, device="cuda").to(torch.bfloat16))
+            scs.append(torch.from_numpy(draw_scores(rng_for(w.wid, layer, 0, T_SCORES),
+                                                    w.score_dist, (Hkv, P))).to("cuda"))
+        torch.cuda.synchronize()
+        # one call per layer ...
+        for layer in range(L):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 e0.record(stream)
-                cache.prefill_compact(layer, 0, k, v, sc)
+                cache.prefill_compact(layer, 0, ks[layer], vs[layer], scs[layer])
                 e1.record(stream)
             torch.cuda.synchronize()
             pre_ms += e0.elapsed_time(e1)
-            del k, v, sc
+        # ... and every layer in one batched call, into a second cache
+        cb = abi.KVpopCache(abi.make_config(L, 1, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
+                                            max_positions=P + 1))
+        items = [(layer, 0, ks[layer], vs[layer], scs[layer]) for layer in range(L)]
+        with torch.cuda.stream(stream):
+            cb.prefill_compact_batch(items)  # warm-up
+        torch.cuda.synchronize()
+        for layer in range(L):
+            cb.reset(0 + layer, 0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            cb.prefill_compact_batch(items)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        pre_batch_ms = e0.elapsed_time(e1)
+        st_a, st_b = cache.state(L - 1, 0), cb.state(L - 1, 0)
+        assert all(a.tolist() == b.tolist() for a, b in zip(st_a.kept, st_b.kept)), \
+            "batched prefill differs"
+        cb.close()
+        del ks, vs, scs, items
+        torch.cuda.empty_cache()
     q = torch.randn((steps, L, 1, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
     kn = torch.randn((steps, L, 1, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
     vn = torch.randn((steps, L, 1, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
@@ -360,11 +386,13 @@ def layered_config(w, steps: int, reps: int):
            "decode_bytes_per_step": dbytes, "decode_steps_timed": reps * steps}
     if P > 0:
         pbytes = L * prefill_bytes(w, P)
-        res.update({"prefill_us_all_layers": pre_ms * 1e3,
-                    "prefill_tokens_per_s": P / (pre_ms / 1e3),
-                    "prefill_GBps": pbytes / (pre_ms / 1e3) / 1e9,
-                    "prefill_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
-                    "prefill_bytes": pbytes})
+        res.update({"prefill_us_all_layers": pre_batch_ms * 1e3,
+                    "prefill_tokens_per_s": P / (pre_batch_ms / 1e3),
+                    "prefill_GBps": pbytes / (pre_batch_ms / 1e3) / 1e9,
+                    "prefill_frac": pbytes / (pre_batch_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                    "prefill_bytes": pbytes,
+                    "prefill_launch": "all layers in one kvpop_prefill_compact_batch call",
+                    "prefill_us_one_call_per_layer": pre_ms * 1e3})
     return res
 
 
@@ -506,9 +534,17 @@ def batched_serving(steps: int, reps: int, mode: str = "graph"):
     cache = abi.KVpopCache(abi.make_config(1, B, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
                                            max_positions=max(lens) + steps + 1))
 
-    def pre():
+    items = [(0, b, pk[b], pv[b], ps[b]) for b in range(B)]
+
+    def reset():
         for b in range(B):
             cache.reset(0, b)
+
+    def pre():  # every prompt of the batch in one call
+        cache.prefill_compact_batch(items)
+
+    def pre_each():  # one call per prompt, for comparison
+        for b in range(B):
             cache.prefill_compact(0, b, pk[b], pv[b], ps[b])
 
     def dec():
@@ -517,31 +553,44 @@ def batched_serving(steps: int, reps: int, mode: str = "graph"):
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
+        reset()
         pre()
         dec()
     torch.cuda.synchronize()
     if mode == "graph":
-        gp, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        gr, gp, ge, gd = (torch.cuda.CUDAGraph() for _ in range(4))
+        with torch.cuda.graph(gr, stream=stream):
+            reset()
+        with torch.cuda.graph(ge, stream=stream):
+            pre_each()
+        with torch.cuda.stream(stream):
+            reset()  # the batched call below needs empty sequences
         with torch.cuda.graph(gp, stream=stream):
             pre()
         with torch.cuda.graph(gd, stream=stream):
             dec()
-        run_pre, run_dec = gp.replay, gd.replay
+        run_reset, run_pre, run_each, run_dec = gr.replay, gp.replay, ge.replay, gd.replay
     else:
-        run_pre, run_dec = pre, dec
-    pre_ms = dec_ms = 0.0
+        run_reset, run_pre, run_each, run_dec = reset, pre, pre_each, dec
+    pre_ms = each_ms = dec_ms = 0.0
     for r in range(reps + 1):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         with torch.cuda.stream(stream):
+            run_reset()
             e[0].record(stream)
-            run_pre()
+            run_each()
             e[1].record(stream)
-            run_dec()
+            run_reset()
             e[2].record(stream)
+            run_pre()
+            e[3].record(stream)
+            run_dec()
+            e[4].record(stream)
         torch.cuda.synchronize()
         if r > 0:
-            pre_ms += e[0].elapsed_time(e[1])
-            dec_ms += e[1].elapsed_time(e[2])
+            each_ms += e[0].elapsed_time(e[1])
+            pre_ms += e[2].elapsed_time(e[3])
+            dec_ms += e[3].elapsed_time(e[4])
     counts = cache.state(0, B - 1).counts
     assert all(int(c) == w.budget for c in counts), "batched caches not full"
     cache.close()
@@ -563,6 +612,9 @@ def batched_serving(steps: int, reps: int, mode: str = "graph"):
         "prefill_tokens_per_s": ptok / pre_s,
         "prefill_GBps": pbytes / pre_s / 1e9,
         "prefill_frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBPS,
+        "prefill_us": pre_s * 1e6,
+        "prefill_launch": "all 64 prompts in one kvpop_prefill_compact_batch call",
+        "prefill_us_one_call_per_prompt": each_ms * 1e3 / reps,
     }
 
 
@@ -583,6 +635,8 @@ def main():
                     help="skip the tiny, 36-layer and 131k-token workloads and the cold-cache line")
     ap.add_argument("--batched-only", action="store_true",
                     help="run only the batch-64 serving measurement (for profiles)")
+    ap.add_argument("--only", choices=("future", "thresholds", "dynamic"), default=None,
+                    help="run only this section on the one-layer workload (for profiles)")
     ap.add_argument("--no-dense-sweep", action="store_true",
                     help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -609,6 +663,18 @@ def main():
         print(json.dumps({"copy_bytes": x.numel() * 4, "copies": max(1, args.steps)}), flush=True)
         return
 
+    if args.only:
+        abi.load()
+        from fixed_budget_learned_amd.configs import LONG_131K_8X, QWEN3_8B_LAYER_4X
+        if args.only == "future":
+            r = future_target_rate(QWEN3_8B_LAYER_4X, max(1, args.steps))
+        elif args.only == "thresholds":
+            r = [prefix_thresholds_rate(QWEN3_8B_LAYER_4X, max(1, args.steps)),
+                 prefix_thresholds_rate(LONG_131K_8X, max(1, args.steps))]
+        else:
+            r = dynamic_backend(args.decode_steps or 1024, max(1, args.steps))
+        print(json.dumps({args.only: r}), flush=True)
+        return
     if args.batched_only:
         abi.load()
         print(json.dumps({"batched_serving": batched_serving(args.decode_steps or 64, args.steps,

@@ -809,14 +809,16 @@ def main():
     if not args.no_batched:
         result["batched_serving"] = batched_serving(64, 3, args.mode)
     if not args.no_configs:
-        from fixed_budget_learned_amd.configs import (LONG_131K_8X, QWEN3_8B_36L_4X, TINY)
+        from fixed_budget_learned_amd.configs import (LONG_131K_8X, QWEN3_8B_36L_4X, TINY,
+                                                      TP8_SHARE_4X)
         result["decode_cold_cache"] = decode_cold(w, 32)
         result["future_attention_target"] = future_target_rate(w, 3)
         result["prefix_thresholds"] = [prefix_thresholds_rate(w, 5),
                                        prefix_thresholds_rate(LONG_131K_8X, 3)]
         result["configs"] = [layered_config(TINY, 512, 2),
                              layered_config(QWEN3_8B_36L_4X, 32, 2),
-                             layered_config(LONG_131K_8X, 32, 2)]
+                             layered_config(LONG_131K_8X, 32, 2),
+                             layered_config(TP8_SHARE_4X, 256, 2)]
     if not args.no_dense_sweep:
         result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
         result["dynamic_backend"] = dynamic_backend(1024, 3)

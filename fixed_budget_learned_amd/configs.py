@@ -71,6 +71,14 @@ BATCH64_SERVING = Workload(
     prompt_len=None, prompt_len_range=(4096, 32768), decode_steps=512,
     score_dist="qlognormal256")
 
+# One GPU's share of the one-layer 4x workload under tensor parallelism over
+# the 8 KV heads: one KV head and its 4 query heads (a measured shape only).
+TP8_SHARE_4X = Workload(
+    wid=6, name="qwen3_8b_layer_4x_tp8_share", n_layers=1, batch=1, n_q_heads=4,
+    n_kv_heads=1, head_dim=128, n_sink=4, n_scored=3772, n_recent=256,
+    prompt_len=16384, prompt_len_range=None, decode_steps=1024,
+    score_dist="normal")
+
 WORKLOADS = {w.wid: w for w in (TINY, QWEN3_8B_LAYER_4X, QWEN3_8B_36L_4X,
                                 LONG_131K_8X, BATCH64_SERVING)}
 BY_NAME = {w.name: w for w in WORKLOADS.values()}

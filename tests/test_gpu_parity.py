@@ -254,16 +254,19 @@ def test_batched_serving_b64():
     kn = np.zeros((steps, B, w.n_kv_heads, w.head_dim), np.uint16)
     vn = np.zeros_like(kn)
     sl = np.zeros((steps, B, w.n_kv_heads), np.float32)
+    items = []  # all 64 prompts in one batched call, as bench.py times it
     for b in range(B):
         if b % 16 == 0:
-            log(f"  prefill sequence {b}")
+            log(f"  inputs of sequence {b}")
         ts = TokenStream(w, 0, b, int(Ps[b]), steps)
-        cache.prefill_compact(0, b, to_dev_bf16(ts.prompt_k()), to_dev_bf16(ts.prompt_v()),
-                              to_dev_f32(ts.prompt_scores()))
+        items.append((0, b, to_dev_bf16(ts.prompt_k()), to_dev_bf16(ts.prompt_v()),
+                      to_dev_f32(ts.prompt_scores())))
         k_, v_ = ts.step_kv()
         q[:, b], kn[:, b], vn[:, b], sl[:, b] = ts.q, k_, v_, ts.step_leaving_scores()
         del ts
+    cache.prefill_compact_batch(items)
     torch.cuda.synchronize()
+    del items
     kept0 = [cache.state(0, b) for b in range(B)]
     qd, kd, vd, sd = to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn), to_dev_f32(sl)
     out = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")

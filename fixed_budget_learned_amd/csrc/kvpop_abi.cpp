@@ -110,11 +110,12 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   L->sel_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
                                                               (size_t(16) << 20) / sel_one)));
   ok = ok && take(sel_one * size_t(L->sel_items), &L->sel);
-  // first-level keys of long prompts: up to PREFILL_NB prompts, within 64 MiB
+  // first-level keys of long prompts: up to PREFILL_NB prompts, within 128 MiB
+  // (all 36 layers of a 131k-token prompt at k = 1,788 take 66 MB)
   const size_t slice_one = size_t(c.n_kv_heads) * kvpop::SLICE_MAX *
                            size_t(std::max(c.n_scored, 1)) * 8;
   L->slice_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
-                                                                (size_t(64) << 20) / slice_one)));
+                                                                (size_t(128) << 20) / slice_one)));
   ok = ok && take(slice_one * size_t(L->slice_items), &L->slice_keys);
   ok = ok && take(size_t(L->slice_items) * c.n_kv_heads * kvpop::SLICE_MAX * 4, &L->slice_nan);
   const size_t parts = heads * size_t(L->nsplit);
@@ -178,6 +179,10 @@ struct kvpop_cache {
     v.ring = reinterpret_cast<int32_t*>(base + lay.ring) + h0 * cfg.n_recent;
     v.ctl = reinterpret_cast<kvpop::HeadCtl*>(base + lay.ctl) + h0;
     return v;
+  }
+  // cache-wide index of the first KV head of (layer, seq)
+  int64_t head0(int32_t l, int32_t s) const {
+    return (int64_t(l) * cfg.batch + s) * cfg.n_kv_heads;
   }
   kvpop::PrefillWork prefill_work() const {
     kvpop::PrefillWork pw;
@@ -320,9 +325,9 @@ int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_
   it.v = v;
   it.scores = scores;
   it.n_tokens = n_tokens;
-  it.seq = seq;
-  it.lv = cache->layer(layer);
-  hipError_t e = kvpop::launch_prefill_batch(cache->geo(), &it, 1, cache->prefill_work(),
+  it.head0 = cache->head0(layer, seq);
+  hipError_t e = kvpop::launch_prefill_batch(cache->geo(), cache->layer(0), &it, 1,
+                                             cache->prefill_work(),
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;
@@ -364,14 +369,13 @@ int kvpop_prefill_compact_batch(kvpop_cache* cache, int32_t n_items,
     it.v = x.v;
     it.scores = x.scores;
     it.n_tokens = x.n_tokens;
-    it.seq = x.seq;
-    it.lv = cache->layer(x.layer);
+    it.head0 = cache->head0(x.layer, x.seq);
     its.push_back(it);
   }
   if (n_items == 0) return KVPOP_OK;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
-  hipError_t e = kvpop::launch_prefill_batch(cache->geo(), its.data(), n_items,
+  hipError_t e = kvpop::launch_prefill_batch(cache->geo(), cache->layer(0), its.data(), n_items,
                                              cache->prefill_work(),
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

@@ -78,7 +78,7 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
 // top k, then one workgroup per head selects from the union.
 constexpr int SLICE_MAX = 16;
 // A batch of prompts shares launches, up to PREFILL_NB prompts per launch.
-constexpr int PREFILL_NB = 32;
+constexpr int PREFILL_NB = 64;
 struct PrefillWork {
   int32_t* sel;          // [sel_items][Hkv][k] kept candidate positions
   int32_t sel_items;     // prompts the selection buffer holds (1 .. PREFILL_NB)
@@ -92,11 +92,12 @@ struct PrefillItem {
   const uint16_t* v;
   const float* scores;    // [Hkv][n_tokens]
   int32_t n_tokens;
-  int32_t seq;
-  LayerView lv;           // the destination layer
+  int64_t head0;          // cache-wide index of the (layer, sequence)'s first KV head
 };
-hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, int32_t n,
-                                const PrefillWork& pw, hipStream_t stream);
+// `all`: views of the whole cache (layer 0 onwards).
+hipError_t launch_prefill_batch(const Geometry& geo, const LayerView& all,
+                                const PrefillItem* items, int32_t n, const PrefillWork& pw,
+                                hipStream_t stream);
 // Prefix top-k thresholds of a prompt ([Hkv][n_tokens] keys), n_scored <=
 // THR_KMAX.
 constexpr int THR_KMAX = 4096;

@@ -22,7 +22,7 @@
 //           per-slot position and key, and the window ring.
 // A batch of (layer, sequence) prompts shares one select and one gather
 // launch: the grid's z is the prompt, each reading its own descriptor from
-// the kernel arguments (up to PREFILL_NB per launch).
+// the kernel arguments (up to PREFILL_NB = 64 per launch, 3.6 KB of arguments).
 // Slot layout after prefill: sinks, then selected candidates in ascending
 // position, then the window in ascending position.
 #include <hip/hip_runtime.h>
@@ -182,15 +182,39 @@ struct SelectArgs {
   int32_t n_slices, slice_len;
 };
 
-// Descriptors of the prompts of one launch (grid z = prompt).
+// One prompt of a select launch.  head0: the cache-wide index of its
+// (layer, sequence)'s first KV head.
+struct SelectItem {
+  const float* scores;   // [Hkv][P]
+  int32_t* sel;          // [Hkv][k] selection slot of the prompt
+  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level slot of the prompt
+  int32_t* slice_nan;    // [Hkv][SLICE_MAX]
+  int64_t head0;
+  int32_t P, n_slices, slice_len;
+};
+
+// Descriptors of the prompts of one launch (grid z = prompt), with what they
+// share; kept small enough for the kernel arguments.
 template <int NB>
 struct SelectBatch {
-  SelectArgs item[NB];
+  HeadCtl* ctl;          // cache-wide control blocks
+  int32_t s, k, W;
+  SelectItem item[NB];
 };
 
 template <int VPT, int MODE, int NB>
 __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch<NB> batch) {
-  const SelectArgs& a = batch.item[blockIdx.z];
+  const SelectItem& it = batch.item[blockIdx.z];
+  SelectArgs a;
+  a.scores = it.scores;
+  a.sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
+  a.k = batch.k;
+  a.sel = it.sel;
+  a.ctl = batch.ctl + it.head0;
+  a.slice_keys = it.slice_keys;
+  a.slice_nan = it.slice_nan;
+  a.n_slices = it.n_slices;
+  a.slice_len = it.slice_len;
   // a batch launch covers its longest prompt's slices: shorter ones have none here
   if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= a.n_slices) return;
   static_assert(MODE != SEL_LIST || VPT == 16, "list mode stages 64-bit keys: at most 16 per thread");
@@ -471,31 +495,34 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch
 // One prompt of a gather launch: its inputs, selection and destination
 // (the cache rows of its (layer, sequence), head 0).
 struct GatherItem {
-  const uint16_t* k;
+  const uint16_t* k;     // [Hkv][P][D]
   const uint16_t* v;
-  const float* scores;
-  PrefillShape sh;
-  const int32_t* sel;
-  uint16_t* kc;
-  uint16_t* vc;
-  uint64_t* keys;
-  int32_t* pos;
-  int32_t* ring;
+  const float* scores;   // [Hkv][P]
+  const int32_t* sel;    // [Hkv][k] its selection
+  int64_t head0;         // cache-wide index of its first KV head
+  int32_t P;
 };
 
 template <int NB>
 struct GatherBatch {
+  uint16_t* kc;          // cache-wide rows and slot metadata
+  uint16_t* vc;
+  uint64_t* keys;
+  int32_t* pos;
+  int32_t* ring;
+  int32_t s, k, W, budget, rows_per_block;
   GatherItem item[NB];
 };
 
 // Rows per gather workgroup: 256 threads move 16 bytes each per pass.
 template <int D, int NB>
-__global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(
-    GatherBatch<NB> batch, int32_t kcap, int32_t budget, int32_t W, int32_t rows_per_block) {
+__global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBatch<NB> batch) {
   constexpr int LPR = D / 8;                   // lanes per row (16 B each)
   constexpr int RPP = GATHER_THREADS / LPR;    // rows per pass
   const GatherItem& it = batch.item[blockIdx.z];
-  const PrefillShape& sh = it.sh;
+  const PrefillShape sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
+  const int32_t kcap = batch.k > 0 ? batch.k : 1;
+  const int32_t budget = batch.budget, W = batch.W, rows_per_block = batch.rows_per_block;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int rg = tid / LPR;
@@ -506,11 +533,12 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(
   const uint16_t* __restrict__ v = it.v;
   const float* __restrict__ scores = it.scores;
   const int32_t* __restrict__ sel = it.sel;
-  uint16_t* __restrict__ kc = it.kc;
-  uint16_t* __restrict__ vc = it.vc;
-  uint64_t* __restrict__ keys = it.keys;
-  int32_t* __restrict__ pos = it.pos;
-  int32_t* __restrict__ ring = it.ring;
+  const int64_t row0 = it.head0 * budget;
+  uint16_t* __restrict__ kc = batch.kc + row0 * D;
+  uint16_t* __restrict__ vc = batch.vc + row0 * D;
+  uint64_t* __restrict__ keys = batch.keys + row0;
+  int32_t* __restrict__ pos = batch.pos + row0;
+  int32_t* __restrict__ ring = batch.ring + it.head0 * W;
 
   const uint4* ksrc = reinterpret_cast<const uint4*>(k + static_cast<int64_t>(g) * sh.P * D);
   const uint4* vsrc = reinterpret_cast<const uint4*>(v + static_cast<int64_t>(g) * sh.P * D);
@@ -596,71 +624,79 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
 
 namespace {
 
-SelectArgs select_args(const Geometry& geo, const PrefillItem& it, int32_t* sel,
-                       const PrefillWork& pw) {
-  SelectArgs sa;
-  sa.scores = it.scores;
-  sa.sh = prefill_shape(it.n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
-  sa.k = geo.n_scored;
-  sa.sel = sel;
-  sa.ctl = it.lv.ctl + static_cast<int64_t>(it.seq) * geo.n_kv_heads;
-  sa.slice_keys = pw.slice_keys;
-  sa.slice_nan = pw.slice_nan;
-  sa.n_slices = 1;
-  sa.slice_len = 0;
-  return sa;
+SelectItem select_item(const PrefillItem& it, int32_t* sel, const PrefillWork& pw) {
+  SelectItem si;
+  si.scores = it.scores;
+  si.sel = sel;
+  si.slice_keys = pw.slice_keys;
+  si.slice_nan = pw.slice_nan;
+  si.head0 = it.head0;
+  si.P = it.n_tokens;
+  si.n_slices = 1;
+  si.slice_len = 0;
+  return si;
 }
 
-GatherItem gather_item(const Geometry& geo, const PrefillItem& it, const int32_t* sel) {
-  const int64_t head0 = static_cast<int64_t>(it.seq) * geo.n_kv_heads;
-  const int64_t row0 = head0 * geo.budget;
-  const int64_t el0 = row0 * geo.head_dim;
+GatherItem gather_item(const PrefillItem& it, const int32_t* sel) {
   GatherItem g;
   g.k = it.k;
   g.v = it.v;
   g.scores = it.scores;
-  g.sh = prefill_shape(it.n_tokens, geo.n_sink, geo.n_scored, geo.n_recent);
   g.sel = sel;
-  g.kc = it.lv.kc + el0;
-  g.vc = it.lv.vc + el0;
-  g.keys = it.lv.keys + row0;
-  g.pos = it.lv.pos + row0;
-  g.ring = it.lv.ring + head0 * geo.n_recent;
+  g.head0 = it.head0;
+  g.P = it.n_tokens;
   return g;
+}
+
+template <int NB>
+void fill_shared(SelectBatch<NB>& sb, GatherBatch<NB>& gb, const Geometry& geo,
+                 const LayerView& all) {
+  sb.ctl = all.ctl;
+  sb.s = gb.s = geo.n_sink;
+  sb.k = gb.k = geo.n_scored;
+  sb.W = gb.W = geo.n_recent;
+  gb.kc = all.kc;
+  gb.vc = all.vc;
+  gb.keys = all.keys;
+  gb.pos = all.pos;
+  gb.ring = all.ring;
+  gb.budget = geo.budget;
 }
 
 constexpr int32_t GATHER_ROWS = 64;  // rows per gather workgroup
 
 // Gather of m prompts whose selections are complete.
 template <int NB>
-hipError_t launch_gather(const Geometry& geo, const GatherBatch<NB>& gb, int32_t m,
-                         hipStream_t stream) {
+hipError_t launch_gather(const Geometry& geo, GatherBatch<NB>& gb, int32_t m, hipStream_t stream) {
   int32_t maxc = 0;
-  for (int32_t i = 0; i < m; ++i) maxc = gb.item[i].sh.count > maxc ? gb.item[i].sh.count : maxc;
+  for (int32_t i = 0; i < m; ++i) {
+    const int32_t c = prefill_shape(gb.item[i].P, geo.n_sink, geo.n_scored, geo.n_recent).count;
+    maxc = c > maxc ? c : maxc;
+  }
   if (maxc == 0) return hipSuccess;
-  const int32_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
+  gb.rows_per_block = GATHER_ROWS;
   const dim3 grid(static_cast<uint32_t>((maxc + GATHER_ROWS - 1) / GATHER_ROWS),
                   static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(m));
   if (geo.head_dim == 128)
-    hipLaunchKernelGGL((prefill_gather_kernel<128, NB>), grid, dim3(GATHER_THREADS), 0, stream, gb,
-                       kcap, geo.budget, geo.n_recent, GATHER_ROWS);
+    hipLaunchKernelGGL((prefill_gather_kernel<128, NB>), grid, dim3(GATHER_THREADS), 0, stream, gb);
   else
-    hipLaunchKernelGGL((prefill_gather_kernel<64, NB>), grid, dim3(GATHER_THREADS), 0, stream, gb,
-                       kcap, geo.budget, geo.n_recent, GATHER_ROWS);
+    hipLaunchKernelGGL((prefill_gather_kernel<64, NB>), grid, dim3(GATHER_THREADS), 0, stream, gb);
   return hipGetLastError();
 }
 
 // Prompts whose candidates fit VPT per thread, up to NB per launch pair.
 template <int VPT, int NB>
-hipError_t launch_head_batch(const Geometry& geo, const PrefillItem* const* its, int32_t m,
-                             const PrefillWork& pw, hipStream_t stream) {
+hipError_t launch_head_batch(const Geometry& geo, const LayerView& all,
+                             const PrefillItem* const* its, int32_t m, const PrefillWork& pw,
+                             hipStream_t stream) {
   const int64_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
   SelectBatch<NB> sb;
   GatherBatch<NB> gb;
+  fill_shared(sb, gb, geo, all);
   for (int32_t i = 0; i < m; ++i) {
     int32_t* sel = pw.sel + i * static_cast<int64_t>(geo.n_kv_heads) * kcap;
-    sb.item[i] = select_args(geo, *its[i], sel, pw);
-    gb.item[i] = gather_item(geo, *its[i], sel);
+    sb.item[i] = select_item(*its[i], sel, pw);
+    gb.item[i] = gather_item(*its[i], sel);
   }
   const dim3 grid(static_cast<uint32_t>(geo.n_kv_heads), 1u, static_cast<uint32_t>(m));
   hipLaunchKernelGGL((prefill_select_kernel<VPT, SEL_HEAD, NB>), grid, dim3(SEL_THREADS), 0,
@@ -671,10 +707,11 @@ hipError_t launch_head_batch(const Geometry& geo, const PrefillItem* const* its,
 }
 
 template <int VPT>
-hipError_t launch_head_class(const Geometry& geo, const PrefillItem* const* its, int32_t m,
-                             const PrefillWork& pw, hipStream_t stream) {
-  if (m == 1) return launch_head_batch<VPT, 1>(geo, its, 1, pw, stream);
-  return launch_head_batch<VPT, PREFILL_NB>(geo, its, m, pw, stream);
+hipError_t launch_head_class(const Geometry& geo, const LayerView& all,
+                             const PrefillItem* const* its, int32_t m, const PrefillWork& pw,
+                             hipStream_t stream) {
+  if (m == 1) return launch_head_batch<VPT, 1>(geo, all, its, 1, pw, stream);
+  return launch_head_batch<VPT, PREFILL_NB>(geo, all, its, m, pw, stream);
 }
 
 // How a prompt longer than 32 candidates per thread selects: two levels
@@ -696,26 +733,29 @@ LongPlan long_plan(const Geometry& geo, const PrefillShape& sh) {
 }
 
 // Two-level selects of m prompts with the same slice length, then their
-// gather; each prompt uses selection and slice slot i of the workspace.
+// gather; each prompt uses selection and first-level slot i of the workspace.
 template <int VPT, int NB>
-hipError_t launch_two_level(const Geometry& geo, const PrefillItem* const* its, int32_t m,
-                            const PrefillWork& pw, hipStream_t stream) {
+hipError_t launch_two_level(const Geometry& geo, const LayerView& all,
+                            const PrefillItem* const* its, int32_t m, const PrefillWork& pw,
+                            hipStream_t stream) {
   const int64_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
   const int64_t slice_one = static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX * kcap;
   SelectBatch<NB> sb;
   GatherBatch<NB> gb;
+  fill_shared(sb, gb, geo, all);
   int32_t max_slices = 1;
   for (int32_t i = 0; i < m; ++i) {
     int32_t* sel = pw.sel + i * static_cast<int64_t>(geo.n_kv_heads) * kcap;
-    SelectArgs& sa = sb.item[i];
-    sa = select_args(geo, *its[i], sel, pw);
-    const LongPlan lp = long_plan(geo, sa.sh);
-    sa.n_slices = lp.n_slices;
-    sa.slice_len = lp.slice_len;
-    sa.slice_keys = pw.slice_keys + i * slice_one;
-    sa.slice_nan = pw.slice_nan + i * static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX;
+    SelectItem& si = sb.item[i];
+    si = select_item(*its[i], sel, pw);
+    const LongPlan lp =
+        long_plan(geo, prefill_shape(its[i]->n_tokens, geo.n_sink, geo.n_scored, geo.n_recent));
+    si.n_slices = lp.n_slices;
+    si.slice_len = lp.slice_len;
+    si.slice_keys = pw.slice_keys + i * slice_one;
+    si.slice_nan = pw.slice_nan + i * static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX;
     max_slices = lp.n_slices > max_slices ? lp.n_slices : max_slices;
-    gb.item[i] = gather_item(geo, *its[i], sel);
+    gb.item[i] = gather_item(*its[i], sel);
   }
   const dim3 slices(static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(max_slices),
                     static_cast<uint32_t>(m));
@@ -732,24 +772,26 @@ hipError_t launch_two_level(const Geometry& geo, const PrefillItem* const* its, 
 }
 
 template <int VPT>
-hipError_t launch_two_level_class(const Geometry& geo, const PrefillItem* const* its, int32_t m,
+hipError_t launch_two_level_class(const Geometry& geo, const LayerView& all,
+                                  const PrefillItem* const* its, int32_t m,
                                   const PrefillWork& pw, hipStream_t stream) {
-  if (m == 1) return launch_two_level<VPT, 1>(geo, its, 1, pw, stream);
-  return launch_two_level<VPT, PREFILL_NB>(geo, its, m, pw, stream);
+  if (m == 1) return launch_two_level<VPT, 1>(geo, all, its, 1, pw, stream);
+  return launch_two_level<VPT, PREFILL_NB>(geo, all, its, m, pw, stream);
 }
 
 // A prompt for which even two levels do not fit: the streaming select, alone.
-hipError_t launch_streaming(const Geometry& geo, const PrefillItem& it, const PrefillWork& pw,
-                            hipStream_t stream) {
+hipError_t launch_streaming(const Geometry& geo, const LayerView& all, const PrefillItem& it,
+                            const PrefillWork& pw, hipStream_t stream) {
   SelectBatch<1> sb;
-  sb.item[0] = select_args(geo, it, pw.sel, pw);
+  GatherBatch<1> gb;
+  fill_shared(sb, gb, geo, all);
+  sb.item[0] = select_item(it, pw.sel, pw);
+  gb.item[0] = gather_item(it, pw.sel);
   const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads));
   hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD, 1>), heads, dim3(SEL_THREADS), 0, stream,
                      sb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  GatherBatch<1> gb;
-  gb.item[0] = gather_item(geo, it, pw.sel);
   return launch_gather<1>(geo, gb, 1, stream);
 }
 
@@ -759,8 +801,9 @@ hipError_t launch_streaming(const Geometry& geo, const PrefillItem& it, const Pr
 // thread; two levels with 16k or 32k slices; streaming) and each group runs
 // in launches of up to `chunk` prompts.  Launches share the workspace, which
 // is safe because they are ordered on the stream.
-hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, int32_t n,
-                                const PrefillWork& pw, hipStream_t stream) {
+hipError_t launch_prefill_batch(const Geometry& geo, const LayerView& all,
+                                const PrefillItem* items, int32_t n, const PrefillWork& pw,
+                                hipStream_t stream) {
   int32_t chunk = pw.sel_items < PREFILL_NB ? pw.sel_items : PREFILL_NB;
   const int32_t chunk_long = pw.slice_items < chunk ? pw.slice_items : chunk;
   if (chunk < 1 || chunk_long < 1) return hipErrorInvalidValue;
@@ -772,10 +815,10 @@ hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, i
     cnt[c] = 0;
     if (m == 0) return hipSuccess;
     switch (c) {
-      case C16: return launch_head_class<16>(geo, grp[c], m, pw, stream);
-      case C32: return launch_head_class<32>(geo, grp[c], m, pw, stream);
-      case L16: return launch_two_level_class<16>(geo, grp[c], m, pw, stream);
-      default: return launch_two_level_class<32>(geo, grp[c], m, pw, stream);
+      case C16: return launch_head_class<16>(geo, all, grp[c], m, pw, stream);
+      case C32: return launch_head_class<32>(geo, all, grp[c], m, pw, stream);
+      case L16: return launch_two_level_class<16>(geo, all, grp[c], m, pw, stream);
+      default: return launch_two_level_class<32>(geo, all, grp[c], m, pw, stream);
     }
   };
   for (int32_t i = 0; i < n; ++i) {
@@ -791,7 +834,7 @@ hipError_t launch_prefill_batch(const Geometry& geo, const PrefillItem* items, i
     } else {
       const LongPlan lp = long_plan(geo, sh);
       if (lp.vpt == 0) {
-        hipError_t e = launch_streaming(geo, it, pw, stream);
+        hipError_t e = launch_streaming(geo, all, it, pw, stream);
         if (e != hipSuccess) return e;
         continue;
       }

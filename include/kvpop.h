@@ -151,7 +151,7 @@ KVPOP_API int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t s
 /* Prefill compaction of several prompts at once: items[i] fills the empty
  * (layer, seq) it names exactly as kvpop_prefill_compact would (same
  * layouts for k, v and scores; n_tokens == 0 leaves it empty).  The prompts
- * share kernel launches (up to 32 per launch; prompts longer than 32,768
+ * share kernel launches (up to 64 per launch; prompts longer than 32,768
  * candidates per head run one at a time), which is how a serving batch, or
  * every layer of one prompt, is compacted without one launch pair per
  * prompt.  Stream-ordered and asynchronous; `items` is read during the call

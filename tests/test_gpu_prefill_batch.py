@@ -6,8 +6,8 @@ cache filled one prompt at a time; the following decode steps must then
 produce identical outputs.  Batches mix every prompt class (inside the
 sinks or the window, up to 16 and 32 candidates per thread, long prompts on
 the two-level path with different slice counts, the streaming path, empty
-prompts), span layers, exceed one launch's 32 prompts, and run with
-selection and first-level buffers smaller than 32 prompts.
+prompts), span layers, exceed one launch's 64 prompts, and run with
+selection and first-level buffers smaller than the batch.
 """
 import numpy as np
 import pytest
@@ -87,8 +87,8 @@ def test_every_prompt_class_in_one_batch():
 def test_more_prompts_than_one_launch_holds():
     geo = Geo(4, 1, 64, 4, 120, 16)
     rng = np.random.default_rng(5)
-    prompts = {(l, b): int(rng.integers(0, 3000)) for l in range(3) for b in range(15)}
-    _run(geo, 3, 15, prompts, 3, seed=11, kind="ties")
+    prompts = {(l, b): int(rng.integers(0, 3000)) for l in range(5) for b in range(15)}
+    _run(geo, 5, 15, prompts, 3, seed=11, kind="ties")
 
 
 def test_small_selection_buffer():
@@ -130,10 +130,10 @@ def test_long_prompts_two_level_batched():
 
 
 def test_long_prompts_small_slice_buffer_and_streaming():
-    """Two-level prompts beyond what the first-level buffer holds at once (7),
-    and, in another cache, a prompt only the streaming select can take."""
+    """Two-level prompts beyond what the first-level buffer holds at once
+    (16), and, in another cache, a prompt only the streaming select can take."""
     geo = Geo(8, 8, 64, 4, 8000, 16)
-    prompts = {(0, b): 40000 + 2500 * b for b in range(9)}
-    _run(geo, 1, 9, prompts, 2, seed=29, check_oracle=False)
+    prompts = {(0, b): 40000 + 1250 * b for b in range(18)}
+    _run(geo, 1, 18, prompts, 2, seed=29, check_oracle=False)
     geo = Geo(4, 1, 64, 4, 9000, 16)
     _run(geo, 1, 3, {(0, 0): 70000, (0, 1): 20000, (0, 2): 41000}, 2, seed=31)

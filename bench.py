@@ -327,19 +327,33 @@ def layered_config(w, steps: int, reps: int):
         cb = abi.KVpopCache(abi.make_config(L, 1, Hq, Hkv, D, w.n_sink, w.n_scored, w.n_recent,
                                             max_positions=P + 1))
         items = [(layer, 0, ks[layer], vs[layer], scs[layer]) for layer in range(L)]
+
+        def reset_all():
+            for layer in range(L):
+                cb.reset(layer, 0)
+
         with torch.cuda.stream(stream):
             cb.prefill_compact_batch(items)  # warm-up
+            reset_all()
         torch.cuda.synchronize()
-        for layer in range(L):
-            cb.reset(0 + layer, 0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
+        # captured, so that the host-side marshalling of the items is not timed
+        g_reset, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pre, stream=stream):
             cb.prefill_compact_batch(items)
-            e1.record(stream)
+        with torch.cuda.graph(g_reset, stream=stream):
+            reset_all()
         torch.cuda.synchronize()
-        pre_batch_ms = e0.elapsed_time(e1)
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                g_reset.replay()
+                e0.record(stream)
+                g_pre.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                pre_batch_ms += e0.elapsed_time(e1) / reps
+        del g_reset, g_pre
         st_a, st_b = cache.state(L - 1, 0), cb.state(L - 1, 0)
         assert all(a.tolist() == b.tolist() for a, b in zip(st_a.kept, st_b.kept)), \
             "batched prefill differs"

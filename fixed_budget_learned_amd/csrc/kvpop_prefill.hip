@@ -64,7 +64,11 @@ __host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int3
   return r;
 }
 
-constexpr int NBINS = 4096;  // radix digits of 12, 12 and 8 bits over the 32-bit code
+// Radix digits over the 32-bit code: 12, 12 and 8 bits (4096-bin histogram),
+// or 11, 11 and 10 bits (2048 bins) where the smaller histogram lets two
+// workgroups share a compute unit's LDS (16 codes per thread, not the list
+// mode).
+constexpr int NBINS = 4096;
 constexpr int TILE_LG = 5;   // streamed compaction: tiles of 32 candidates per thread
 
 // Coalesced load of candidates [0, n) at `sc` into LDS as order codes, laid
@@ -222,7 +226,10 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch
   constexpr int NWAVE = SEL_THREADS / WAVE;
   constexpr int LMAX = VPT > 0 ? VPT : (1 << TILE_LG);
   constexpr int STAGE_WORDS = (MODE == SEL_LIST ? 2 : 1) * SEL_THREADS * (LMAX + 1);
-  __shared__ uint32_t hist[NBINS];
+  constexpr bool NARROW = (VPT == 16 && MODE != SEL_LIST);
+  constexpr int HBINS = NARROW ? NBINS / 2 : NBINS;
+  constexpr int SH0 = NARROW ? 21 : 20, SH1 = NARROW ? 10 : 8, LAST = NARROW ? 1024 : 256;
+  __shared__ uint32_t hist[HBINS];
   __shared__ __align__(16) uint32_t stage[STAGE_WORDS];
   __shared__ uint32_t scan_buf[NWAVE + 1];
   __shared__ uint32_t s_bin, s_above, s_nan, s_neq;
@@ -354,10 +361,10 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch
       });
       if constexpr (MODE != SEL_SLICE) publish_min(mk, mpos);
     } else {
-      // ---- radix select of the kk-th largest code: 12, 12, 8 bits --------
+      // ---- radix select of the kk-th largest code: three digits --------
       uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
       auto visit = [&](auto&& f) { for_each([&](int32_t, int32_t, uint32_t o) { f(o); }); };
-      const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
+      const int shifts[3] = {SH0, SH1, 0}, nbins[3] = {HBINS, HBINS, LAST};
 #pragma unroll
       for (int ps = 0; ps < 3; ++ps) {
         radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(SEL_THREADS) void prefill_select_kernel(SelectBatch
       publish_min(mk, mpos);
     } else {
       uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
-      const int shifts[3] = {20, 8, 0}, nbins[3] = {NBINS, NBINS, 256};
+      const int shifts[3] = {SH0, SH1, 0}, nbins[3] = {HBINS, HBINS, LAST};
 #pragma unroll
       for (int ps = 0; ps < 3; ++ps) {
         auto visit = [&](auto&& f) { stream_codes<16>(sc, C, ps == 0, &nan, f); };

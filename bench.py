@@ -8,9 +8,11 @@ eviction + GQA decode attention).  Inputs are resident in HBM before timing.
 Each phase is captured once in a HIP graph and replayed.
 
 Prints ONE JSON line.  value = decode steps per second of whole-pass time
-(prefill included).  The roofline object covers the decode kernel:
-algorithmic bytes per launch / average decode launch time (HIP events on the
-replay stream).  cpu_baseline times the CPU oracle on a bounded sample.
+(prefill included).  The roofline object covers the decode step (at batch 1
+the attention kernel over 32 splits per KV head and the kernel that merges
+the splits and updates the cache): algorithmic bytes per step / average
+decode step time (HIP events on the replay stream).  cpu_baseline times the
+CPU oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode graph|eager]
 """
@@ -32,8 +34,8 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_kernel_qwen3_8b_layer_4x_tr
 PROFILE_PMC_B64 = os.path.join(ROOT, "profiles", "decode_kernel_batched_serving_b64_traffic.json")
 
 
-def decode_bytes_per_launch(w, n_kept: int) -> int:
-    """Algorithmic bytes of one decode launch at batch w.batch.
+def decode_bytes_per_step(w, n_kept: int) -> int:
+    """Algorithmic bytes of one decode step (one layer) at batch w.batch.
 
     Read K and V of every kept row, read q, write out, append the new K/V row.
     """
@@ -52,7 +54,7 @@ def prefill_bytes(w, P: int) -> int:
 
 
 def _load_traffic(kernel_hash: str, path: str = PROFILE_PMC):
-    """HBM traffic per decode launch from the committed counter summary, if it
+    """HBM traffic per decode step from the committed counter summary, if it
     was taken on the current kernel source."""
     try:
         with open(path) as f:
@@ -61,7 +63,7 @@ def _load_traffic(kernel_hash: str, path: str = PROFILE_PMC):
         return None
     if d.get("kernel_source_sha1") != kernel_hash:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("hbm_bytes_per_step")
 
 
 def _kernel_hash() -> str:
@@ -287,7 +289,7 @@ def dynamic_backend(steps: int, reps: int, every: int = 256):
 
 def layered_config(w, steps: int, reps: int):
     """Decode steps/s and prefill tokens/s of a batch-1 workload over all its
-    layers (each step and each prefill runs one launch per layer), with the
+    layers (each step and each prefill runs once per layer), with the
     fraction of the HBM roofline.  Seeded device-side N(0,1) K/V/q; scores
     drawn as the workload states.  Prefill inputs are generated one layer at
     a time (the 131k workload needs 19 GB of them in all).
@@ -392,7 +394,7 @@ def layered_config(w, steps: int, reps: int):
     # decode bytes per step: every layer reads its kept rows; a cache started
     # empty holds at least P + steps rows during the timed replays
     kept = min(w.budget, P + steps + 1)
-    dbytes = L * decode_bytes_per_launch(w, kept)
+    dbytes = L * decode_bytes_per_step(w, kept)
     res = {"workload": w.name, "layers": L, "batch": 1, "budget": w.budget, "prompt_len": P,
            "decode_us_per_step": us, "decode_steps_per_s": 1e6 / us,
            "decode_GBps": dbytes / (us * 1e-6) / 1e9,
@@ -411,9 +413,9 @@ def layered_config(w, steps: int, reps: int):
 
 
 def decode_cold(w, steps: int):
-    """Decode launch time of the one-layer workload when its cache is not
+    """Decode step time of the one-layer workload when its cache is not
     resident in any cache level: a 1 GiB buffer is written between steps
-    (more than the 256 MB last-level cache), then one decode launch is timed
+    (more than the 256 MB last-level cache), then one decode step is timed
     alone with events around it."""
     import torch
     from fixed_budget_learned_amd import abi
@@ -445,10 +447,10 @@ def decode_cold(w, steps: int):
     cache.close()
     ms.sort()
     us = ms[len(ms) // 2] * 1e3
-    bpl = decode_bytes_per_launch(w, w.budget)
-    return {"decode_us_per_launch_median": us, "GBps": bpl / (us * 1e-6) / 1e9,
-            "frac": bpl / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "launches": steps,
-            "note": "1 GiB written between steps; events around each single launch "
+    bpl = decode_bytes_per_step(w, w.budget)
+    return {"decode_us_per_step_median": us, "GBps": bpl / (us * 1e-6) / 1e9,
+            "frac": bpl / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "steps": steps,
+            "note": "1 GiB written between steps; events around each single step "
                     "(includes its launch latency)"}
 
 
@@ -609,7 +611,7 @@ def batched_serving(steps: int, reps: int, mode: str = "graph"):
     assert all(int(c) == w.budget for c in counts), "batched caches not full"
     cache.close()
     us = dec_ms * 1e3 / (reps * steps)
-    bpl = decode_bytes_per_launch(w, w.budget)
+    bpl = decode_bytes_per_step(w, w.budget)
     gbps = bpl / (us * 1e-6) / 1e9
     ptok = sum(lens)
     pbytes = sum(prefill_bytes(w, P) for P in lens)
@@ -620,9 +622,10 @@ def batched_serving(steps: int, reps: int, mode: str = "graph"):
         "decode_us_per_step": us, "decode_steps_per_s": 1e6 / us,
         "decode_tokens_per_s": B * 1e6 / us,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "bytes_per_launch": bpl,
+                     "frac": gbps / HBM_PEAK_GBPS, "bytes_per_step": bpl,
                      "traffic": _load_traffic(_kernel_hash(), PROFILE_PMC_B64),
-                     "kernel": "decode_kernel (head_dim 128, 4 query heads per KV head)"},
+                     "kernel": "decode_kernel, one workgroup per KV head (head_dim 128, "
+                               "4 query heads per KV head)"},
         "prefill_tokens_per_s": ptok / pre_s,
         "prefill_GBps": pbytes / pre_s / 1e9,
         "prefill_frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBPS,
@@ -775,17 +778,17 @@ def main():
     assert st.n == P + S - 1 and all(int(c) == w.budget for c in st.counts), "unexpected final state"
     cache.close()
 
-    launches = args.steps * S
-    dec_launch_s = dec_ms / 1e3 / launches
+    dsteps = args.steps * S
+    dec_step_s = dec_ms / 1e3 / dsteps
     n_kept = w.budget
-    bpl = decode_bytes_per_launch(w, n_kept)
-    achieved = bpl / dec_launch_s / 1e9
+    bpl = decode_bytes_per_step(w, n_kept)
+    achieved = bpl / dec_step_s / 1e9
     khash = _kernel_hash()
     traffic = _load_traffic(khash)
     pbytes = prefill_bytes(w, P)
     result = {
         "metric": METRIC,
-        "value": launches / (total_ms / 1e3),
+        "value": dsteps / (total_ms / 1e3),
         "unit": "decode steps/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -800,8 +803,8 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "budget": w.budget,
                    "n_sink": w.n_sink, "n_scored": w.n_scored, "n_recent": w.n_recent,
                    "prompt_len": P, "decode_steps_per_pass": S, "launch": args.mode},
-        "decode_only_steps_per_s": launches / (dec_ms / 1e3),
-        "decode_us_per_launch": dec_launch_s * 1e6,
+        "decode_only_steps_per_s": dsteps / (dec_ms / 1e3),
+        "decode_us_per_step": dec_step_s * 1e6,
         "prefill_us": pre_ms * 1e3 / args.steps,
         "prefill_tokens_per_s": P * args.steps / (pre_ms / 1e3),
         "prefill_GBps": pbytes * args.steps / (pre_ms / 1e3) / 1e9,
@@ -812,9 +815,10 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "traffic_unit": "bytes per launch (FETCH_SIZE and WRITE_SIZE, copy-calibrated)",
-            "kernel": "decode_kernel (head_dim 128, 4 query heads per KV head)",
-            "bytes_per_launch": bpl,
+            "traffic_unit": "bytes per step (FETCH_SIZE and WRITE_SIZE, copy-calibrated)",
+            "kernel": "decode step: decode_kernel (32 splits per KV head) and decode_finish_kernel "
+                      "(split merge and cache update); head_dim 128, 4 query heads per KV head",
+            "bytes_per_step": bpl,
             "note": "one layer's working set (16.5 MB) fits in the 256 MB last-level cache, so "
                     "back-to-back steps can be served partly from cache",
         },

@@ -19,19 +19,19 @@
 // token about to leave the window, so no dependent lookup is needed), so no
 // workgroup waits for another.  A workgroup reads K/V of its slots from the
 // cache, and substitutes the k_new/v_new row for the slot the new token
-// takes.  It writes a partial softmax state (max, sum, unnormalised
-// accumulator) and the minimum key over its slots as they will be after
-// this step.  The last workgroup of a head to finish (ticket counter,
-// device-scope release/acquire, one L2 writeback per workgroup) merges the
-// partials into the bf16 output, reduces the next minimum, and only then
-// writes the cache update (new K/V row, keys, positions, window ring,
-// control block).  Every mutation therefore happens after all workgroups of
-// the head have finished reading; no read in the launch races with a write.
+// takes.  With one split per head (batched serving) the workgroup then
+// writes the output and the cache update (new K/V row, keys, positions,
+// window ring, control block) itself.  With several, each writes a partial
+// softmax state (max, sum, unnormalised accumulator) and the minimum key
+// over its slots as they will be after this step, and a second launch with
+// one workgroup per head merges them into the bf16 output and writes the
+// cache update.  Either way every mutation happens after all reads of the
+// head's slots: within the workgroup, or across the launch boundary.
 //
 // Latency.  All loads a workgroup needs (K/V and keys of its first chunk,
 // q, the new row, the control block, the score) are issued before anything
 // waits, and chunks (K/V rows and their keys) are double-buffered in
-// registers.  The merge issues all of its partial loads at once.
+// registers.  The merge issues all of its loads at once.
 //
 // Inner loop.  LPR = D/16 lanes share one row; each lane holds two 16-byte
 // pieces (offsets 16*lane and D + 16*lane bytes), so every load instruction
@@ -70,7 +70,6 @@ struct DecodeParams {
   float* part_acc;
   float* part_ml;
   MinPart* part_min;
-  uint32_t* tickets;
   int32_t n_heads;
   int32_t budget, n_sink, n_scored, n_recent;
   int32_t nsplit, rows_per_split;
@@ -206,6 +205,222 @@ __device__ __forceinline__ float row16_sum_groups(float x) {
   return x;
 }
 
+// The step's eviction decision for one head, derived from its control block
+// and the leaving token's score; every workgroup that needs it derives the
+// same one.
+struct Decision {
+  int32_t n;            // the new token's position
+  int32_t newslot;      // slot the new token takes
+  int32_t count_new, nscored_new;
+  int32_t st;           // slot of the leaving token (-1: none leaves)
+  int32_t flags;
+  bool admitted;        // the leaving token keeps a scored slot
+  uint64_t keyt;        // its key
+};
+
+__device__ __forceinline__ Decision decide(const HeadCtl& c, float sg, int32_t n_sink,
+                                           int32_t n_scored, int32_t W) {
+  Decision d;
+  d.n = c.n + 1;
+  const int32_t t = d.n - W;
+  d.newslot = c.count;
+  d.count_new = c.count;
+  d.nscored_new = c.nscored;
+  d.st = -1;
+  d.admitted = false;
+  d.keyt = KEY_NONE;
+  d.flags = c.flags;
+  if (t < n_sink) {
+    d.count_new = c.count + 1;                   // sink, or window still filling
+  } else {
+    d.st = c.leave_slot;
+    if (score_is_nan(sg)) d.flags |= 1;
+    d.keyt = make_key(score_code(sg), t);
+    if (c.nscored < n_scored) {                  // free scored slot
+      d.admitted = true;
+      d.count_new = c.count + 1;
+      d.nscored_new = c.nscored + 1;
+    } else if (d.keyt > c.minkey) {              // replaces the least important
+      d.admitted = true;
+      d.newslot = c.minslot;
+    } else {                                     // dropped for good
+      d.newslot = d.st;
+    }
+  }
+  return d;
+}
+
+// Merge the partial results of a head's splits into the bf16 output rows of
+// its G query heads, and the splits' key minima into s_mk/s_ms (one entry
+// per 16-lane row of the workgroup).  Called by the whole 256-thread
+// workgroup.  Every load (accumulators, maxima and sums, key minima) is
+// issued before the first wait.
+template <int D, int G>
+__device__ __forceinline__ void merge_splits(const DecodeParams& p, int head, float* s_buf,
+                                             float* s_L, uint64_t* s_mk, int32_t* s_ms) {
+  constexpr int NT = 256;
+  constexpr int NWAVE = NT / WAVE;
+  constexpr int R16 = WAVE / 16;
+  constexpr int Q4 = G * D / 4;          // float4s in one split's accumulator
+  static_assert(Q4 <= NT && NT % Q4 == 0, "merge layout");
+  constexpr int TS = NT / Q4;            // threads per float4 column
+  constexpr int MB = MAX_SPLITS / TS < 16 ? MAX_SPLITS / TS : 16;  // loads in flight per thread
+  constexpr int SPL = MAX_SPLITS / WAVE;  // splits per lane
+  static_assert(MAX_SPLITS <= NT, "one key minimum per thread");
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wid = tid / WAVE;
+  const int r16 = lane / 16;
+  const int ns = p.nsplit;
+  const int64_t p0 = static_cast<int64_t>(head) * ns;
+  float* s_pf = s_buf;                     // [ns][G] rescale factor
+  float* s_red = s_buf + MAX_SPLITS * G;   // [TS][G*D] per-thread-group sums
+  const int j4 = tid % Q4;
+  const int s0 = tid / Q4;
+  const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc) + j4;
+  float4 raw[MB];
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int sp = s0 + u * TS;
+    raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  MinPart mp;
+  mp.key = KEY_NONE;
+  mp.slot = 0x7FFFFFFF;
+  if (tid < ns) mp = p.part_min[p0 + tid];
+  const float2* pml2 = reinterpret_cast<const float2*>(p.part_ml);
+  for (int h = wid; h < G; h += NWAVE) {
+    float2 ml[SPL];
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int sp = lane + u * WAVE;
+      ml[u] = (sp < ns) ? pml2[(p0 + sp) * G + h] : make_float2(-INFINITY, 0.f);
+    }
+    float M = ml[0].x;
+#pragma unroll
+    for (int u = 1; u < SPL; ++u) M = fmaxf(M, ml[u].x);
+    M = wave_max(M);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int sp = lane + u * WAVE;
+      const float f = fast_exp2(ml[u].x - Ms);
+      if (sp < ns) s_pf[sp * G + h] = f;
+      L = fmaf(ml[u].y, f, L);
+    }
+    L = wave_sum(L);
+    if (lane == 0) s_L[h] = L;
+  }
+  {
+    uint64_t k0 = mp.key;
+    int32_t sl0 = mp.slot;
+    row16_min_key(k0, sl0);
+    if (lane % 16 == 0) {
+      s_mk[wid * R16 + r16] = k0;
+      s_ms[wid * R16 + r16] = sl0;
+    }
+  }
+  __syncthreads();
+  const int hq = (j4 * 4) / D;
+  float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int sp = s0 + u * TS;
+    const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
+    a4.x = fmaf(raw[u].x, f, a4.x);
+    a4.y = fmaf(raw[u].y, f, a4.y);
+    a4.z = fmaf(raw[u].z, f, a4.z);
+    a4.w = fmaf(raw[u].w, f, a4.w);
+  }
+  for (int sb = s0 + MB * TS; sb < ns; sb += MB * TS) {  // more than MB*TS splits
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int sp = sb + u * TS;
+      raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int sp = sb + u * TS;
+      const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
+      a4.x = fmaf(raw[u].x, f, a4.x);
+      a4.y = fmaf(raw[u].y, f, a4.y);
+      a4.z = fmaf(raw[u].z, f, a4.z);
+      a4.w = fmaf(raw[u].w, f, a4.w);
+    }
+  }
+  if (TS > 1) reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
+  if (TS > 1) __syncthreads();
+  if (s0 == 0) {
+    float4 o = a4;
+    for (int ts = 1; ts < TS; ++ts) {
+      const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
+      o.x += y.x;
+      o.y += y.y;
+      o.z += y.z;
+      o.w += y.w;
+    }
+    const float invL = 1.f / s_L[hq];
+    const uint32_t b0 = f32_to_bf16_rne(o.x * invL), b1 = f32_to_bf16_rne(o.y * invL);
+    const uint32_t b2 = f32_to_bf16_rne(o.z * invL), b3 = f32_to_bf16_rne(o.w * invL);
+    reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + j4] =
+        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+  }
+}
+
+// Write the step's cache update for one head: the new K/V row, slot keys
+// and position, the window ring and the control block (whose least
+// important key is the minimum of the s_mk/s_ms entries).
+template <int D, int G>
+__device__ __forceinline__ void update_cache(const DecodeParams& p, int head, const Decision& dc,
+                                             const uint4 (&knew)[2], const uint4 (&vnew)[2],
+                                             int32_t ring_next, const uint64_t* s_mk,
+                                             const int32_t* s_ms) {
+  constexpr int NWAVE = 256 / WAVE;
+  constexpr int R16 = WAVE / 16;
+  constexpr int LPR = D / 16;
+  constexpr int HALF4 = D / 16;
+  constexpr int ROW4 = D / 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int64_t hrow = static_cast<int64_t>(head) * p.budget;
+  const int32_t W = p.n_recent;
+  if (tid < LPR) {  // lane tid holds chunks tid and tid + D/16 of the new row
+    uint4* kw = reinterpret_cast<uint4*>(p.kc) + (hrow + dc.newslot) * ROW4 + tid;
+    uint4* vw = reinterpret_cast<uint4*>(p.vc) + (hrow + dc.newslot) * ROW4 + tid;
+    kw[0] = knew[0];
+    kw[HALF4] = knew[1];
+    vw[0] = vnew[0];
+    vw[HALF4] = vnew[1];
+  }
+  if (tid < WAVE) {
+    uint64_t k0 = KEY_NONE;
+    int32_t sl0 = 0x7FFFFFFF;
+    if (lane < NWAVE * R16) {
+      k0 = s_mk[lane];
+      sl0 = s_ms[lane];
+    }
+    wave_min_key_dpp(k0, sl0);
+    if (lane == 0) {
+      const int32_t n = dc.n;
+      if (dc.admitted) p.keys[hrow + dc.st] = dc.keyt;
+      p.keys[hrow + dc.newslot] = KEY_NONE;
+      p.pos[hrow + dc.newslot] = n;
+      if (n >= p.n_sink) p.ring[static_cast<int64_t>(head) * W + (n % W)] = dc.newslot;
+      HeadCtl nc;
+      nc.n = n;
+      nc.count = dc.count_new;
+      nc.nscored = dc.nscored_new;
+      nc.minslot = (k0 == KEY_NONE) ? -1 : sl0;
+      nc.minkey = k0;
+      nc.flags = dc.flags;
+      // with a one-token window the next leaving token is the one just added
+      nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? dc.newslot : ring_next);
+      p.ctl[head] = nc;
+    }
+  }
+}
+
 // One workgroup of 256 threads per (KV head, split).  K/V rows stream
 // through registers in chunks of 2 rows per thread, double-buffered: the
 // loads of the next chunk are in flight while the current one is computed.
@@ -222,31 +437,27 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int R16 = WAVE / 16;         // 16-lane DPP rows per wavefront
   constexpr int ACC = 16;                // accumulators per head per lane
   constexpr int Q4 = G * D / 4;          // float4s in one split's accumulator
-  static_assert(Q4 <= NT, "merge needs one thread per float4");
-  constexpr int TS = NT / Q4;            // merge threads per float4 column
-  constexpr int MB = 16;                 // merge loads in flight per thread
+  static_assert(Q4 <= NT, "one thread per float4 of the accumulator");
   // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators, each
   // block padded by 8 floats so that neighbouring lanes' blocks start in
-  // different LDS banks; the finishing workgroup reuses it for the split merge
+  // different LDS banks
   constexpr int ACC_STRIDE = G * ACC + 8;
   constexpr int LDS_ROWS = NWAVE * R16 * LPR * ACC_STRIDE;
-  constexpr int LDS_MERGE = MAX_SPLITS * G + TS * G * D;
   static_assert(NWAVE * R16 <= WAVE, "key minima of the workgroup fit one wavefront");
-  constexpr int LDS_F = LDS_ROWS > LDS_MERGE ? LDS_ROWS : LDS_MERGE;
 
-  __shared__ __align__(16) float s_buf[LDS_F];
+  __shared__ __align__(16) float s_buf[LDS_ROWS];
   __shared__ float s_wm[NWAVE][G];       // wave max (log2 units)
   __shared__ float s_wl[NWAVE][R16][G];  // per DPP-row sums of p
-  __shared__ float s_L[G];
   __shared__ uint64_t s_mk[NWAVE * R16];
   __shared__ int32_t s_ms[NWAVE * R16];
-  __shared__ int32_t s_last;
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wid = tid / WAVE;
 
   // ---- workgroup -> (head, split); all splits of a head on one XCD when
-  // the head count allows (workgroups are dealt to the 8 XCDs round robin).
+  // the head count allows (workgroups are dealt to the 8 XCDs round robin),
+  // so the head's control block, queries and new row, which every split
+  // reads, come from one L2.
   int head, split;
   {
     const int bid = blockIdx.x;
@@ -307,31 +518,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 
   // ---- eviction decision, identical in every workgroup of the head -------
-  const int32_t n = c.n + 1;
-  const int32_t t = n - W;
-  int32_t newslot = c.count, count_new = c.count, nscored_new = c.nscored, st = -1;
-  bool admitted = false;
-  uint64_t keyt = KEY_NONE;
-  int32_t flags = c.flags;
-  if (t < p.n_sink) {
-    count_new = c.count + 1;                     // sink, or window still filling
-  } else {
-    st = c.leave_slot;
-    if (score_is_nan(sg)) flags |= 1;
-    keyt = make_key(score_code(sg), t);
-    if (c.nscored < p.n_scored) {                // free scored slot
-      admitted = true;
-      count_new = c.count + 1;
-      nscored_new = c.nscored + 1;
-    } else if (keyt > c.minkey) {                // replaces the least important
-      admitted = true;
-      newslot = c.minslot;
-    } else {                                     // dropped for good
-      newslot = st;
-    }
-  }
-  // slot of the next token to leave (needed by the finishing workgroup)
-  const int32_t ring_next = p.ring[static_cast<int64_t>(head) * W + ((n + 1) % W)];
+  const Decision dc = decide(c, sg, p.n_sink, p.n_scored, W);
+  const int32_t newslot = dc.newslot, count_new = dc.count_new, st = dc.st;
+  const bool admitted = dc.admitted;
+  const uint64_t keyt = dc.keyt;
+  // slot of the next token to leave (needed by the cache update)
+  const int32_t ring_next = p.ring[static_cast<int64_t>(head) * W + ((dc.n + 1) % W)];
 
   // ---- attention over slots [lo, hi) --------------------------------------
   const int32_t hi = min(lo + p.rows_per_split, count_new);
@@ -524,8 +716,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
     }
   }
-  // Several splits: publish the partial results; the last workgroup of the
-  // head to finish merges them.  A single split is complete already.
+  // Several splits: publish the partial results and the key minimum; the
+  // second launch (decode_finish_kernel) merges them.  A single split is
+  // complete already.
   if (!single) {
     if (wid == 0) {
       uint64_t k0 = KEY_NONE;
@@ -539,172 +732,57 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         MinPart mp;
         mp.key = k0;
         mp.slot = sl0;
-        mp.pad = 0;
+        mp.pad = ring_next;  // read by the finishing launch
         p.part_min[pidx] = mp;
       }
     }
-
-    // ---- ticket: the last workgroup of the head finishes the step ----------
-    // Every thread's stores complete, then one device-scope release (an L2
-    // writeback) covers the whole workgroup before the ticket is taken.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const uint32_t prev =
-          __hip_atomic_fetch_add(&p.tickets[head], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    // ---- merge the splits ----------------------------------------------------
-    // Wave h (and h + NWAVE, ...) reduces head h's split maxima and sums with
-    // one split per lane; the accumulator loads are issued first so that their
-    // latency overlaps the reductions.
-    const int ns = p.nsplit;
-    const int64_t p0 = static_cast<int64_t>(head) * ns;
-    float* s_pf = s_buf;                     // [ns][G] rescale factor
-    float* s_red = s_buf + MAX_SPLITS * G;   // [TS][G*D] per-thread-group sums
-    const int j4 = tid % Q4;
-    const int s0 = tid / Q4;
-    const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc);
-    float4 raw[MB];
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-      const int sp = s0 + u * TS;
-      raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const float2* pml2 = reinterpret_cast<const float2*>(p.part_ml);
-    for (int h = wid; h < G; h += NWAVE) {
-      constexpr int SPL = MAX_SPLITS / WAVE;  // splits per lane
-      float2 ml[SPL];
-#pragma unroll
-      for (int u = 0; u < SPL; ++u) {
-        const int sp = lane + u * WAVE;
-        ml[u] = (sp < ns) ? pml2[(p0 + sp) * G + h] : make_float2(-INFINITY, 0.f);
-      }
-      float M = ml[0].x;
-#pragma unroll
-      for (int u = 1; u < SPL; ++u) M = fmaxf(M, ml[u].x);
-      M = wave_max(M);
-      const float Ms = (M == -INFINITY) ? 0.f : M;
-      float L = 0.f;
-#pragma unroll
-      for (int u = 0; u < SPL; ++u) {
-        const int sp = lane + u * WAVE;
-        const float f = fast_exp2(ml[u].x - Ms);
-        if (sp < ns) s_pf[sp * G + h] = f;
-        L = fmaf(ml[u].y, f, L);
-      }
-      L = wave_sum(L);
-      if (lane == 0) s_L[h] = L;
-    }
-    {
-      uint64_t k0 = KEY_NONE;
-      int32_t sl0 = 0x7FFFFFFF;
-      for (int sp = tid; sp < ns; sp += NT) {
-        const MinPart mp = p.part_min[p0 + sp];
-        if (key_less(mp.key, mp.slot, k0, sl0)) {
-          k0 = mp.key;
-          sl0 = mp.slot;
-        }
-      }
-      row16_min_key(k0, sl0);
-      if (lane % 16 == 0) {
-        s_mk[wid * R16 + r16] = k0;
-        s_ms[wid * R16 + r16] = sl0;
-      }
-    }
-    __syncthreads();
-    const int hq = (j4 * 4) / D;
-    float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-      const int sp = s0 + u * TS;
-      const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
-      a4.x = fmaf(raw[u].x, f, a4.x);
-      a4.y = fmaf(raw[u].y, f, a4.y);
-      a4.z = fmaf(raw[u].z, f, a4.z);
-      a4.w = fmaf(raw[u].w, f, a4.w);
-    }
-    for (int sb = s0 + MB * TS; sb < ns; sb += MB * TS) {  // more than MB*TS splits
-#pragma unroll
-      for (int u = 0; u < MB; ++u) {
-        const int sp = sb + u * TS;
-        raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4 + j4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < MB; ++u) {
-        const int sp = sb + u * TS;
-        const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
-        a4.x = fmaf(raw[u].x, f, a4.x);
-        a4.y = fmaf(raw[u].y, f, a4.y);
-        a4.z = fmaf(raw[u].z, f, a4.z);
-        a4.w = fmaf(raw[u].w, f, a4.w);
-      }
-    }
-    if (TS > 1) reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
-    if (TS > 1) __syncthreads();
-    if (s0 == 0) {
-      float4 o = a4;
-      for (int ts = 1; ts < TS; ++ts) {
-        const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
-        o.x += y.x;
-        o.y += y.y;
-        o.z += y.z;
-        o.w += y.w;
-      }
-      const float invL = 1.f / s_L[hq];
-      const uint32_t b0 = f32_to_bf16_rne(o.x * invL), b1 = f32_to_bf16_rne(o.y * invL);
-      const uint32_t b2 = f32_to_bf16_rne(o.z * invL), b3 = f32_to_bf16_rne(o.w * invL);
-      reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + j4] =
-          make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    }
+    return;
   }
 
   // ---- cache update: new row, slot metadata, window ring, control block --
-  if (tid < LPR) {  // lane tid holds chunks tid and tid + D/16 of the new row
-    uint4* kw = reinterpret_cast<uint4*>(p.kc) + (hrow + newslot) * ROW4 + tid;
-    uint4* vw = reinterpret_cast<uint4*>(p.vc) + (hrow + newslot) * ROW4 + tid;
-    kw[0] = knew0;
-    kw[HALF4] = knew1;
-    vw[0] = vnew0;
-    vw[HALF4] = vnew1;
-  }
-  if (wid == 0) {
-    uint64_t k0 = KEY_NONE;
-    int32_t sl0 = 0x7FFFFFFF;
-    if (lane < NWAVE * R16) {
-      k0 = s_mk[lane];
-      sl0 = s_ms[lane];
-    }
-    wave_min_key_dpp(k0, sl0);
-    if (lane == 0) {
-      if (admitted) p.keys[hrow + st] = keyt;
-      p.keys[hrow + newslot] = KEY_NONE;
-      p.pos[hrow + newslot] = n;
-      if (n >= p.n_sink) p.ring[static_cast<int64_t>(head) * W + (n % W)] = newslot;
-      HeadCtl nc;
-      nc.n = n;
-      nc.count = count_new;
-      nc.nscored = nscored_new;
-      nc.minslot = (k0 == KEY_NONE) ? -1 : sl0;
-      nc.minkey = k0;
-      nc.flags = flags;
-      // with a one-token window the next leaving token is the one just added
-      nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? newslot : ring_next);
-      p.ctl[head] = nc;
-      p.tickets[head] = 0u;
-    }
-  }
+  const uint4 knew[2] = {knew0, knew1}, vnew[2] = {vnew0, vnew1};
+  update_cache<D, G>(p, head, dc, knew, vnew, ring_next, s_mk, s_ms);
+}
+
+// Second launch of a step with several splits: one workgroup per KV head
+// merges the splits' partial results into the output and writes the cache
+// update.  The launch boundary orders it after every read of the first
+// launch, so no ticket or release is needed.  All of its loads (control
+// block, score, new row, partials) are independent and issued together.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
+  constexpr int NWAVE = 256 / WAVE;
+  constexpr int R16 = WAVE / 16;
+  constexpr int LPR = D / 16;
+  constexpr int HALF4 = D / 16;
+  constexpr int ROW4 = D / 8;
+  constexpr int TS = 256 / (G * D / 4);
+  __shared__ __align__(16) float s_buf[MAX_SPLITS * G + TS * G * D];
+  __shared__ float s_L[G];
+  __shared__ uint64_t s_mk[NWAVE * R16];
+  __shared__ int32_t s_ms[NWAVE * R16];
+  const int head = blockIdx.x;
+  const int cc = threadIdx.x % LPR;
+  const HeadCtl c = p.ctl[head];
+  const float sg = p.score_leaving[head];
+  const int32_t ring_next = p.part_min[static_cast<int64_t>(head) * p.nsplit].pad;
+  const uint4* knp = reinterpret_cast<const uint4*>(p.k_new) + static_cast<int64_t>(head) * ROW4 + cc;
+  const uint4* vnp = reinterpret_cast<const uint4*>(p.v_new) + static_cast<int64_t>(head) * ROW4 + cc;
+  const uint4 knew[2] = {knp[0], knp[HALF4]};
+  const uint4 vnew[2] = {vnp[0], vnp[HALF4]};
+  merge_splits<D, G>(p, head, s_buf, s_L, s_mk, s_ms);
+  const Decision dc = decide(c, sg, p.n_sink, p.n_scored, p.n_recent);
+  update_cache<D, G>(p, head, dc, knew, vnew, ring_next, s_mk, s_ms);
 }
 
 template <int D, int G>
 hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                      stream, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || prm.nsplit == 1) return e;
+  hipLaunchKernelGGL((decode_finish_kernel<D, G>), dim3(static_cast<uint32_t>(prm.n_heads)),
+                     dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -748,7 +826,6 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
   prm.part_acc = work.part_acc;
   prm.part_ml = work.part_ml;
   prm.part_min = work.part_min;
-  prm.tickets = work.tickets;
   prm.n_heads = geo.batch * geo.n_kv_heads;
   prm.budget = geo.budget;
   prm.n_sink = geo.n_sink;

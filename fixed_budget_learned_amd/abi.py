@@ -43,7 +43,8 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_sink", ctypes.c_int32),
                 ("n_scored", ctypes.c_int32), ("n_recent", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("decode_splits", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("prune_interval", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("prune_interval", ctypes.c_int32),
+                ("decode_finish", ctypes.c_int32)]
 
 
 class PrefillItem(ctypes.Structure):
@@ -103,12 +104,15 @@ def strerror(code: int) -> str:
 
 def make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_sink, n_scored, n_recent,
                 max_positions=1 << 30, decode_splits=0, softmax_scale=0.0,
-                prune_interval=0) -> Config:
+                prune_interval=0, decode_finish=0) -> Config:
     """prune_interval 0: Static backend; P >= 1: Dynamic backend pruned after
-    every P-th decode step of a layer (see the header)."""
+    every P-th decode step of a layer.  decode_finish 0: the library chooses
+    how split heads are merged; 1: in the same launch; 2: in a second launch
+    (see the header)."""
     return Config(int(n_layers), int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim),
                   int(n_sink), int(n_scored), int(n_recent), int(max_positions),
-                  int(decode_splits), float(softmax_scale), int(prune_interval))
+                  int(decode_splits), float(softmax_scale), int(prune_interval),
+                  int(decode_finish))
 
 
 def required_bytes(cfg: Config) -> int:

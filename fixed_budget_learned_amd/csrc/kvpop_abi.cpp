@@ -21,8 +21,8 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   size_t kc, vc, keys, pos, ring, ctl, sel, slice_keys, slice_nan, part_acc, part_ml, part_min,
-      total;
-  int32_t nsplit, rows_per_split, threads, rows_per_thread;
+      tickets, total;
+  int32_t nsplit, rows_per_split, threads, rows_per_thread, finish_apart;
   int32_t sel_items;    // prompts one batched prefill launch can select at once
   int32_t slice_items;  // long prompts one batched two-level select can hold
 };
@@ -50,6 +50,7 @@ bool config_valid(const kvpop_config* c) {
   if (capacity_of(*c) > (1 << 20)) return false;
   if (c->max_positions < 1 || c->max_positions > (1 << 30)) return false;
   if (c->decode_splits < 0 || c->decode_splits > kvpop::decode_max_splits()) return false;
+  if (c->decode_finish < 0 || c->decode_finish > 2) return false;
   if (std::isnan(c->softmax_scale) || std::isinf(c->softmax_scale)) return false;
   return true;
 }
@@ -58,12 +59,17 @@ bool config_valid(const kvpop_config* c) {
 // workgroups of 256 threads, each thread holding 2 rows per pass.  With 256
 // or more heads (batched serving) each head is one workgroup: the step needs
 // no cross-workgroup merge at all.  With fewer heads the splits fill the
-// 256 compute units once (one workgroup per unit), and a second launch
-// merges them.  Every split keeps at least 128 slots: at batch 1, twice the
-// splits of half the slots (two workgroups per unit) measured slower, since
-// the workgroups start later and the merge has twice the partials.
+// 256 compute units once (one workgroup per unit).  Every split keeps at
+// least 128 slots: at batch 1, twice the splits of half the slots (two
+// workgroups per unit) measured slower, since the workgroups start later and
+// the merge has twice the partials.
+//
+// Split heads are merged in a second launch when the grid is full and every
+// split is at most 128 slots (two chunks per workgroup): then all splits of
+// a head finish together and their ticket atomics would queue.  Otherwise
+// the last split's workgroup merges in the same launch.
 void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
-                         int32_t* threads, int32_t* rows_per_thread) {
+                         int32_t* threads, int32_t* rows_per_thread, int32_t* finish_apart) {
   const int64_t budget = capacity_of(c);
   const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
   const int nt = 256, np = 2;
@@ -81,6 +87,10 @@ void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_p
   *rows_per_split = int32_t(rows);
   *threads = nt;
   *rows_per_thread = np;
+  if (c.decode_finish == 0)
+    *finish_apart = (heads * ns >= 256 && rows <= 128) ? 1 : 0;
+  else
+    *finish_apart = (c.decode_finish == 2) ? 1 : 0;
 }
 
 bool compute_layout(const kvpop_config& c, Layout* L) {
@@ -88,7 +98,8 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   const size_t heads_all = size_t(c.n_layers) * c.batch * c.n_kv_heads;
   const size_t heads = size_t(c.batch) * c.n_kv_heads;
   const size_t G = size_t(c.n_q_heads / c.n_kv_heads);
-  choose_decode_shape(c, &L->nsplit, &L->rows_per_split, &L->threads, &L->rows_per_thread);
+  choose_decode_shape(c, &L->nsplit, &L->rows_per_split, &L->threads, &L->rows_per_thread,
+                      &L->finish_apart);
   size_t rows, kvb, tmp;
   if (!mul_ok(heads_all, budget, &rows)) return false;
   if (!mul_ok(rows, size_t(c.head_dim) * 2, &kvb)) return false;
@@ -122,6 +133,7 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
   ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
   ok = ok && mul_ok(parts, sizeof(kvpop::MinPart), &tmp) && take(tmp, &L->part_min);
+  ok = ok && take(heads * 4, &L->tickets);
   L->total = off;
   return ok;
 }
@@ -197,10 +209,12 @@ struct kvpop_cache {
     w.part_acc = reinterpret_cast<float*>(base + lay.part_acc);
     w.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
     w.part_min = reinterpret_cast<kvpop::MinPart*>(base + lay.part_min);
+    w.tickets = reinterpret_cast<uint32_t*>(base + lay.tickets);
     w.nsplit = lay.nsplit;
     w.rows_per_split = lay.rows_per_split;
     w.threads = lay.threads;
     w.rows_per_thread = lay.rows_per_thread;
+    w.finish_apart = lay.finish_apart;
     return w;
   }
 };
@@ -259,8 +273,11 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
     c->owns = true;
   }
   const size_t heads_all = size_t(cfg->n_layers) * cfg->batch * cfg->n_kv_heads;
+  const size_t heads = size_t(cfg->batch) * cfg->n_kv_heads;
   hipError_t e = kvpop::launch_init_ctl(reinterpret_cast<kvpop::HeadCtl*>(c->base + L.ctl),
-                                        int64_t(heads_all), nullptr);
+                                        int64_t(heads_all),
+                                        reinterpret_cast<uint32_t*>(c->base + L.tickets),
+                                        int64_t(heads), nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) {
     if (c->owns) (void)hipFree(c->base);
@@ -290,7 +307,8 @@ int kvpop_cache_reset(kvpop_cache* cache, int32_t layer, int32_t seq, void* stre
   if (!dg.ok) return KVPOP_EHIP;
   kvpop::LayerView lv = cache->layer(layer);
   hipError_t e = kvpop::launch_init_ctl(lv.ctl + size_t(seq) * cache->cfg.n_kv_heads,
-                                        cache->cfg.n_kv_heads, static_cast<hipStream_t>(stream));
+                                        cache->cfg.n_kv_heads, nullptr, 0,
+                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;
     return KVPOP_EHIP;

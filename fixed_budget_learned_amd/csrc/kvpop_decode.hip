@@ -1,6 +1,6 @@
-// One decode step of the fixed-budget cache for gfx950, fused into a single
-// launch per layer: the delayed-eviction update and split-K GQA decode
-// attention over the bounded cache.
+// One decode step of the fixed-budget cache for gfx950: the delayed-eviction
+// update and split-K GQA decode attention over the bounded cache, fused into
+// one launch per layer (two where a second launch merges split heads).
 //
 // What a step does for each (sequence, KV head), token n = previous n + 1:
 //   * Token t = n - W leaves the protected window and only now receives its
@@ -23,10 +23,29 @@
 // writes the output and the cache update (new K/V row, keys, positions,
 // window ring, control block) itself.  With several, each writes a partial
 // softmax state (max, sum, unnormalised accumulator) and the minimum key
-// over its slots as they will be after this step, and a second launch with
-// one workgroup per head merges them into the bf16 output and writes the
-// cache update.  Either way every mutation happens after all reads of the
-// head's slots: within the workgroup, or across the launch boundary.
+// over its slots as they will be after this step, and the splits are merged
+// into the bf16 output, followed by the cache update, in one of two ways:
+//   * ticket: each workgroup takes a ticket after publishing, and the last
+//     one of the head merges;
+//   * second launch: decode_finish_kernel, one workgroup per head, merges
+//     after the launch boundary.
+// Either way every mutation happens after all reads of the head's slots, so
+// nothing races.  The ticket's tail is the last workgroups' atomics; the
+// second launch costs a launch.  The second launch wins when every split is
+// short and the grid is full, so that all workgroups of a head reach their
+// ticket at once (batch 1 of the 4x layer: 12.6 against 13.0 us per step);
+// the ticket wins otherwise (longer splits, whose workgroups finish spread
+// out, or few heads: 12.1 against 13.0 us at 512 slots per split, 10.8
+// against 12.5 us for one KV head).
+//
+// Publishing for the ticket without an L2 writeback.  The partial results
+// are written with agent-scope atomic stores, which gfx950 writes through to
+// the device's point of coherence; each workgroup waits until all of its
+// stores are acknowledged (vmcnt 0 and a barrier) before its ticket atomic.
+// The finishing workgroup invalidates its L2 (agent-scope acquire) before
+// it reads them.  A release fence would add a writeback of the whole L2
+// (buffer_wbl2), which only ordinary cached stores need: 1.6 us per
+// workgroup at batch 1.
 //
 // Latency.  All loads a workgroup needs (K/V and keys of its first chunk,
 // q, the new row, the control block, the score) are issued before anything
@@ -72,7 +91,9 @@ struct DecodeParams {
   MinPart* part_min;
   int32_t n_heads;
   int32_t budget, n_sink, n_scored, n_recent;
+  uint32_t* tickets;
   int32_t nsplit, rows_per_split;
+  int32_t finish_apart;  // several splits: merged by decode_finish_kernel
   float scale_log2e;
 };
 
@@ -417,6 +438,7 @@ __device__ __forceinline__ void update_cache(const DecodeParams& p, int head, co
       // with a one-token window the next leaving token is the one just added
       nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? dc.newslot : ring_next);
       p.ctl[head] = nc;
+      p.tickets[head] = 0u;
     }
   }
 }
@@ -424,7 +446,9 @@ __device__ __forceinline__ void update_cache(const DecodeParams& p, int head, co
 // One workgroup of 256 threads per (KV head, split).  K/V rows stream
 // through registers in chunks of 2 rows per thread, double-buffered: the
 // loads of the next chunk are in flight while the current one is computed.
-template <int D, int G>
+// APART: split heads are merged by decode_finish_kernel (else by the last
+// split's workgroup, after a ticket).
+template <int D, int G, bool APART>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int NT = 256;
   constexpr int NP = 2;                  // rows per thread per chunk
@@ -440,16 +464,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   static_assert(Q4 <= NT, "one thread per float4 of the accumulator");
   // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators, each
   // block padded by 8 floats so that neighbouring lanes' blocks start in
-  // different LDS banks
+  // different LDS banks; the finishing workgroup reuses it for the split merge
   constexpr int ACC_STRIDE = G * ACC + 8;
   constexpr int LDS_ROWS = NWAVE * R16 * LPR * ACC_STRIDE;
+  constexpr int LDS_MERGE = MAX_SPLITS * G + (NT / Q4) * G * D;
   static_assert(NWAVE * R16 <= WAVE, "key minima of the workgroup fit one wavefront");
+  constexpr int LDS_F = LDS_ROWS > LDS_MERGE ? LDS_ROWS : LDS_MERGE;
 
-  __shared__ __align__(16) float s_buf[LDS_ROWS];
+  __shared__ __align__(16) float s_buf[LDS_F];
   __shared__ float s_wm[NWAVE][G];       // wave max (log2 units)
   __shared__ float s_wl[NWAVE][R16][G];  // per DPP-row sums of p
+  __shared__ float s_L[G];
   __shared__ uint64_t s_mk[NWAVE * R16];
   __shared__ int32_t s_ms[NWAVE * R16];
+  __shared__ int32_t s_last;
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wid = tid / WAVE;
@@ -457,7 +485,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   // ---- workgroup -> (head, split); all splits of a head on one XCD when
   // the head count allows (workgroups are dealt to the 8 XCDs round robin),
   // so the head's control block, queries and new row, which every split
-  // reads, come from one L2.
+  // reads, come from one L2, and its ticket atomics from one XCD.
   int head, split;
   {
     const int bid = blockIdx.x;
@@ -711,13 +739,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       const uint32_t b2 = f32_to_bf16_rne(a.z * invL), b3 = f32_to_bf16_rne(a.w * invL);
       reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + o4] =
           make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    } else {
+    } else if (APART) {  // the launch boundary publishes them
       reinterpret_cast<float4*>(p.part_acc)[pidx * Q4 + o4] = a;
       if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
+    } else {  // written through to the point of coherence (see the file comment)
+      float* pa = p.part_acc + (pidx * Q4 + o4) * 4;
+      __hip_atomic_store(pa + 0, a.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pa + 1, a.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pa + 2, a.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pa + 3, a.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        float* pm = p.part_ml + (pidx * G + h) * 2;
+        __hip_atomic_store(pm + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pm + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
-  // Several splits: publish the partial results and the key minimum; the
-  // second launch (decode_finish_kernel) merges them.  A single split is
+  // Several splits: publish the partial results; the second launch or the
+  // last workgroup of the head to finish merges them.  A single split is
   // complete already.
   if (!single) {
     if (wid == 0) {
@@ -728,15 +767,33 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         sl0 = s_ms[lane];
       }
       wave_min_key_dpp(k0, sl0);
-      if (lane == 0) {
+      if (lane == 0 && APART) {
         MinPart mp;
         mp.key = k0;
         mp.slot = sl0;
         mp.pad = ring_next;  // read by the finishing launch
         p.part_min[pidx] = mp;
+      } else if (lane == 0) {
+        __hip_atomic_store(&p.part_min[pidx].key, k0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.part_min[pidx].slot, sl0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    return;
+    if (APART) return;
+
+    // ---- ticket: the last workgroup of the head finishes the step ----------
+    // Every thread's write-through stores are acknowledged before thread 0
+    // takes the ticket; the finisher's acquire invalidates its L2.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&p.tickets[head], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_splits<D, G>(p, head, s_buf, s_L, s_mk, s_ms);
   }
 
   // ---- cache update: new row, slot metadata, window ring, control block --
@@ -777,10 +834,17 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
 
 template <int D, int G>
 hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     stream, prm);
+  // The instance with the in-launch merge runs only where it merges; one
+  // split per head and the second-launch finish use the one without it.
+  if (prm.nsplit > 1 && !prm.finish_apart) {
+    hipLaunchKernelGGL((decode_kernel<D, G, false>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(256), 0, stream, prm);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_kernel<D, G, true>), dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                     0, stream, prm);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || prm.nsplit == 1) return e;
+  if (e != hipSuccess || !prm.finish_apart) return e;
   hipLaunchKernelGGL((decode_finish_kernel<D, G>), dim3(static_cast<uint32_t>(prm.n_heads)),
                      dim3(256), 0, stream, prm);
   return hipGetLastError();
@@ -826,6 +890,7 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
   prm.part_acc = work.part_acc;
   prm.part_ml = work.part_ml;
   prm.part_min = work.part_min;
+  prm.tickets = work.tickets;
   prm.n_heads = geo.batch * geo.n_kv_heads;
   prm.budget = geo.budget;
   prm.n_sink = geo.n_sink;
@@ -833,6 +898,7 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
   prm.n_recent = geo.n_recent;
   prm.nsplit = work.nsplit;
   prm.rows_per_split = work.rows_per_split;
+  prm.finish_apart = (work.nsplit > 1 && work.finish_apart) ? 1 : 0;
   prm.scale_log2e = scale_log2e;
   const int G = geo.n_q_heads / geo.n_kv_heads;
   if (work.nsplit < 1 || work.nsplit > MAX_SPLITS ||

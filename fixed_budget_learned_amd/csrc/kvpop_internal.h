@@ -62,15 +62,18 @@ struct DecodeWork {
   float* part_acc;     // [B*Hkv][nsplit][G][D]
   float* part_ml;      // [B*Hkv][nsplit][G][2]  (running max in log2 units, sum)
   MinPart* part_min;   // [B*Hkv][nsplit]
+  uint32_t* tickets;   // [B*Hkv], zero between calls
   int32_t nsplit;
   int32_t rows_per_split;
   int32_t threads;     // workgroup size of the decode kernel (256)
   int32_t rows_per_thread;  // K/V rows one thread holds per pass (2)
+  int32_t finish_apart;     // several splits: merge in a second launch
 };
 
 // Launchers: return hipSuccess or the launch error.  All work is enqueued
 // on `stream`; nothing is synchronised.
-hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, hipStream_t stream);
+hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int64_t n_tickets,
+                           hipStream_t stream);
 // Prefill workspace (one per cache; calls are stream-ordered).  Long prompts
 // select in two levels: up to SLICE_MAX slices per head first keep their own
 // top k, then one workgroup per head selects from the union.

@@ -599,7 +599,8 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBa
   }
 }
 
-__global__ void init_ctl_kernel(HeadCtl* __restrict__ ctl, int64_t n_heads) {
+__global__ void init_ctl_kernel(HeadCtl* __restrict__ ctl, int64_t n_heads,
+                                uint32_t* __restrict__ tickets, int64_t n_tickets) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n_heads) {
     HeadCtl c;
@@ -612,17 +613,19 @@ __global__ void init_ctl_kernel(HeadCtl* __restrict__ ctl, int64_t n_heads) {
     c.leave_slot = -1;
     ctl[i] = c;
   }
+  if (tickets != nullptr && i < n_tickets) tickets[i] = 0u;
 }
 
 }  // namespace
 
-hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, hipStream_t stream) {
-  const int64_t n = n_heads;
+hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int64_t n_tickets,
+                           hipStream_t stream) {
+  const int64_t n = n_heads > n_tickets ? n_heads : n_tickets;
   if (n == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (n + threads - 1) / threads;
   hipLaunchKernelGGL(init_ctl_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(threads), 0,
-                     stream, ctl, n_heads);
+                     stream, ctl, n_heads, tickets, n_tickets);
   return hipGetLastError();
 }
 

@@ -101,6 +101,12 @@ typedef struct kvpop_config {
                                 each of its heads is pruned back to its top
                                 n_scored (also on demand, kvpop_cache_prune).
                             Both hold the same rows right after a prune. */
+  int32_t decode_finish; /* how a decode step merges a head's splits (no
+                            effect with one split):
+                            0 = chosen by the library from the launch shape;
+                            1 = the last split's workgroup, in the same launch;
+                            2 = a second launch, one workgroup per head.
+                            The outputs and cache updates are identical. */
 } kvpop_config;
 
 typedef struct kvpop_state {

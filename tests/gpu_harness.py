@@ -76,11 +76,11 @@ class Geo:
 
 
 def make_cache(geo: Geo, n_layers=1, batch=1, decode_splits=0, max_positions=1 << 30,
-               prune_interval=0):
+               prune_interval=0, decode_finish=0):
     cfg = abi.make_config(n_layers, batch, geo.n_q_heads, geo.n_kv_heads, geo.head_dim,
                           geo.n_sink, geo.n_scored, geo.n_recent,
                           max_positions=max_positions, decode_splits=decode_splits,
-                          prune_interval=prune_interval)
+                          prune_interval=prune_interval, decode_finish=decode_finish)
     return abi.KVpopCache(cfg)
 
 

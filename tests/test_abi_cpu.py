@@ -84,6 +84,7 @@ def test_required_bytes_layout(lib):
     dict(batch=0), dict(max_positions=0), dict(decode_splits=257),
     dict(softmax_scale=float("nan")), dict(n_kv_heads=0),
     dict(prune_interval=-1), dict(prune_interval=4097),
+    dict(decode_finish=-1), dict(decode_finish=3),
 ])
 def test_invalid_configs_rejected(lib, bad):
     c = _cfg(**bad)

@@ -338,9 +338,9 @@ def test_dense_131k_context():
 # Determinism, split invariance, state machine
 # ---------------------------------------------------------------------------
 
-def _decode_run(geo, P, steps, splits, seed=7, kind="normal"):
+def _decode_run(geo, P, steps, splits, seed=7, kind="normal", finish=0):
     s = Stream(geo, P + steps, seed, kind)
-    cache = make_cache(geo, decode_splits=splits)
+    cache = make_cache(geo, decode_splits=splits, decode_finish=finish)
     cache.prefill_compact(0, 0, to_dev_bf16(s.k[:, :P]), to_dev_bf16(s.v[:, :P]),
                           to_dev_f32(s.scores[:, :P]))
     out = torch.empty((1, geo.n_q_heads, geo.head_dim), dtype=torch.bfloat16, device="cuda")
@@ -369,6 +369,33 @@ def test_deterministic_and_split_invariant():
             xf = out_to_f64(torch.from_numpy(x).view(torch.bfloat16))
             yf = out_to_f64(torch.from_numpy(y).view(torch.bfloat16))
             assert np.abs(xf - yf).max() <= 2e-3
+
+
+@pytest.mark.parametrize("geo,P,steps,splits,kind", [
+    (Geo(32, 8, 128, 4, 3772, 256), 16384, 20, 0, "normal"),   # full grid, 128-slot splits
+    (Geo(32, 8, 128, 4, 3772, 256), 16384, 20, 16, "ties"),    # 256-slot splits
+    (Geo(4, 1, 128, 4, 3772, 256), 9000, 24, 0, "normal"),     # one KV head, 32 splits
+    (Geo(16, 2, 64, 4, 7000, 64), 20000, 24, 0, "uniform"),    # D 64, long splits
+    (Geo(8, 8, 128, 2, 900, 16), 1500, 40, 7, "ties"),         # odd split count
+], ids=["4x_layer", "16_splits", "one_head", "d64_long", "odd"])
+def test_split_finishes_identical(geo, P, steps, splits, kind):
+    """Merging a head's splits in the last split's workgroup (decode_finish 1)
+    and in a second launch (decode_finish 2) run the same arithmetic: outputs
+    and kept sets must agree bit for bit, and with the oracle's kept set."""
+    log(f"finishes geo={geo} P={P} steps={steps} splits={splits} kind={kind}")
+    t_out, t_kept = _decode_run(geo, P, steps, splits, kind=kind, finish=1)
+    l_out, l_kept = _decode_run(geo, P, steps, splits, kind=kind, finish=2)
+    assert t_kept == l_kept
+    for i, (x, y) in enumerate(zip(t_out, l_out)):
+        assert np.array_equal(x, y), f"step {i}: the two finishes differ"
+    s = Stream(geo, P + steps, 7, kind)
+    orc = make_oracle(geo)
+    orc.prefill(s.k[:, :P], s.v[:, :P], s.scores[:, :P])
+    for n in range(P, P + steps):
+        ref = orc.decode(s.q[n], s.k[:, n], s.v[:, n], s.leaving(n), attend=(n == P + steps - 1))
+    check_output(out_to_f64(torch.from_numpy(t_out[-1]).view(torch.bfloat16))[0], ref, "last step")
+    for g in range(geo.n_kv_heads):
+        assert t_kept[g] == orc.kept(g), g
 
 
 def test_state_machine_errors_and_reset():

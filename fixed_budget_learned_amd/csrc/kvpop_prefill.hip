@@ -521,6 +521,18 @@ struct GatherBatch {
   GatherItem item[NB];
 };
 
+// 16-byte loads and stores that do not allocate in the caches: the prompt's
+// rows are read once and the cache rows are not read again by this launch.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load16(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store16(uint4 x, uint4* p) {
+  const u32x4_nt v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
+}
+
 // Rows per gather workgroup: 256 threads move 16 bytes each per pass.
 template <int D, int NB>
 __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBatch<NB> batch) {
@@ -575,8 +587,8 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBa
         } else {
           p = sh.w0 + (r - sh.s_eff - sh.kk);
         }
-        kr[u] = ksrc[static_cast<int64_t>(p) * LPR + c];
-        vr[u] = vsrc[static_cast<int64_t>(p) * LPR + c];
+        kr[u] = nt_load16(&ksrc[static_cast<int64_t>(p) * LPR + c]);
+        vr[u] = nt_load16(&vsrc[static_cast<int64_t>(p) * LPR + c]);
       }
       pos_r[u] = p;
       scored_r[u] = scored;
@@ -585,8 +597,8 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBa
     for (int u = 0; u < RPT; ++u) {
       const int32_t r = rb + u * RPP;
       if (r < r1) {
-        kdst[static_cast<int64_t>(r) * LPR + c] = kr[u];
-        vdst[static_cast<int64_t>(r) * LPR + c] = vr[u];
+        nt_store16(kr[u], &kdst[static_cast<int64_t>(r) * LPR + c]);
+        nt_store16(vr[u], &vdst[static_cast<int64_t>(r) * LPR + c]);
         if (c == 0) {
           const int64_t hs = static_cast<int64_t>(g) * budget + r;
           const int32_t p = pos_r[u];

@@ -410,7 +410,12 @@ int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, const float* s
   if (scores == nullptr || thr == nullptr) return KVPOP_EINVAL;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
+  // the first-level prefill buffer (free between calls) holds the segment starts
+  const kvpop::PrefillWork pw = cache->prefill_work();
+  const int64_t ws_keys = int64_t(pw.slice_items) * c.n_kv_heads * kvpop::SLICE_MAX *
+                          std::max(c.n_scored, 1);
   hipError_t e = kvpop::launch_prefix_thresholds(cache->geo(), n_tokens, scores, thr,
+                                                 pw.slice_keys, ws_keys,
                                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;

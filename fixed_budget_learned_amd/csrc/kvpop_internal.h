@@ -100,10 +100,14 @@ hipError_t launch_prefill_batch(const Geometry& geo, const LayerView& all,
                                 const PrefillItem* items, int32_t n, const PrefillWork& pw,
                                 hipStream_t stream);
 // Prefix top-k thresholds of a prompt ([Hkv][n_tokens] keys), n_scored <=
-// THR_KMAX.
+// THR_KMAX.  ws: workspace of ws_keys keys for the segment starts
+// ([Hkv][S][n_scored]; the number of segments S is capped to fit it); with
+// ws NULL the prompt is one segment per head.
 constexpr int THR_KMAX = 4096;
+constexpr int THR_SEG_MAX = 32;
 hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const float* scores,
-                                    uint64_t* thr, hipStream_t stream);
+                                    uint64_t* thr, uint64_t* ws, int64_t ws_keys,
+                                    hipStream_t stream);
 // Future-attention target of one sequence: work [2][Hq][n_tokens] fp32
 // (each query's log2-domain log-sum-exp, then each query head's share of the
 // target), y [Hkv][n_tokens] fp32 output; scale_log2e: the softmax scale

@@ -5,9 +5,19 @@
 // reaches it.  The "Qwen3-8B-KVpop-4x" model card lists a prefix top-k
 // thresholds kernel among its cache backends; the contract is a reading.
 //
-// One 1024-thread workgroup per KV head sweeps the candidates in chunks,
+// Segments.  The candidates of a head are cut into S segments (S = 1 for
+// short prompts, up to THR_SEG_MAX), spaced geometrically so that each
+// expects about as many entrants (k * ln(end / start) after the first k).
+// A first launch finds, for every segment, the exact top-k of all
+// candidates before it (for the first segment: the first k): a radix select
+// over the prefix (12-, 12- and 8-bit digits of the score code, ties at the
+// threshold code resolved by position, the newest kept), a gather of the k
+// keys and a sort in LDS.  The second launch runs one workgroup per
+// (segment, head) from that set.
+//
+// Within a segment a 1024-thread workgroup sweeps the candidates in chunks,
 // keeping the current top-k keys sorted ascending in LDS (R, k <= THR_KMAX;
-// R starts as k zero keys, below every real key).  A chunk holds about
+// in the first segment R starts as k zero keys, below every real key).  A chunk holds about
 // THR_ETARGET * m / k candidates after m have been seen (64 to 4,096), so
 // that about THR_ETARGET of them beat its threshold.  For a chunk with
 // threshold T0 = R[0]:
@@ -32,6 +42,9 @@
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
+#include <algorithm>
+#include <cmath>
+
 namespace kvpop {
 namespace {
 
@@ -39,6 +52,184 @@ constexpr int THR_THREADS = 1024;
 constexpr int THR_ARR = 1024;      // entrants one chunk can hold
 constexpr int THR_VMAX = 4;        // candidates per thread
 constexpr int THR_ETARGET = 192;   // expected entrants per chunk
+
+// Segment plan of a prompt: candidate ranges [b[j], b[j+1]) for j < S.
+struct ThrPlan {
+  int32_t S;
+  int32_t b[THR_SEG_MAX + 1];
+};
+
+// Ascending bitonic sort of a[0, p2) in LDS (p2 a power of two, at most
+// 4 * THR_THREADS); called by the whole workgroup.  Thread t handles pairs
+// t and t + 1,024, loading both before comparing.  A stage of stride 64 or
+// less stays inside the 128 elements of one wavefront (pair i touches
+// [2i - i mod stride, + stride], and pairs 64w .. 64w + 63 lie in block w),
+// and a wavefront's LDS operations run in order, so two such stages in a
+// row need no workgroup barrier between them.
+__device__ __forceinline__ void bitonic_sort_lds(uint64_t* a, int32_t p2) {
+  const int32_t tid = static_cast<int32_t>(threadIdx.x);
+  const int32_t npairs = p2 / 2;
+  for (int32_t size = 2; size <= p2; size <<= 1) {
+    for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      int32_t lo[2], hi[2];
+      uint64_t x[2], y[2];
+      bool live[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int32_t i = tid + u * THR_THREADS;
+        live[u] = i < npairs;
+        lo[u] = 2 * i - (i & (stride - 1));
+        hi[u] = lo[u] + stride;
+        if (live[u]) {
+          x[u] = a[lo[u]];
+          y[u] = a[hi[u]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool up = (lo[u] & size) == 0;
+        if (live[u] && (x[u] > y[u]) == up) {
+          a[lo[u]] = y[u];
+          a[hi[u]] = x[u];
+        }
+      }
+      const int32_t next = stride > 1 ? stride >> 1 : (size < p2 ? size : 0);
+      if (stride > 64 || next > 64)
+        __syncthreads();
+      else
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the next stage's loads after these stores
+    }
+  }
+  __syncthreads();
+}
+
+// f(i, code) for every candidate i in [0, n) of sc, coalesced, U loads per
+// thread in flight.  Every thread runs the same number of rounds; f is
+// called for i < n only.
+template <int U, typename F>
+__device__ __forceinline__ void stream_scores(const float* __restrict__ sc, int32_t n, F&& f) {
+  for (int32_t i0 = threadIdx.x; i0 - static_cast<int32_t>(threadIdx.x) < n;
+       i0 += THR_THREADS * U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = sc[min(i0 + u * THR_THREADS, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) f(i0 + u * THR_THREADS, score_code(x[u]));
+  }
+}
+
+// The exact top-k keys (ascending) of the first b[j] candidates of head g
+// (b[0] = k: the first k), the start of segment j, into
+// ws[(g * S + j) * k ...].  Grid (S, Hkv).
+__global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
+    const float* __restrict__ scores, int32_t P, int32_t s, int32_t k, ThrPlan plan,
+    uint64_t* __restrict__ ws) {
+  constexpr int NWAVE = THR_THREADS / WAVE;
+  __shared__ uint32_t hist[4096];
+  __shared__ uint64_t keys[THR_KMAX];
+  __shared__ uint32_t scan_buf[NWAVE + 1];
+  __shared__ uint32_t s_bin, s_above, s_neq, s_n;
+  __shared__ int32_t s_pcut;
+  const int j = blockIdx.x;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int32_t b = plan.b[j];                     // candidates [0, b), b >= k
+  const float* __restrict__ sc = scores + static_cast<int64_t>(g) * P + s;
+
+  // ---- radix select of the k-th largest code: 12-, 12- and 8-bit digits.
+  // The wide first digit (sign, exponent, 3 mantissa bits) spreads the codes
+  // of real-valued scores over many bins; with 8 bits most fell into a few
+  // bins and the histogram atomics serialised.
+  uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(k);
+  const int shifts[3] = {20, 8, 0}, nbins[3] = {4096, 4096, 256};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass], nb = nbins[pass];
+    for (int i = tid; i < nb; i += THR_THREADS) hist[i] = 0u;
+    __syncthreads();
+    stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
+      if (i < b && (o & mask) == prefix)
+        atomicAdd(&hist[(o >> shift) & static_cast<uint32_t>(nb - 1)], 1u);
+    });
+    __syncthreads();
+    // thread t holds bins nb-1-4t down to nb-4-4t, from the top
+    uint32_t h[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int bin = nb - 1 - 4 * tid - q;
+      h[q] = bin >= 0 ? hist[bin] : 0u;
+      sum += h[q];
+    }
+    uint32_t tot;
+    uint32_t ex = block_exclusive_scan_u32<THR_THREADS>(sum, scan_buf, &tot);
+    if (ex < krem && krem <= ex + sum) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (krem <= ex + h[q]) {
+          s_bin = static_cast<uint32_t>(nb - 1 - 4 * tid - q);
+          s_above = ex;
+          s_neq = h[q];
+          break;
+        }
+        ex += h[q];
+      }
+    }
+    __syncthreads();
+    krem -= s_above;
+    prefix |= s_bin << shift;
+    mask |= static_cast<uint32_t>(nb - 1) << shift;
+  }
+  const uint32_t t = prefix;               // the k-th largest code
+  const uint32_t drop = s_neq - krem;      // ties at t that lose (the oldest)
+
+  // ---- the first kept tie, in position order: rank `drop` among ties ------
+  if (tid == 0) s_pcut = 0;
+  if (drop > 0) {
+    const int32_t L = (b + THR_THREADS - 1) / THR_THREADS;  // contiguous run
+    const int32_t lo = min(tid * L, b), hi = min(lo + L, b);
+    uint32_t cnt = 0;
+    for (int32_t i = lo; i < hi; ++i) cnt += score_code(sc[i]) == t ? 1u : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan_u32<THR_THREADS>(cnt, scan_buf, &tot);
+    if (ex <= drop && drop < ex + cnt) {
+      uint32_t r = ex;
+      for (int32_t i = lo; i < hi; ++i) {
+        if (score_code(sc[i]) == t) {
+          if (r == drop) {
+            s_pcut = i;
+            break;
+          }
+          ++r;
+        }
+      }
+    }
+  }
+  if (tid == 0) s_n = 0u;
+  __syncthreads();
+  const int32_t pcut = s_pcut;
+
+  // ---- gather the k keys that reach the k-th largest key ------------------
+  stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
+    const bool keep = i < b && (o > t || (o == t && i >= pcut));
+    const uint64_t m = __ballot(keep);
+    uint32_t base = 0;
+    if (lane == 0 && m != 0ull) base = atomicAdd(&s_n, static_cast<uint32_t>(__popcll(m)));
+    base = __shfl(base, 0, WAVE);
+    if (keep) {
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      keys[base + below] = make_key(o, s + i);
+    }
+  });
+  int32_t p2 = 1;
+  while (p2 < k) p2 <<= 1;
+  __syncthreads();
+  for (int32_t i = k + tid; i < p2; i += THR_THREADS) keys[i] = ~0ull;  // sorts past the keys
+  __syncthreads();
+  bitonic_sort_lds(keys, p2);
+  uint64_t* dst = ws + (static_cast<int64_t>(g) * plan.S + j) * k;
+  for (int32_t i = tid; i < k; i += THR_THREADS) dst[i] = keys[i];
+}
 
 // #(x in a[0..n) with x < v), a sorted ascending
 __device__ __forceinline__ int32_t count_below(const uint64_t* a, int32_t n, uint64_t v) {
@@ -61,9 +252,10 @@ __device__ __forceinline__ int nth_set_bit(uint64_t mask, int n, int lane) {
   return __ffsll(static_cast<unsigned long long>(__ballot(hit))) - 1;
 }
 
+// One workgroup per (segment, head): grid (S, Hkv).
 __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
     const float* __restrict__ scores, int32_t P, int32_t s, int32_t k, int32_t W,
-    uint64_t* __restrict__ thr) {
+    uint64_t* __restrict__ thr, ThrPlan plan, const uint64_t* __restrict__ ws) {
   constexpr int NWAVE = THR_THREADS / WAVE;
   __shared__ uint64_t Rbuf[2][THR_KMAX];
   __shared__ uint64_t arr[THR_ARR];       // entrant keys in arrival order
@@ -75,7 +267,8 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
   __shared__ uint64_t tq[THR_ARR + 1];    // threshold after q entrants
   __shared__ uint32_t scan_buf[NWAVE + 1];
 
-  const int g = blockIdx.x;
+  const int jseg = blockIdx.x;
+  const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const float* sc = scores + static_cast<int64_t>(g) * P;
   uint64_t* out = thr + static_cast<int64_t>(g) * P;
@@ -83,15 +276,26 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
   const int32_t C = c1 > s ? c1 - s : 0;
   // positions before the first candidate leaves the window
   const int32_t n_first = min(P, s + W);           // positions [0, n_first)
-  for (int32_t n = tid; n < n_first; n += THR_THREADS) out[n] = 0ull;
+  if (jseg == 0)
+    for (int32_t n = tid; n < n_first; n += THR_THREADS) out[n] = 0ull;
   if (C == 0) return;
 
   uint64_t* R = Rbuf[0];
   uint64_t* R2 = Rbuf[1];
-  // ---- warm-up: until k candidates have left the window every one is kept
-  // (threshold 0); R = the first min(k, C) keys sorted, then zero keys ------
   const int32_t w0 = min(k, C);
-  {
+  const int32_t cs = plan.b[jseg], ce = plan.b[jseg + 1];  // this segment's candidates
+  if (plan.S > 1) {
+    // the top-k of every candidate before the segment, from the first launch
+    const uint64_t* src = ws + (static_cast<int64_t>(g) * plan.S + jseg) * k;
+    for (int32_t i = tid; i < k; i += THR_THREADS) R[i] = src[i];
+    __syncthreads();
+    if (jseg == 0) {  // the first k candidates: fewer than k after all but the last
+      for (int32_t i = tid; i < k - 1; i += THR_THREADS) out[s + W + i] = 0ull;
+      if (tid == 0) out[s + W + k - 1] = R[0];
+    }
+  } else {
+    // ---- warm-up: until k candidates have left the window every one is kept
+    // (threshold 0); R = the first min(k, C) keys sorted, then zero keys -----
     int32_t p2 = 1;
     while (p2 < k) p2 <<= 1;
     for (int32_t i = tid; i < p2; i += THR_THREADS) {
@@ -106,21 +310,7 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
       R2[i] = v;
     }
     __syncthreads();
-    for (int32_t size = 2; size <= p2; size <<= 1) {
-      for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int32_t i = tid; i < p2 / 2; i += THR_THREADS) {
-          const int32_t lo = 2 * i - (i & (stride - 1));
-          const int32_t hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const uint64_t a = R2[lo], b = R2[hi];
-          if ((a > b) == up) {
-            R2[lo] = b;
-            R2[hi] = a;
-          }
-        }
-        __syncthreads();
-      }
-    }
+    bitonic_sort_lds(R2, p2);
     uint64_t* t = R;
     R = R2;
     R2 = t;
@@ -144,10 +334,10 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
       xs[v] = (v < V) ? sc[s + i] : 0.f;
     }
   };
-  int32_t len = min(chunk_len(w0), C - w0);
+  int32_t len = min(chunk_len(cs), ce - cs);
   int V = (len + THR_THREADS - 1) / THR_THREADS;
-  if (w0 < C) load_run(w0, V);
-  for (int32_t c0 = w0; c0 < C;) {
+  if (cs < ce) load_run(cs, V);
+  for (int32_t c0 = cs; c0 < ce;) {
     // ---- 1. this thread's candidates and the entrants ---------------------
     const uint64_t T0 = R[0];
     uint64_t key[THR_VMAX];
@@ -164,13 +354,13 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
       }
       before = block_exclusive_scan_u32<THR_THREADS>(own, scan_buf, &e);
       if (e <= THR_ARR) break;
-      len = min(THR_THREADS, C - c0);  // too many entrants: one per thread
+      len = min(THR_THREADS, ce - c0);  // too many entrants: one per thread
       V = 1;
       load_run(c0, V);
     }
     // next chunk's scores go out now; their latency overlaps this chunk
     const int32_t c_next = c0 + len;
-    const int32_t len_next = c_next < C ? min(chunk_len(c_next), C - c_next) : 0;
+    const int32_t len_next = c_next < ce ? min(chunk_len(c_next), ce - c_next) : 0;
     const int V_next = (len_next + THR_THREADS - 1) / THR_THREADS;
     uint32_t qv[THR_VMAX];  // entrants up to and including each of this run
     {
@@ -181,7 +371,7 @@ __global__ __launch_bounds__(THR_THREADS) void prefix_thresholds_kernel(
         qv[v] = q;
       }
     }
-    if (c_next < C) load_run(c_next, V_next);
+    if (c_next < ce) load_run(c_next, V_next);
     __syncthreads();
     // ---- 2. sort the entrants: rank = #smaller, over broadcast reads ------
     if (tid < static_cast<int>(e)) {
@@ -282,7 +472,8 @@ __global__ void fill_u64_kernel(uint64_t* __restrict__ p, int64_t n, uint64_t v)
 }  // namespace
 
 hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const float* scores,
-                                    uint64_t* thr, hipStream_t stream) {
+                                    uint64_t* thr, uint64_t* ws, int64_t ws_keys,
+                                    hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
   if (geo.n_scored == 0) {
     const int64_t n = static_cast<int64_t>(geo.n_kv_heads) * n_tokens;
@@ -290,9 +481,39 @@ hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const
                        0, stream, thr, n, KEY_NONE);
     return hipGetLastError();
   }
-  if (geo.n_scored > THR_KMAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefix_thresholds_kernel, dim3(geo.n_kv_heads), dim3(THR_THREADS), 0, stream,
-                     scores, n_tokens, geo.n_sink, geo.n_scored, geo.n_recent, thr);
+  const int32_t k = geo.n_scored;
+  if (k > THR_KMAX) return hipErrorInvalidValue;
+  // segments: about one per 512 candidates after the first k, at most
+  // THR_SEG_MAX and as many as the workspace holds, spaced geometrically
+  // from k to C
+  const int32_t c1 = n_tokens - geo.n_recent;
+  const int32_t C = c1 > geo.n_sink ? c1 - geo.n_sink : 0;
+  const int32_t w0 = k < C ? k : C;
+  ThrPlan plan;
+  plan.S = 1;
+  const int64_t fit = ws != nullptr ? ws_keys / (static_cast<int64_t>(geo.n_kv_heads) * k) : 0;
+  if (C - w0 >= 4096 && fit >= 2)
+    plan.S = static_cast<int32_t>(std::min<int64_t>(std::min<int64_t>(THR_SEG_MAX, fit),
+                                                    (C - w0) / 512));
+  plan.b[0] = w0;
+  for (int j = 1; j < plan.S; ++j) {
+    const double f = std::pow(static_cast<double>(C) / w0, static_cast<double>(j) / plan.S);
+    const int64_t bj = static_cast<int64_t>(std::floor(w0 * f));
+    plan.b[j] = static_cast<int32_t>(std::min<int64_t>(std::max<int64_t>(bj, plan.b[j - 1]), C));
+  }
+  plan.b[plan.S] = C;
+  for (int j = plan.S + 1; j <= THR_SEG_MAX; ++j) plan.b[j] = C;
+  if (plan.S > 1) {
+    hipLaunchKernelGGL(thresholds_segment_start_kernel,
+                       dim3(static_cast<uint32_t>(plan.S), static_cast<uint32_t>(geo.n_kv_heads)),
+                       dim3(THR_THREADS), 0, stream, scores, n_tokens, geo.n_sink, k, plan, ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(prefix_thresholds_kernel,
+                     dim3(static_cast<uint32_t>(plan.S), static_cast<uint32_t>(geo.n_kv_heads)),
+                     dim3(THR_THREADS), 0, stream, scores, n_tokens, geo.n_sink, k, geo.n_recent,
+                     thr, plan, ws);
   return hipGetLastError();
 }
 

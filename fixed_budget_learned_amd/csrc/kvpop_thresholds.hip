@@ -212,13 +212,15 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
   stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
     const bool keep = i < b && (o > t || (o == t && i >= pcut));
     const uint64_t m = __ballot(keep);
-    uint32_t base = 0;
-    if (lane == 0 && m != 0ull) base = atomicAdd(&s_n, static_cast<uint32_t>(__popcll(m)));
-    base = __shfl(base, 0, WAVE);
-    if (keep) {
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-          static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-      keys[base + below] = make_key(o, s + i);
+    if (m != 0ull) {  // wavefront-uniform; most rounds keep nothing
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s_n, static_cast<uint32_t>(__popcll(m)));
+      base = __shfl(base, 0, WAVE);
+      if (keep) {
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+        keys[base + below] = make_key(o, s + i);
+      }
     }
   });
   int32_t p2 = 1;

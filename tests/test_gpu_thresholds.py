@@ -62,6 +62,8 @@ CASES = [
     ("k_one_long", (1, 4, 1, 16), 20000, "normal"),               # 4,096-candidate chunks
     ("k_two_ties", (2, 4, 2, 8), 9000, "ties"),
     ("increasing_overflow", (1, 4, 100, 16), 12000, "increasing"),  # every candidate enters
+    ("decreasing_segments", (1, 4, 300, 16), 12000, "decreasing"),   # every segment starts from the first k
+    ("largest_k_32_segments", (1, 4, 4096, 64), 40000, "normal"),
     ("qwen3_8b_layer_4x", (8, 4, 3772, 256), 16384, "normal"),
     ("long_context_131k", (8, 4, 1788, 256), 131072, "normal"),
 ]

@@ -816,8 +816,9 @@ def main():
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
             "traffic_unit": "bytes per step (FETCH_SIZE and WRITE_SIZE, copy-calibrated)",
-            "kernel": "decode step: decode_kernel (32 splits per KV head) and decode_finish_kernel "
-                      "(split merge and cache update); head_dim 128, 4 query heads per KV head",
+            "kernel": "decode step: decode_kernel, 32 splits per KV head; the last split of each "
+                      "head merges the partials and writes the cache update in the same launch; "
+                      "head_dim 128, 4 query heads per KV head",
             "bytes_per_step": bpl,
             "note": "one layer's working set (16.5 MB) fits in the 256 MB last-level cache, so "
                     "back-to-back steps can be served partly from cache",

@@ -64,10 +64,10 @@ bool config_valid(const kvpop_config* c) {
 // workgroups per unit) measured slower, since the workgroups start later and
 // the merge has twice the partials.
 //
-// Split heads are merged in a second launch when the grid is full and every
-// split is at most 128 slots (two chunks per workgroup): then all splits of
-// a head finish together and their ticket atomics would queue.  Otherwise
-// the last split's workgroup merges in the same launch.
+// Split heads are merged by the last split's workgroup, in the same launch,
+// unless the configuration asks for the second launch: with each head's
+// ticket on its own cache line the in-launch merge measured faster on every
+// shape from 1 to 24 sequences (4x layer at batch 1: 10.7 against 12.4 us).
 void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
                          int32_t* threads, int32_t* rows_per_thread, int32_t* finish_apart) {
   const int64_t budget = capacity_of(c);
@@ -87,10 +87,7 @@ void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_p
   *rows_per_split = int32_t(rows);
   *threads = nt;
   *rows_per_thread = np;
-  if (c.decode_finish == 0)
-    *finish_apart = (heads * ns >= 256 && rows <= 128) ? 1 : 0;
-  else
-    *finish_apart = (c.decode_finish == 2) ? 1 : 0;
+  *finish_apart = (c.decode_finish == 2) ? 1 : 0;
 }
 
 bool compute_layout(const kvpop_config& c, Layout* L) {
@@ -133,7 +130,7 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
   ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
   ok = ok && mul_ok(parts, sizeof(kvpop::MinPart), &tmp) && take(tmp, &L->part_min);
-  ok = ok && take(heads * 4, &L->tickets);
+  ok = ok && take(heads * 4 * kvpop::TICKET_STRIDE, &L->tickets);
   L->total = off;
   return ok;
 }
@@ -277,7 +274,7 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
   hipError_t e = kvpop::launch_init_ctl(reinterpret_cast<kvpop::HeadCtl*>(c->base + L.ctl),
                                         int64_t(heads_all),
                                         reinterpret_cast<uint32_t*>(c->base + L.tickets),
-                                        int64_t(heads), nullptr);
+                                        int64_t(heads) * kvpop::TICKET_STRIDE, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) {
     if (c->owns) (void)hipFree(c->base);

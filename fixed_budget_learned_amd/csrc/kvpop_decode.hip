@@ -79,6 +79,12 @@ constexpr int MAX_SPLITS = 256;
 // batch 64 it raises the step from 5.9 to 6.6 TB/s; batch 1, whose layer
 // fits in the last-level cache, is unchanged.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor, last word: 32-bit data format (untyped access).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+// Cache-policy operand of buffer stores: SC1, write through to the device's
+// point of coherence (what an agent-scope atomic store uses).
+constexpr int CPOL_SC1 = 16;
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -448,7 +454,7 @@ __device__ __forceinline__ void update_cache(const DecodeParams& p, int head, co
       // with a one-token window the next leaving token is the one just added
       nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? dc.newslot : ring_next);
       p.ctl[head] = nc;
-      p.tickets[head] = 0u;
+      p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE] = 0u;
     }
   }
 }
@@ -753,11 +759,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       reinterpret_cast<float4*>(p.part_acc)[pidx * Q4 + o4] = a;
       if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
     } else {  // written through to the point of coherence (see the file comment)
-      float* pa = p.part_acc + (pidx * Q4 + o4) * 4;
-      __hip_atomic_store(pa + 0, a.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pa + 1, a.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pa + 2, a.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pa + 3, a.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // One 16-byte store per thread with the write-through cache bit, so a
+      // wavefront writes whole cache lines (four 4-byte atomic stores wrote
+      // each line four times).  The descriptor covers this split's partial.
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          p.part_acc + pidx * Q4 * 4, 0, Q4 * 16, BUF_RSRC_WORD3);
+      const u32x4_t v = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                         __float_as_uint(a.w)};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, o4 * 16, 0, CPOL_SC1);
       if (d == 0) {
         float* pm = p.part_ml + (pidx * G + h) * 2;
         __hip_atomic_store(pm + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -797,7 +806,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     __syncthreads();
     if (tid == 0) {
       const uint32_t prev =
-          __hip_atomic_fetch_add(&p.tickets[head], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(&p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
     }
     __syncthreads();

@@ -57,12 +57,16 @@ struct Geometry {
   int32_t slack;
 };
 
+// Each head's split ticket sits alone in a 256-byte block: atomics on one
+// cache line serialise in L2, so heads sharing a line would queue together.
+constexpr int TICKET_STRIDE = 64;
+
 // Decode workspace, shared by every layer (calls are stream-ordered).
 struct DecodeWork {
-  float* part_acc;     // [B*Hkv][nsplit][G][D]
+  float* part_acc;     // [B*Hkv][nsplit][2][G*D/4] float2: (x, y) pairs, then (z, w)
   float* part_ml;      // [B*Hkv][nsplit][G][2]  (running max in log2 units, sum)
   MinPart* part_min;   // [B*Hkv][nsplit]
-  uint32_t* tickets;   // [B*Hkv], zero between calls
+  uint32_t* tickets;   // [B*Hkv][TICKET_STRIDE], element 0 used; zero between calls
   int32_t nsplit;
   int32_t rows_per_split;
   int32_t threads;     // workgroup size of the decode kernel (256)

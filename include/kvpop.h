@@ -103,7 +103,7 @@ typedef struct kvpop_config {
                             Both hold the same rows right after a prune. */
   int32_t decode_finish; /* how a decode step merges a head's splits (no
                             effect with one split):
-                            0 = chosen by the library from the launch shape;
+                            0 = the library's default, currently 1;
                             1 = the last split's workgroup, in the same launch;
                             2 = a second launch, one workgroup per head.
                             The outputs and cache updates are identical. */

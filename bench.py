@@ -66,12 +66,21 @@ def _load_traffic(kernel_hash: str, path: str = PROFILE_PMC):
     return d.get("hbm_bytes_per_step")
 
 
+def _strip_comments(src: str) -> str:
+    """C++ source without comments and blank lines: what the compiler sees
+    of it, so that an edited comment does not count as a changed kernel."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
+
+
 def _kernel_hash() -> str:
     import hashlib
     h = hashlib.sha1()
     for name in ("kvpop_decode.hip", "kvpop_device.h", "kvpop_internal.h"):
-        with open(os.path.join(ROOT, "fixed_budget_learned_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fixed_budget_learned_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

@@ -1,6 +1,7 @@
 // One decode step of the fixed-budget cache for gfx950: the delayed-eviction
 // update and split-K GQA decode attention over the bounded cache, fused into
-// one launch per layer (two where a second launch merges split heads).
+// one launch per layer (two if the configuration asks for a second launch
+// to merge split heads).
 //
 // What a step does for each (sequence, KV head), token n = previous n + 1:
 //   * Token t = n - W leaves the protected window and only now receives its
@@ -25,22 +26,22 @@
 // softmax state (max, sum, unnormalised accumulator) and the minimum key
 // over its slots as they will be after this step, and the splits are merged
 // into the bf16 output, followed by the cache update, in one of two ways:
-//   * ticket: each workgroup takes a ticket after publishing, and the last
-//     one of the head merges;
+//   * ticket (the default): each workgroup takes a ticket after publishing,
+//     and the last one of the head merges;
 //   * second launch: decode_finish_kernel, one workgroup per head, merges
 //     after the launch boundary.
 // Either way every mutation happens after all reads of the head's slots, so
-// nothing races.  The ticket's tail is the last workgroups' atomics; the
-// second launch costs a launch.  The second launch wins when every split is
-// short and the grid is full, so that all workgroups of a head reach their
-// ticket at once (batch 1 of the 4x layer: 12.6 against 13.0 us per step);
-// the ticket wins otherwise (longer splits, whose workgroups finish spread
-// out, or few heads: 12.1 against 13.0 us at 512 slots per split, 10.8
-// against 12.5 us for one KV head).
+// nothing races.  The ticket's tail is one atomic round trip and the merge's
+// loads; the second launch costs a launch.  Each head's ticket counter sits
+// alone in a 256-byte block: atomics on one cache line serialise in L2, and
+// with the counters packed the 256 ticket atomics of a batch-1 step queued
+// behind one line (12.4 us per step with the second launch, 13.0 with that
+// ticket, 10.7 with one counter per block).
 //
 // Publishing for the ticket without an L2 writeback.  The partial results
-// are written with agent-scope atomic stores, which gfx950 writes through to
-// the device's point of coherence; each workgroup waits until all of its
+// are written with write-through stores (SC1: 16-byte buffer stores for the
+// accumulators, agent-scope atomic stores for the rest), which reach the
+// device's point of coherence; each workgroup waits until all of its
 // stores are acknowledged (vmcnt 0 and a barrier) before its ticket atomic.
 // The finishing workgroup invalidates its L2 (agent-scope acquire) before
 // it reads them.  A release fence would add a writeback of the whole L2

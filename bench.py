@@ -661,8 +661,10 @@ def main():
                     help="skip the tiny, 36-layer and 131k-token workloads and the cold-cache line")
     ap.add_argument("--batched-only", action="store_true",
                     help="run only the batch-64 serving measurement (for profiles)")
-    ap.add_argument("--only", choices=("future", "thresholds", "dynamic"), default=None,
-                    help="run only this section on the one-layer workload (for profiles)")
+    ap.add_argument("--only", choices=("future", "thresholds", "dynamic", "long_context"),
+                    default=None,
+                    help="run only this section (for profiles): future, thresholds and dynamic "
+                         "on the one-layer workload, long_context the 36-layer 131k-token one")
     ap.add_argument("--no-dense-sweep", action="store_true",
                     help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -697,6 +699,8 @@ def main():
         elif args.only == "thresholds":
             r = [prefix_thresholds_rate(QWEN3_8B_LAYER_4X, max(1, args.steps)),
                  prefix_thresholds_rate(LONG_131K_8X, max(1, args.steps))]
+        elif args.only == "long_context":
+            r = layered_config(LONG_131K_8X, args.decode_steps or 32, max(1, args.steps))
         else:
             r = dynamic_backend(args.decode_steps or 1024, max(1, args.steps))
         print(json.dumps({args.only: r}), flush=True)

@@ -661,10 +661,12 @@ def main():
                     help="skip the tiny, 36-layer and 131k-token workloads and the cold-cache line")
     ap.add_argument("--batched-only", action="store_true",
                     help="run only the batch-64 serving measurement (for profiles)")
-    ap.add_argument("--only", choices=("future", "thresholds", "dynamic", "long_context"),
+    ap.add_argument("--only", choices=("future", "thresholds", "dynamic", "long_context",
+                                       "stack_16k"),
                     default=None,
                     help="run only this section (for profiles): future, thresholds and dynamic "
-                         "on the one-layer workload, long_context the 36-layer 131k-token one")
+                         "on the one-layer workload, long_context the 36-layer 131k-token one, "
+                         "stack_16k the 36-layer 16k-token one")
     ap.add_argument("--no-dense-sweep", action="store_true",
                     help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -693,7 +695,7 @@ def main():
 
     if args.only:
         abi.load()
-        from fixed_budget_learned_amd.configs import LONG_131K_8X, QWEN3_8B_LAYER_4X
+        from fixed_budget_learned_amd.configs import LONG_131K_8X, QWEN3_8B_36L_4X, QWEN3_8B_LAYER_4X
         if args.only == "future":
             r = future_target_rate(QWEN3_8B_LAYER_4X, max(1, args.steps))
         elif args.only == "thresholds":
@@ -701,6 +703,8 @@ def main():
                  prefix_thresholds_rate(LONG_131K_8X, max(1, args.steps))]
         elif args.only == "long_context":
             r = layered_config(LONG_131K_8X, args.decode_steps or 32, max(1, args.steps))
+        elif args.only == "stack_16k":
+            r = layered_config(QWEN3_8B_36L_4X, args.decode_steps or 32, max(1, args.steps))
         else:
             r = dynamic_backend(args.decode_steps or 1024, max(1, args.steps))
         print(json.dumps({args.only: r}), flush=True)

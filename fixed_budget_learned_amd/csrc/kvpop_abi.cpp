@@ -455,8 +455,8 @@ int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, cons
     if (int64_t(nh[b]) + 1 >= c.max_positions) return KVPOP_ESTATE;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
-  hipError_t e = kvpop::launch_decode(cache->geo(), cache->layer(layer), cache->work(), q, k_new,
-                                      v_new, score_leaving, out, cache->scale_log2e,
+  hipError_t e = kvpop::launch_decode(cache->geo(), cache->layer(layer), cache->work(), 1, q,
+                                      k_new, v_new, score_leaving, out, cache->scale_log2e,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     cache->poisoned = true;

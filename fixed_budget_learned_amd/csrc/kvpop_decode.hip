@@ -17,42 +17,47 @@
 // Decomposition.  The grid is (head, split): each workgroup owns a range of
 // slots of one KV head.  Every workgroup re-derives the same eviction
 // decision from the head's control block (which also carries the slot of the
-// token about to leave the window, so no dependent lookup is needed), so no
-// workgroup waits for another.  A workgroup reads K/V of its slots from the
-// cache, and substitutes the k_new/v_new row for the slot the new token
-// takes.  With one split per head (batched serving) the workgroup then
-// writes the output and the cache update (new K/V row, keys, positions,
-// window ring, control block) itself.  With several, each writes a partial
-// softmax state (max, sum, unnormalised accumulator) and the minimum key
-// over its slots as they will be after this step, and the splits are merged
-// into the bf16 output, followed by the cache update, in one of two ways:
+// token about to leave the window), so no workgroup waits for another.  A
+// workgroup reads K/V of its slots from the cache and substitutes the
+// k_new/v_new row, and the new keys, for the slots that change, so the slot
+// contents in memory are never needed for those two slots during the step.
+// That lets split 0 write the new row, the two changed keys, the new
+// position and the window ring as soon as it has the decision.  Only the
+// control block (read by every workgroup at its start) and the output wait
+// for the end of the step.  With one split per head (batched serving) the
+// workgroup writes them itself.  With several, each writes a partial
+// softmax state (max, sum, unnormalised accumulator) and the minimum key of
+// its slots as they stand after this step, and the splits are merged into
+// the bf16 output and the new control block in one of two ways:
 //   * ticket (the default): each workgroup takes a ticket after publishing,
 //     and the last one of the head merges;
 //   * second launch: decode_finish_kernel, one workgroup per head, merges
 //     after the launch boundary.
-// Either way every mutation happens after all reads of the head's slots, so
-// nothing races.  The ticket's tail is one atomic round trip and the merge's
-// loads; the second launch costs a launch.  Each head's ticket counter sits
-// alone in a 256-byte block: atomics on one cache line serialise in L2, and
-// with the counters packed the 256 ticket atomics of a batch-1 step queued
-// behind one line (12.4 us per step with the second launch, 13.0 with that
-// ticket, 10.7 with one counter per block).
+// Each head's ticket counter sits alone in a 256-byte block: atomics on one
+// cache line serialise in L2.
 //
-// Publishing for the ticket without an L2 writeback.  The partial results
-// are written with write-through stores (SC1: 16-byte buffer stores for the
-// accumulators, agent-scope atomic stores for the rest), which reach the
-// device's point of coherence; each workgroup waits until all of its
-// stores are acknowledged (vmcnt 0 and a barrier) before its ticket atomic.
-// The finishing workgroup invalidates its L2 (agent-scope acquire) before
-// it reads them.  A release fence would add a writeback of the whole L2
-// (buffer_wbl2), which only ordinary cached stores need: 1.6 us per
-// workgroup at batch 1.
+// Publishing for the ticket.  The partial results are written with
+// write-through stores (cache policy SC1, what an agent-scope atomic store
+// uses), which reach the device's point of coherence; each workgroup waits
+// until its stores are acknowledged (vmcnt 0) and meets the others at a
+// barrier before one thread takes the ticket, so every store of the
+// workgroup is performed before its ticket.  The finishing workgroup reads
+// the partials with coherent loads (cache policy SC1, what an agent-scope
+// atomic load uses), which do not hit stale lines of its L2, so it needs no
+// L2 invalidate.  A release fence would add a writeback of the whole L2,
+// which only ordinary cached stores need.
 //
-// Latency.  All loads a workgroup needs (K/V and keys of its first chunk,
-// q, the new row, the control block, the score) are issued before anything
-// waits, and chunks (K/V rows and their keys) are double-buffered in
-// registers; K/V rows are read with non-temporal loads.  The merge issues
-// all of its loads at once.
+// Latency.  At batch 1 a step is a chain: the K/V stream, then the
+// reduction of a workgroup's 256 threads into one partial state, the
+// publishing round trip and the ticket, then the finisher's merge.  With one
+// wave per SIMD every instruction of that chain is exposed (about 4 cycles
+// per instruction), so the reductions are written to keep the instruction
+// count low: DPP folded into the adds, v_permlane32/16_swap transposing
+// pairs of accumulators so that each level halves the registers instead of
+// duplicating sums, one small LDS exchange across waves, and a finisher in
+// which every thread owns a few output columns and takes one load per
+// split.  The chunk loop issues no loads past the last chunk, so the
+// reduction does not wait for a dummy prefetch.
 //
 // Inner loop.  LPR = D/16 lanes share one row; each lane holds two 16-byte
 // pieces (offsets 16*lane and D + 16*lane bytes), so every load instruction
@@ -64,8 +69,6 @@
 // probabilities of both rows are packed into one register, the two rows' V
 // values are interleaved with v_perm, and v_dot2 adds both products into the
 // fp32 accumulator (the sum of probabilities uses the same rounded values).
-// Row groups are summed with DPP inside each wave and through LDS across
-// waves.
 #include <hip/hip_runtime.h>
 
 #include "kvpop_device.h"
@@ -80,12 +83,15 @@ constexpr int MAX_SPLITS = 256;
 // batch 64 it raises the step from 5.9 to 6.6 TB/s; batch 1, whose layer
 // fits in the last-level cache, is unchanged.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Raw buffer descriptor, last word: 32-bit data format (untyped access).
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
-// Cache-policy operand of buffer stores: SC1, write through to the device's
-// point of coherence (what an agent-scope atomic store uses).
+// Cache-policy operand of buffer accesses: SC1, coherent at agent scope
+// (stores write through to the device's point of coherence; loads do not
+// hit stale L2 lines).
 constexpr int CPOL_SC1 = 16;
+
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -103,19 +109,17 @@ struct DecodeParams {
   int32_t* pos;
   int32_t* ring;
   HeadCtl* ctl;
-  float* part_acc;
-  float* part_ml;
-  MinPart* part_min;
+  float* part_acc;    // [heads][nsplit][G*D]
+  float* part_ml;     // [heads][nsplit][G][2]  (max in log2 units, sum)
+  MinPart* part_min;  // [heads][nsplit]
+  uint32_t* tickets;
   int32_t n_heads;
   int32_t budget, n_sink, n_scored, n_recent;
-  uint32_t* tickets;
   int32_t nsplit, rows_per_split;
-  int32_t finish_apart;  // several splits: merged by decode_finish_kernel
   float scale_log2e;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -123,15 +127,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// DPP row controls (rows of 16 lanes).
-constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+// DPP controls (rows of 16 lanes).
+constexpr int DPP_QUAD_XOR1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_ROR8 = 0x128;    // lane i reads lane i^8 of its row
 
+// x read from another lane; every lane has a valid source, so bound_ctrl
+// lets the compiler fold the move into the consuming add.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of LPR lanes (LPR = 4 or 8); result in all lanes.
@@ -143,70 +150,80 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ bool key_less(uint64_t ka, int32_t sa, uint64_t kb, int32_t sb) {
-  return ka < kb || (ka == kb && sa < sb);
-}
-
-// Full-wavefront reductions: DPP inside each 16-lane row, then two
-// cross-row exchanges.  Results land in every lane.
-__device__ __forceinline__ float row16_max(float x) {
+// Full-wavefront max and sum (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
   x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
   x = fmaxf(x, dpp_f<DPP_HALF_MIRROR>(x));
   x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float row16_sum(float x) {
+__device__ __forceinline__ float wave_sum(float x) {
   x += dpp_f<DPP_QUAD_XOR1>(x);
   x += dpp_f<DPP_QUAD_XOR2>(x);
   x += dpp_f<DPP_HALF_MIRROR>(x);
   x += dpp_f<DPP_ROW_MIRROR>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Minimum of a 64-bit key over the wavefront (every lane gets it).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_mov_dpp(static_cast<uint32_t>(x), CTRL, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp(static_cast<uint32_t>(x >> 32), CTRL, 0xF, 0xF, true);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return b < a ? b : a; }
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+  x = min_u64(x, dpp_u64<DPP_QUAD_XOR1>(x));
+  x = min_u64(x, dpp_u64<DPP_QUAD_XOR2>(x));
+  x = min_u64(x, dpp_u64<DPP_HALF_MIRROR>(x));
+  x = min_u64(x, dpp_u64<DPP_ROW_MIRROR>(x));
+  {
+    const uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    x = min_u64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]);
+  }
+  {
+    const uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    x = min_u64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]);
+  }
   return x;
 }
-__device__ __forceinline__ float wave_max(float x) {
-  x = row16_max(x);
-  x = fmaxf(x, __shfl_xor(x, 16, WAVE));
-  return fmaxf(x, __shfl_xor(x, 32, WAVE));
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row16_sum(x);
-  x += __shfl_xor(x, 16, WAVE);
-  return x + __shfl_xor(x, 32, WAVE);
-}
 
-template <int CTRL>
-__device__ __forceinline__ void dpp_min_key_step(uint64_t& key, int32_t& slot) {
-  const uint32_t lo = static_cast<uint32_t>(key), hi = static_cast<uint32_t>(key >> 32);
-  const uint32_t lo2 = __builtin_amdgcn_update_dpp(0u, lo, CTRL, 0xF, 0xF, false);
-  const uint32_t hi2 = __builtin_amdgcn_update_dpp(0u, hi, CTRL, 0xF, 0xF, false);
-  const int32_t s2 = __builtin_amdgcn_update_dpp(0, slot, CTRL, 0xF, 0xF, false);
-  const uint64_t k2 = (static_cast<uint64_t>(hi2) << 32) | lo2;
-  if (key_less(k2, s2, key, slot)) {
-    key = k2;
-    slot = s2;
-  }
+// Transposing pair reductions.  Each takes two per-lane values a and b and
+// returns one register in which half of the lanes hold a summed with its
+// partner lane and the other half b summed with its partner:
+//   swap32: lanes 0-31 a(l) + a(l+32), lanes 32-63 b(l-32) + b(l)
+//   swap16: rows 0, 2 a summed over rows (0,1) / (2,3); rows 1, 3 b likewise
+//   xor8:   lanes with bit 3 clear a(l) + a(l^8), set b(l) + b(l^8)
+//   xor4:   the same on lane bit 2
+// so a value needs half an instruction pair per level and no lane holds a
+// duplicate.
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// Lexicographic minimum of (key, slot) over each 16-lane row, in all lanes.
-__device__ __forceinline__ void row16_min_key(uint64_t& key, int32_t& slot) {
-  dpp_min_key_step<DPP_QUAD_XOR1>(key, slot);
-  dpp_min_key_step<DPP_QUAD_XOR2>(key, slot);
-  dpp_min_key_step<DPP_HALF_MIRROR>(key, slot);
-  dpp_min_key_step<DPP_ROW_MIRROR>(key, slot);
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// ... and over the whole wavefront.
-__device__ __forceinline__ void wave_min_key_dpp(uint64_t& key, int32_t& slot) {
-  row16_min_key(key, slot);
-#pragma unroll
-  for (int m = 16; m <= 32; m *= 2) {
-    const uint64_t k2 = __shfl_xor(key, m, WAVE);
-    const int32_t s2 = __shfl_xor(slot, m, WAVE);
-    if (key_less(k2, s2, key, slot)) {
-      key = k2;
-      slot = s2;
-    }
-  }
+__device__ __forceinline__ float xor8_add(float a, float b, bool hi) {
+  const float c = hi ? b : a, d = hi ? a : b;
+  return c + dpp_f<DPP_ROW_ROR8>(d);
+}
+__device__ __forceinline__ float xor4_add(float a, float b, bool hi) {
+  const float c = hi ? b : a, d = hi ? a : b;
+  return c + __shfl_xor(d, 4, WAVE);
 }
 
 // Lazy rescaling: the running max only moves when a logit exceeds it by
@@ -219,28 +236,16 @@ constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
 // 2^-126 flush to zero, which the softmax weights tolerate).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, WAVE)); }
-
 // Max over the whole wavefront of a value that is identical within aligned
 // groups of LPR lanes.
 template <int LPR>
 __device__ __forceinline__ float wave_max_groups(float x) {
-  if constexpr (LPR <= 4) x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
-                               0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF,
-                                                           false)));  // row_ror:8
-  x = xor_max(x, 16);
-  x = xor_max(x, 32);
-  return x;
-}
-
-// Sum over the row groups of one 16-lane DPP row (lanes i, i+8 [, i+4, i+12]).
-template <int LPR>
-__device__ __forceinline__ float row16_sum_groups(float x) {
-  if constexpr (LPR <= 4)
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-  return x;
+  if constexpr (LPR <= 4) x = fmaxf(x, dpp_f<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_f<DPP_ROW_ROR8>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // The step's eviction decision for one head, derived from its control block
@@ -288,176 +293,222 @@ __device__ __forceinline__ Decision decide(const HeadCtl& c, float sg, int32_t n
   return d;
 }
 
-// Merge the partial results of a head's splits into the bf16 output rows of
-// its G query heads, and the splits' key minima into s_mk/s_ms (one entry
-// per 16-lane row of the workgroup).  Called by the whole 256-thread
-// workgroup.  Every load (accumulators, maxima and sums, key minima) is
-// issued before the first wait.
-template <int D, int G>
-__device__ __forceinline__ void merge_splits(const DecodeParams& p, int head, float* s_buf,
-                                             float* s_L, uint64_t* s_mk, int32_t* s_ms) {
-  constexpr int NT = 256;
-  constexpr int NWAVE = NT / WAVE;
-  constexpr int R16 = WAVE / 16;
-  constexpr int Q4 = G * D / 4;          // float4s in one split's accumulator
-  static_assert(Q4 <= NT && NT % Q4 == 0, "merge layout");
-  constexpr int TS = NT / Q4;            // threads per float4 column
-  constexpr int MB = MAX_SPLITS / TS < 16 ? MAX_SPLITS / TS : 16;  // loads in flight per thread
-  constexpr int SPL = MAX_SPLITS / WAVE;  // splits per lane
-  static_assert(MAX_SPLITS <= NT, "one key minimum per thread");
-  const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1);
-  const int wid = tid / WAVE;
-  const int r16 = lane / 16;
-  const int ns = p.nsplit;
-  const int64_t p0 = static_cast<int64_t>(head) * ns;
-  float* s_pf = s_buf;                     // [ns][G] rescale factor
-  float* s_red = s_buf + MAX_SPLITS * G;   // [TS][G*D] per-thread-group sums
-  const int j4 = tid % Q4;
-  const int s0 = tid / Q4;
-  const float4* pacc4 = reinterpret_cast<const float4*>(p.part_acc) + j4;
-  float4 raw[MB];
-#pragma unroll
-  for (int u = 0; u < MB; ++u) {
-    const int sp = s0 + u * TS;
-    raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  MinPart mp;
-  mp.key = KEY_NONE;
-  mp.slot = 0x7FFFFFFF;
-  if (tid < ns) mp = p.part_min[p0 + tid];
-  const float2* pml2 = reinterpret_cast<const float2*>(p.part_ml);
-  for (int h = wid; h < G; h += NWAVE) {
-    float2 ml[SPL];
-#pragma unroll
-    for (int u = 0; u < SPL; ++u) {
-      const int sp = lane + u * WAVE;
-      ml[u] = (sp < ns) ? pml2[(p0 + sp) * G + h] : make_float2(-INFINITY, 0.f);
-    }
-    float M = ml[0].x;
-#pragma unroll
-    for (int u = 1; u < SPL; ++u) M = fmaxf(M, ml[u].x);
-    M = wave_max(M);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
-#pragma unroll
-    for (int u = 0; u < SPL; ++u) {
-      const int sp = lane + u * WAVE;
-      const float f = fast_exp2(ml[u].x - Ms);
-      if (sp < ns) s_pf[sp * G + h] = f;
-      L = fmaf(ml[u].y, f, L);
-    }
-    L = wave_sum(L);
-    if (lane == 0) s_L[h] = L;
-  }
-  {
-    uint64_t k0 = mp.key;
-    int32_t sl0 = mp.slot;
-    row16_min_key(k0, sl0);
-    if (lane % 16 == 0) {
-      s_mk[wid * R16 + r16] = k0;
-      s_ms[wid * R16 + r16] = sl0;
-    }
-  }
-  __syncthreads();
-  const int hq = (j4 * 4) / D;
-  float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int u = 0; u < MB; ++u) {
-    const int sp = s0 + u * TS;
-    const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
-    a4.x = fmaf(raw[u].x, f, a4.x);
-    a4.y = fmaf(raw[u].y, f, a4.y);
-    a4.z = fmaf(raw[u].z, f, a4.z);
-    a4.w = fmaf(raw[u].w, f, a4.w);
-  }
-  for (int sb = s0 + MB * TS; sb < ns; sb += MB * TS) {  // more than MB*TS splits
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-      const int sp = sb + u * TS;
-      raw[u] = (sp < ns) ? pacc4[(p0 + sp) * Q4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-      const int sp = sb + u * TS;
-      const float f = (sp < ns) ? s_pf[sp * G + hq] : 0.f;
-      a4.x = fmaf(raw[u].x, f, a4.x);
-      a4.y = fmaf(raw[u].y, f, a4.y);
-      a4.z = fmaf(raw[u].z, f, a4.z);
-      a4.w = fmaf(raw[u].w, f, a4.w);
-    }
-  }
-  if (TS > 1) reinterpret_cast<float4*>(s_red)[s0 * Q4 + j4] = a4;
-  if (TS > 1) __syncthreads();
-  if (s0 == 0) {
-    float4 o = a4;
-    for (int ts = 1; ts < TS; ++ts) {
-      const float4 y = reinterpret_cast<const float4*>(s_red)[ts * Q4 + j4];
-      o.x += y.x;
-      o.y += y.y;
-      o.z += y.z;
-      o.w += y.w;
-    }
-    const float invL = 1.f / s_L[hq];
-    const uint32_t b0 = f32_to_bf16_rne(o.x * invL), b1 = f32_to_bf16_rne(o.y * invL);
-    const uint32_t b2 = f32_to_bf16_rne(o.z * invL), b3 = f32_to_bf16_rne(o.w * invL);
-    reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + j4] =
-        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-  }
-}
-
-// Write the step's cache update for one head: the new K/V row, slot keys
-// and position, the window ring and the control block (whose least
-// important key is the minimum of the s_mk/s_ms entries).
-template <int D, int G>
-__device__ __forceinline__ void update_cache(const DecodeParams& p, int head, const Decision& dc,
-                                             const uint4 (&knew)[2], const uint4 (&vnew)[2],
-                                             int32_t ring_next, const uint64_t* s_mk,
-                                             const int32_t* s_ms) {
-  constexpr int NWAVE = 256 / WAVE;
-  constexpr int R16 = WAVE / 16;
+// The slot-side part of the step's cache update: the new K/V row, the keys
+// of the two slots that change, the new position and its window ring entry.
+// Every workgroup of the step substitutes these values for the slots they
+// concern, so they are written as soon as the decision is known (by one
+// workgroup of the head).  lane < D/16 holds pieces lane and lane + D/16 of
+// the new row.
+template <int D>
+__device__ __forceinline__ void write_slot_update(const DecodeParams& p, int head,
+                                                  const Decision& dc, const uint4& kn0,
+                                                  const uint4& kn1, const uint4& vn0,
+                                                  const uint4& vn1) {
   constexpr int LPR = D / 16;
   constexpr int HALF4 = D / 16;
   constexpr int ROW4 = D / 8;
   const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1);
   const int64_t hrow = static_cast<int64_t>(head) * p.budget;
-  const int32_t W = p.n_recent;
-  if (tid < LPR) {  // lane tid holds chunks tid and tid + D/16 of the new row
+  if (tid < LPR) {
     uint4* kw = reinterpret_cast<uint4*>(p.kc) + (hrow + dc.newslot) * ROW4 + tid;
     uint4* vw = reinterpret_cast<uint4*>(p.vc) + (hrow + dc.newslot) * ROW4 + tid;
-    kw[0] = knew[0];
-    kw[HALF4] = knew[1];
-    vw[0] = vnew[0];
-    vw[HALF4] = vnew[1];
+    kw[0] = kn0;
+    kw[HALF4] = kn1;
+    vw[0] = vn0;
+    vw[HALF4] = vn1;
   }
-  if (tid < WAVE) {
-    uint64_t k0 = KEY_NONE;
-    int32_t sl0 = 0x7FFFFFFF;
-    if (lane < NWAVE * R16) {
-      k0 = s_mk[lane];
-      sl0 = s_ms[lane];
-    }
-    wave_min_key_dpp(k0, sl0);
-    if (lane == 0) {
-      const int32_t n = dc.n;
-      if (dc.admitted) p.keys[hrow + dc.st] = dc.keyt;
-      p.keys[hrow + dc.newslot] = KEY_NONE;
-      p.pos[hrow + dc.newslot] = n;
-      if (n >= p.n_sink) p.ring[static_cast<int64_t>(head) * W + (n % W)] = dc.newslot;
-      HeadCtl nc;
-      nc.n = n;
-      nc.count = dc.count_new;
-      nc.nscored = dc.nscored_new;
-      nc.minslot = (k0 == KEY_NONE) ? -1 : sl0;
-      nc.minkey = k0;
-      nc.flags = dc.flags;
-      // with a one-token window the next leaving token is the one just added
-      nc.leave_slot = (n + 1 - W < p.n_sink) ? -1 : (W == 1 ? dc.newslot : ring_next);
-      p.ctl[head] = nc;
-      p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE] = 0u;
+  if (tid == 0) {
+    if (dc.admitted) p.keys[hrow + dc.st] = dc.keyt;
+    p.keys[hrow + dc.newslot] = KEY_NONE;
+    p.pos[hrow + dc.newslot] = dc.n;
+    if (dc.n >= p.n_sink) p.ring[static_cast<int64_t>(head) * p.n_recent + (dc.n % p.n_recent)] =
+        dc.newslot;
+  }
+}
+
+// The control block after the step.  Thread 0 writes every field but
+// minslot; minslot is written by the thread that holds the least important
+// key (-1 by thread 0 when no scored token is held).
+__device__ __forceinline__ void write_ctl(const DecodeParams& p, int head, const Decision& dc,
+                                          uint64_t minkey, int32_t leave_next, bool zero_thread,
+                                          bool holds_min, int32_t minslot) {
+  HeadCtl* c = p.ctl + head;
+  if (zero_thread) {
+    c->n = dc.n;
+    c->count = dc.count_new;
+    c->nscored = dc.nscored_new;
+    c->minkey = minkey;
+    c->flags = dc.flags;
+    c->leave_slot = leave_next;
+    if (minkey == KEY_NONE) c->minslot = -1;
+  }
+  if (holds_min && minkey != KEY_NONE) c->minslot = minslot;
+}
+
+// Slot of the next token to leave the window, for the new control block.
+__device__ __forceinline__ int32_t next_leave_slot(const Decision& dc, int32_t ring_next,
+                                                   int32_t n_sink, int32_t W) {
+  // with a one-token window the next leaving token is the one just added
+  return (dc.n + 1 - W < n_sink) ? -1 : (W == 1 ? dc.newslot : ring_next);
+}
+
+// Window ring entry of the token that leaves at the next step (read by the
+// workgroup that writes the control block).
+__device__ __forceinline__ int32_t read_ring_next(const DecodeParams& p, int head,
+                                                  const Decision& dc) {
+  const int32_t W = p.n_recent;
+  if (W == 1 || dc.n + 1 - W < p.n_sink) return -1;
+  return p.ring[static_cast<int64_t>(head) * W + ((dc.n + 1) % W)];
+}
+
+// LDS of the split merge.
+struct FinishLds {
+  float f[8][MAX_SPLITS];  // [head of the group][split] rescale factor (0 past nsplit)
+  float L[8];              // [head] merged softmax sum
+  uint64_t wmin[4];        // [wave] least important key of the splits it read
+};
+
+// Merge the nsplit partial states of `head` into its bf16 output rows and
+// write the new control block.  Called by all 256 threads of one workgroup.
+// COHERENT: read the partials with SC1 loads (in-launch ticket; the second
+// launch reads after the launch boundary).  Every thread owns FPT
+// consecutive output columns and issues one load per split for them, all
+// before the first wait; loads past the last split fall outside the buffer
+// descriptors' ranges and read 0, so no load needs a branch.  The splits'
+// (max, sum) pairs are turned into per-split factors by one wavefront per
+// query head.
+template <int D, int G, bool COHERENT>
+__device__ __forceinline__ void finish_head(const DecodeParams& p, int head, const Decision& dc,
+                                            int32_t ring_next, FinishLds& fl) {
+  constexpr int NT = 256;
+  constexpr int NWAVE = NT / WAVE;
+  constexpr int GD = G * D;
+  constexpr int FPT = GD >= NT ? GD / NT : 1;
+  constexpr int NACT = GD / FPT;
+  constexpr int MB = 32;                 // splits loaded per batch
+  constexpr int SPL = MAX_SPLITS / WAVE;
+  constexpr int HPW = (G + NWAVE - 1) / NWAVE;  // query heads per wave
+  constexpr int CP = COHERENT ? CPOL_SC1 : 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wid = tid / WAVE;
+  const int ns = p.nsplit;
+  const int64_t p0 = static_cast<int64_t>(head) * ns;
+  const int32_t W = p.n_recent;
+
+  const __amdgpu_buffer_rsrc_t r_acc = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_acc + p0 * GD, 0, ns * GD * 4, BUF_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t r_ml = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_ml + p0 * G * 2, 0, ns * G * 8, BUF_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t r_min = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_min + p0, 0, ns * 16, BUF_RSRC_WORD3);
+
+  // ---- issue the loads: key minima, (max, sum) pairs, the first batch of
+  // accumulators, and the ring entry of the next leaving token
+  const u32x2_t kraw = __builtin_amdgcn_raw_buffer_load_b64(r_min, tid * 16, 0, CP);
+  const uint32_t sraw = __builtin_amdgcn_raw_buffer_load_b32(r_min, tid * 16 + 8, 0, CP);
+  u32x2_t ml[HPW][SPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = wid + hh * NWAVE;
+    if (h < G) {  // uniform
+#pragma unroll
+      for (int u = 0; u < SPL; ++u)
+        ml[hh][u] = __builtin_amdgcn_raw_buffer_load_b64(r_ml, ((lane + u * WAVE) * G + h) * 8, 0, CP);
     }
   }
+  float raw[MB][FPT];
+  auto load_batch = [&](int sb) {
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const uint32_t off = static_cast<uint32_t>(((sb + u) * GD + tid * FPT) * 4);
+      if constexpr (FPT == 4) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r_acc, off, 0, CP);
+        raw[u][0] = __uint_as_float(v.x);
+        raw[u][1] = __uint_as_float(v.y);
+        raw[u][2] = __uint_as_float(v.z);
+        raw[u][3] = __uint_as_float(v.w);
+      } else if constexpr (FPT == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r_acc, off, 0, CP);
+        raw[u][0] = __uint_as_float(v.x);
+        raw[u][1] = __uint_as_float(v.y);
+      } else {
+        raw[u][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_acc, off, 0, CP));
+      }
+    }
+  };
+  load_batch(0);
+
+  // ---- per query head: M = max of the splits' maxima, factor 2^(m_s - M)
+  // (0 past the last split), merged sum
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = wid + hh * NWAVE;
+    if (h < G) {  // uniform
+      float mv[SPL];
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        mv[u] = (lane + u * WAVE < ns) ? __uint_as_float(ml[hh][u].x) : -INFINITY;
+        M = fmaxf(M, mv[u]);
+      }
+      M = wave_max(M);
+      const float Ms = (M == -INFINITY) ? 0.f : M;
+      float Lsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        const float f = fast_exp2(mv[u] - Ms);
+        fl.f[h][lane + u * WAVE] = f;
+        Lsum = fmaf(__uint_as_float(ml[hh][u].y), f, Lsum);
+      }
+      Lsum = wave_sum(Lsum);
+      if (lane == 0) fl.L[h] = Lsum;
+    }
+  }
+  // ---- the least important key over the splits (keys are unique)
+  const uint64_t mkey = tid < ns ? (static_cast<uint64_t>(kraw.y) << 32) | kraw.x : KEY_NONE;
+  {
+    const uint64_t wm = wave_min_u64(mkey);
+    if (lane == 0) fl.wmin[wid] = wm;
+  }
+  __syncthreads();
+
+  // ---- accumulate this thread's columns over the splits
+  const bool act = tid < NACT;
+  const int hq = act ? (tid * FPT) / D : 0;
+  float a[FPT];
+#pragma unroll
+  for (int j = 0; j < FPT; ++j) a[j] = 0.f;
+  for (int sb = 0; sb < ns; sb += MB) {
+    if (sb > 0) load_batch(sb);
+#pragma unroll
+    for (int u = 0; u < MB; u += 4) {
+      const float4 f4 = *reinterpret_cast<const float4*>(&fl.f[hq][sb + u]);
+      const float fu[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int j = 0; j < FPT; ++j) a[j] = fmaf(raw[u + k][j], fu[k], a[j]);
+    }
+  }
+  if (act) {
+    const float invL = 1.f / fl.L[hq];
+    uint16_t* o = p.out + static_cast<int64_t>(head) * GD + tid * FPT;
+    if constexpr (FPT == 1) {
+      *o = static_cast<uint16_t>(f32_to_bf16_rne(a[0] * invL));
+    } else {
+      uint32_t w[FPT / 2];
+#pragma unroll
+      for (int j = 0; j < FPT / 2; ++j)
+        w[j] = f32_to_bf16_rne(a[2 * j] * invL) | (f32_to_bf16_rne(a[2 * j + 1] * invL) << 16);
+      if constexpr (FPT == 2) *reinterpret_cast<uint32_t*>(o) = w[0];
+      else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+    }
+  }
+  const uint64_t minkey = min_u64(min_u64(fl.wmin[0], fl.wmin[1]), min_u64(fl.wmin[2], fl.wmin[3]));
+  write_ctl(p, head, dc, minkey, next_leave_slot(dc, ring_next, p.n_sink, W), tid == 0,
+            mkey == minkey, static_cast<int32_t>(sraw));
+  if (tid == 0) p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE] = 0u;
 }
 
 // One workgroup of 256 threads per (KV head, split).  K/V rows stream
@@ -475,26 +526,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int CHUNK = NP * RPP;        // rows per chunk
   static_assert(CHUNK <= NT, "one key per thread per chunk");
   constexpr int NWAVE = NT / WAVE;
-  constexpr int R16 = WAVE / 16;         // 16-lane DPP rows per wavefront
   constexpr int ACC = 16;                // accumulators per head per lane
-  constexpr int Q4 = G * D / 4;          // float4s in one split's accumulator
-  static_assert(Q4 <= NT, "one thread per float4 of the accumulator");
-  // LDS: per (wave, DPP row, lane-in-group) the G x 16 accumulators, each
-  // block padded by 8 floats so that neighbouring lanes' blocks start in
-  // different LDS banks; the finishing workgroup reuses it for the split merge
-  constexpr int ACC_STRIDE = G * ACC + 8;
-  constexpr int LDS_ROWS = NWAVE * R16 * LPR * ACC_STRIDE;
-  constexpr int LDS_MERGE = MAX_SPLITS * G + (NT / Q4) * G * D;
-  static_assert(NWAVE * R16 <= WAVE, "key minima of the workgroup fit one wavefront");
-  constexpr int LDS_F = LDS_ROWS > LDS_MERGE ? LDS_ROWS : LDS_MERGE;
+  constexpr int NV = G * ACC;            // accumulators per lane
+  constexpr int RGW = WAVE / LPR;        // row groups per wavefront (8 or 16)
+  constexpr int NVF = NV / RGW;          // accumulators per lane after the wave reduction
+  constexpr int GD = G * D;
+  constexpr int FPT = GD >= NT ? GD / NT : 1;  // output columns per thread in the combine
+  constexpr int NACT = GD / FPT;
+  constexpr int ROW4 = D / 8;            // uint4 per row
 
-  __shared__ __align__(16) float s_buf[LDS_F];
-  __shared__ float s_wm[NWAVE][G];       // wave max (log2 units)
-  __shared__ float s_wl[NWAVE][R16][G];  // per DPP-row sums of p
-  __shared__ float s_L[G];
-  __shared__ uint64_t s_mk[NWAVE * R16];
-  __shared__ int32_t s_ms[NWAVE * R16];
+  __shared__ __align__(16) float s_wacc[NWAVE][GD];   // each wave's accumulators
+  __shared__ float2 s_wml[NWAVE][G];                  // each wave's (max, sum)
+  __shared__ uint64_t s_wmin[NWAVE];                  // each wave's least important key
   __shared__ int32_t s_last;
+  __shared__ __align__(16) FinishLds s_fin;
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wid = tid / WAVE;
@@ -525,15 +570,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int rg = tid / LPR;
   const int cc = tid % LPR;
   const int64_t hrow = static_cast<int64_t>(head) * p.budget;
-  constexpr int ROW4 = D / 8;            // uint4 per row
   const uint4* kb = reinterpret_cast<const uint4*>(p.kc) + hrow * ROW4 + cc;
   const uint4* vb = reinterpret_cast<const uint4*>(p.vc) + hrow * ROW4 + cc;
   const uint64_t* kyb = p.keys + hrow;
 
-  // Load the K/V rows and keys of the chunk starting at slot b.  The loads
-  // are unconditional (rows past the slot range read slot 0, and compute
-  // masks them), so every chunk issues the same number of loads and the
-  // compiler can wait for one chunk while the next is still in flight.
+  // Load the K/V rows and keys of the chunk starting at slot b.  Rows past
+  // the slot range read slot 0 (compute masks them).
   auto load_chunk = [&](uint4 (&kk)[NP][2], uint4 (&vv)[NP][2], uint64_t& key, int32_t b) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -561,14 +603,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     qv[h][0] = qp[0];
     qv[h][1] = qp[HALF4];
   }
-
   // ---- eviction decision, identical in every workgroup of the head -------
   const Decision dc = decide(c, sg, p.n_sink, p.n_scored, W);
   const int32_t newslot = dc.newslot, count_new = dc.count_new, st = dc.st;
   const bool admitted = dc.admitted;
   const uint64_t keyt = dc.keyt;
-  // slot of the next token to leave (needed by the cache update)
-  const int32_t ring_next = p.ring[static_cast<int64_t>(head) * W + ((dc.n + 1) % W)];
+  if (split == 0) write_slot_update<D>(p, head, dc, knew0, knew1, vnew0, vnew1);
+  // the next leaving token's slot (for the control block), read while the
+  // K/V loads are in flight; only the workgroup that finishes uses it
+  const int32_t ring_next = read_ring_next(p, head, dc);
 
   // ---- attention over slots [lo, hi) --------------------------------------
   const int32_t hi = min(lo + p.rows_per_split, count_new);
@@ -659,7 +702,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       for (int h = 0; h < G; ++h) {
         const float ms = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
         float2_t pf = {fast_exp2(x[i][h] - ms), fast_exp2(x[i + 1][h] - ms)};
-        ph[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2v_t));
+        ph[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2_t));
         l_run[h] = dot2_bf16(ph[h], BF16_ONE_PAIR, l_run[h]);
       }
 #pragma unroll
@@ -680,183 +723,208 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
   };
 
-  // ping-pong over chunks: load the next chunk while computing this one
-  // (also after the last one, so that the load count never depends on the
-  // path taken)
-  for (int32_t base = lo; base < hi;) {
-    load_chunk(kB, vB, keyB, base + CHUNK);
-    compute_chunk(kA, vA, keyA, base);
-    base += CHUNK;
-    if (base >= hi) break;
-    load_chunk(kA, vA, keyA, base + CHUNK);
-    compute_chunk(kB, vB, keyB, base);
-    base += CHUNK;
+  // Chunks.  A split of at most two chunks (batch 1) requests both at once
+  // and computes them in order, so no load is left in flight after the
+  // last one.  Longer splits ping-pong: the next chunk's loads are issued
+  // before the current one is computed (and after the last, whose loads
+  // read slot 0), so the load count never depends on the path taken and
+  // the compiler's wait for the current chunk counts exactly the loads
+  // issued after it.
+  const int32_t nch = hi > lo ? (hi - lo + CHUNK - 1) / CHUNK : 0;
+  if (nch <= 2) {
+    load_chunk(kB, vB, keyB, lo + CHUNK);
+    if (nch > 0) compute_chunk(kA, vA, keyA, lo);
+    if (nch > 1) compute_chunk(kB, vB, keyB, lo + CHUNK);
+  } else {
+    for (int32_t base = lo; base < hi;) {
+      load_chunk(kB, vB, keyB, base + CHUNK);
+      compute_chunk(kA, vA, keyA, base);
+      base += CHUNK;
+      if (base >= hi) break;
+      load_chunk(kA, vA, keyA, base + CHUNK);
+      compute_chunk(kB, vB, keyB, base);
+      base += CHUNK;
+    }
   }
 
-  // ---- merge the row groups of the workgroup -----------------------------
-  // Key minimum: DPP inside each 16-lane row, one LDS entry per row.
-  const int r16 = lane / 16;
-  row16_min_key(mk, msl);
-  if (lane % 16 == 0) {
-    s_mk[wid * R16 + r16] = mk;
-    s_ms[wid * R16 + r16] = msl;
-  }
-  // Accumulators: all row groups of a wave share m_run, so they add plainly;
-  // DPP sums the groups of each 16-lane row, LDS takes one copy per row.
-  const bool writer = (lane % 16) < LPR;  // first row group of the DPP row
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float lsum = row16_sum_groups<LPR>(l_run[h]);
-    if (lane % 16 == 0) s_wl[wid][r16][h] = lsum;
-    if (lane == 0) s_wm[wid][h] = m_run[h];
-#pragma unroll
-    for (int e = 0; e < ACC; ++e) acc[h][e] = row16_sum_groups<LPR>(acc[h][e]);
-  }
-  if (writer) {
-    float4* dst = reinterpret_cast<float4*>(&s_buf[((wid * R16 + r16) * LPR + cc) * ACC_STRIDE]);
+  // ---- reduce the workgroup to one softmax state ---------------------------
+  // Inside each wave: the row groups share m_run, so their accumulators add
+  // plainly.  The transposing pair reductions leave lane l with NVF
+  // consecutive accumulator indices [NVF * (l / LPR), +NVF) of its column
+  // slot cc, summed over all row groups of the wave.
+  {
+    float v[NV];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < ACC; e += 4)
-        dst[(h * ACC + e) / 4] = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+      for (int e = 0; e < ACC; ++e) v[h * ACC + e] = acc[h][e];
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) v[i] = swap32_add(v[i], v[i + NV / 2]);
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i) v[i] = swap16_add(v[i], v[i + NV / 4]);
+    const bool b3 = (lane >> 3) & 1;
+#pragma unroll
+    for (int i = 0; i < NV / 8; ++i) v[i] = xor8_add(v[i], v[i + NV / 8], b3);
+    if constexpr (LPR == 4) {
+      const bool b2 = (lane >> 2) & 1;
+#pragma unroll
+      for (int i = 0; i < NV / 16; ++i) v[i] = xor4_add(v[i], v[i + NV / 16], b2);
+    }
+    // accumulator index vi = h * 16 + e holds column (e / 8) * D/2 + 8 cc + e % 8
+    const int vb = NVF * (lane / LPR);
+#pragma unroll
+    for (int i = 0; i < NVF; i += (NVF >= 4 ? 4 : NVF)) {
+      const int vi = vb + i;
+      const int h = vi / ACC, e = vi % ACC;
+      float* dst = &s_wacc[wid][h * D + (e / 8) * (D / 2) + 8 * cc + e % 8];
+      if constexpr (NVF >= 4) *reinterpret_cast<float4*>(dst) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+      else if constexpr (NVF == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[i], v[i + 1]);
+      else *dst = v[i];
+    }
+    // each wave's sum of p: l_run is the same in the LPR lanes of a row group
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float l = swap32_add(l_run[h], l_run[h]);
+      l = swap16_add(l, l);
+      l += dpp_f<DPP_ROW_ROR8>(l);
+      if constexpr (LPR == 4) l += __shfl_xor(l, 4, WAVE);
+      if (lane == 0) s_wml[wid][h] = make_float2(m_run[h], l);
+    }
+  }
+  {
+    const uint64_t wm = wave_min_u64(mk);
+    if (lane == 0) s_wmin[wid] = wm;
   }
   __syncthreads();
-  const int64_t pidx = static_cast<int64_t>(head) * p.nsplit + split;
-  const bool single = (p.nsplit == 1);  // uniform
-  // Each thread forms 4 consecutive outputs (same lane slot, same head):
-  // element d of head h sits at lane (d mod D/2)/8, accumulator 8*(2d/D) + d%8.
-  for (int o4 = tid; o4 < Q4; o4 += NT) {
-    const int h = (o4 * 4) / D;
-    const int d = (o4 * 4) % D;
-    const int cl = (d % (D / 2)) / 8;
-    const int j = (d / (D / 2)) * 8 + d % 8;
-    float M = s_wm[0][h];
-#pragma unroll
-    for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, s_wm[w][h]);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f;
+
+  // ---- combine the waves: thread t owns columns [t * FPT, +FPT) ------------
+  const uint64_t wg_minkey = min_u64(min_u64(s_wmin[0], s_wmin[1]), min_u64(s_wmin[2], s_wmin[3]));
+  const bool holds_min = (mk == wg_minkey);  // only meaningful for a real key
+  const bool act = tid < NACT;
+  const int hq = (tid * FPT) / D;
+  float a[FPT];
+  float M = -INFINITY, Lsum = 0.f;
+  {
+    float2 wml[NWAVE];
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) {
-      const float f = fast_exp2(s_wm[w][h] - Ms);
+      wml[w] = s_wml[w][act ? hq : 0];
+      M = fmaxf(M, wml[w].x);
+    }
+    const float Ms = (M == -INFINITY) ? 0.f : M;
 #pragma unroll
-      for (int r = 0; r < R16; ++r) {
-        const float4 v = *reinterpret_cast<const float4*>(
-            &s_buf[((w * R16 + r) * LPR + cl) * ACC_STRIDE + h * ACC + j]);
-        a.x = fmaf(v.x, f, a.x);
-        a.y = fmaf(v.y, f, a.y);
-        a.z = fmaf(v.z, f, a.z);
-        a.w = fmaf(v.w, f, a.w);
-        L = fmaf(s_wl[w][r][h], f, L);
+    for (int j = 0; j < FPT; ++j) a[j] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      const float f = fast_exp2(wml[w].x - Ms);
+      Lsum = fmaf(wml[w].y, f, Lsum);
+      const float* src = &s_wacc[w][act ? tid * FPT : 0];
+      float xs[FPT];
+      if constexpr (FPT == 4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(src);
+        xs[0] = t4.x; xs[1] = t4.y; xs[2] = t4.z; xs[3] = t4.w;
+      } else if constexpr (FPT == 2) {
+        const float2 t2 = *reinterpret_cast<const float2*>(src);
+        xs[0] = t2.x; xs[1] = t2.y;
+      } else {
+        xs[0] = *src;
       }
-    }
-    if (single) {  // the only split: normalise and store the output row
-      const float invL = 1.f / L;
-      const uint32_t b0 = f32_to_bf16_rne(a.x * invL), b1 = f32_to_bf16_rne(a.y * invL);
-      const uint32_t b2 = f32_to_bf16_rne(a.z * invL), b3 = f32_to_bf16_rne(a.w * invL);
-      reinterpret_cast<uint2*>(p.out)[static_cast<int64_t>(head) * Q4 + o4] =
-          make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    } else if (APART) {  // the launch boundary publishes them
-      reinterpret_cast<float4*>(p.part_acc)[pidx * Q4 + o4] = a;
-      if (d == 0) reinterpret_cast<float2*>(p.part_ml)[pidx * G + h] = make_float2(M, L);
-    } else {  // written through to the point of coherence (see the file comment)
-      // One 16-byte store per thread with the write-through cache bit, so a
-      // wavefront writes whole cache lines (four 4-byte atomic stores wrote
-      // each line four times).  The descriptor covers this split's partial.
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          p.part_acc + pidx * Q4 * 4, 0, Q4 * 16, BUF_RSRC_WORD3);
-      const u32x4_t v = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
-                         __float_as_uint(a.w)};
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, o4 * 16, 0, CPOL_SC1);
-      if (d == 0) {
-        float* pm = p.part_ml + (pidx * G + h) * 2;
-        __hip_atomic_store(pm + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(pm + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+#pragma unroll
+      for (int j = 0; j < FPT; ++j) a[j] = fmaf(xs[j], f, a[j]);
     }
   }
-  // Several splits: publish the partial results; the second launch or the
-  // last workgroup of the head to finish merges them.  A single split is
-  // complete already.
-  if (!single) {
-    if (wid == 0) {
-      uint64_t k0 = KEY_NONE;
-      int32_t sl0 = 0x7FFFFFFF;
-      if (lane < NWAVE * R16) {
-        k0 = s_mk[lane];
-        sl0 = s_ms[lane];
-      }
-      wave_min_key_dpp(k0, sl0);
-      if (lane == 0 && APART) {
-        MinPart mp;
-        mp.key = k0;
-        mp.slot = sl0;
-        mp.pad = ring_next;  // read by the finishing launch
-        p.part_min[pidx] = mp;
-      } else if (lane == 0) {
-        __hip_atomic_store(&p.part_min[pidx].key, k0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.part_min[pidx].slot, sl0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    if (APART) return;
 
-    // ---- ticket: the last workgroup of the head finishes the step ----------
-    // Every thread's write-through stores are acknowledged before thread 0
-    // takes the ticket; the finisher's acquire invalidates its L2.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev =
-          __hip_atomic_fetch_add(&p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
+  if (p.nsplit == 1) {  // uniform: the only split; output and control block here
+    if (act) {
+      const float invL = 1.f / Lsum;
+      uint16_t* o = p.out + static_cast<int64_t>(head) * GD + tid * FPT;
+      if constexpr (FPT == 1) {
+        *o = static_cast<uint16_t>(f32_to_bf16_rne(a[0] * invL));
+      } else {
+        uint32_t w[FPT / 2];
+#pragma unroll
+        for (int j = 0; j < FPT / 2; ++j)
+          w[j] = f32_to_bf16_rne(a[2 * j] * invL) | (f32_to_bf16_rne(a[2 * j + 1] * invL) << 16);
+        if constexpr (FPT == 2) *reinterpret_cast<uint32_t*>(o) = w[0];
+        else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+      }
     }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    merge_splits<D, G>(p, head, s_buf, s_L, s_mk, s_ms);
+    write_ctl(p, head, dc, wg_minkey, next_leave_slot(dc, ring_next, p.n_sink, W), tid == 0,
+              holds_min, msl);
+    return;
   }
 
-  // ---- cache update: new row, slot metadata, window ring, control block --
-  const uint4 knew[2] = {knew0, knew1}, vnew[2] = {vnew0, vnew1};
-  update_cache<D, G>(p, head, dc, knew, vnew, ring_next, s_mk, s_ms);
+  // ---- several splits: publish this split's partial state -----------------
+  const int64_t pidx = static_cast<int64_t>(head) * p.nsplit + split;
+  {
+    constexpr int CP = APART ? 0 : CPOL_SC1;  // the launch boundary publishes for APART
+    const __amdgpu_buffer_rsrc_t r_acc =
+        __builtin_amdgcn_make_buffer_rsrc(p.part_acc + pidx * GD, 0, GD * 4, BUF_RSRC_WORD3);
+    if (act) {
+      const uint32_t off = static_cast<uint32_t>(tid * FPT * 4);
+      if constexpr (FPT == 4)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                    __float_as_uint(a[3])}, r_acc, off, 0, CP);
+      else if constexpr (FPT == 2)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(a[0]), __float_as_uint(a[1])},
+                                              r_acc, off, 0, CP);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a[0]), r_acc, off, 0, CP);
+      if ((tid * FPT) % D == 0) {
+        const __amdgpu_buffer_rsrc_t r_ml =
+            __builtin_amdgcn_make_buffer_rsrc(p.part_ml + pidx * G * 2, 0, G * 8, BUF_RSRC_WORD3);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(M), __float_as_uint(Lsum)},
+                                              r_ml, hq * 8, 0, CP);
+      }
+    }
+    // key minimum of the split: key by thread 0, slot by the thread holding it
+    const __amdgpu_buffer_rsrc_t r_min =
+        __builtin_amdgcn_make_buffer_rsrc(p.part_min + pidx, 0, 16, BUF_RSRC_WORD3);
+    if (tid == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(
+          u32x2_t{static_cast<uint32_t>(wg_minkey), static_cast<uint32_t>(wg_minkey >> 32)}, r_min, 0,
+          0, CP);
+    if (holds_min && wg_minkey != KEY_NONE)
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(msl), r_min, 8, 0, CP);
+  }
+  if (APART) return;
+
+  // ---- ticket: the last workgroup of the head finishes the step ------------
+  // Every thread's write-through stores are acknowledged before thread 0
+  // takes the ticket.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(
+        &p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE], 1u, __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  finish_head<D, G, true>(p, head, dc, ring_next, s_fin);
 }
 
 // Second launch of a step with several splits: one workgroup per KV head
-// merges the splits' partial results into the output and writes the cache
-// update.  The launch boundary orders it after every read of the first
-// launch, so no ticket or release is needed.  All of its loads (control
-// block, score, new row, partials) are independent and issued together.
+// merges the splits' partial results into the output and writes the control
+// block.  The launch boundary orders it after every access of the first
+// launch, so no ticket is needed.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
-  constexpr int NWAVE = 256 / WAVE;
-  constexpr int R16 = WAVE / 16;
-  constexpr int LPR = D / 16;
-  constexpr int HALF4 = D / 16;
-  constexpr int ROW4 = D / 8;
-  constexpr int TS = 256 / (G * D / 4);
-  __shared__ __align__(16) float s_buf[MAX_SPLITS * G + TS * G * D];
-  __shared__ float s_L[G];
-  __shared__ uint64_t s_mk[NWAVE * R16];
-  __shared__ int32_t s_ms[NWAVE * R16];
+  __shared__ __align__(16) FinishLds s_fin;
   const int head = blockIdx.x;
-  const int cc = threadIdx.x % LPR;
   const HeadCtl c = p.ctl[head];
   const float sg = p.score_leaving[head];
-  const int32_t ring_next = p.part_min[static_cast<int64_t>(head) * p.nsplit].pad;
-  const uint4* knp = reinterpret_cast<const uint4*>(p.k_new) + static_cast<int64_t>(head) * ROW4 + cc;
-  const uint4* vnp = reinterpret_cast<const uint4*>(p.v_new) + static_cast<int64_t>(head) * ROW4 + cc;
-  const uint4 knew[2] = {knp[0], knp[HALF4]};
-  const uint4 vnew[2] = {vnp[0], vnp[HALF4]};
-  merge_splits<D, G>(p, head, s_buf, s_L, s_mk, s_ms);
   const Decision dc = decide(c, sg, p.n_sink, p.n_scored, p.n_recent);
-  update_cache<D, G>(p, head, dc, knew, vnew, ring_next, s_mk, s_ms);
+  finish_head<D, G, false>(p, head, dc, read_ring_next(p, head, dc), s_fin);
 }
 
 template <int D, int G>
-hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
+hipError_t launch_one(const DecodeParams& prm, bool apart, int64_t blocks, hipStream_t stream) {
   // The instance with the in-launch merge runs only where it merges; one
   // split per head and the second-launch finish use the one without it.
-  if (prm.nsplit > 1 && !prm.finish_apart) {
+  if (prm.nsplit > 1 && !apart) {
     hipLaunchKernelGGL((decode_kernel<D, G, false>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(256), 0, stream, prm);
     return hipGetLastError();
@@ -864,19 +932,20 @@ hipError_t launch_one(const DecodeParams& prm, int64_t blocks, hipStream_t strea
   hipLaunchKernelGGL((decode_kernel<D, G, true>), dim3(static_cast<uint32_t>(blocks)), dim3(256),
                      0, stream, prm);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !prm.finish_apart) return e;
+  if (e != hipSuccess || prm.nsplit == 1) return e;
   hipLaunchKernelGGL((decode_finish_kernel<D, G>), dim3(static_cast<uint32_t>(prm.n_heads)),
                      dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int G, const DecodeParams& prm, int64_t blocks, hipStream_t stream) {
+hipError_t launch_d(int G, const DecodeParams& prm, bool apart, int64_t blocks,
+                    hipStream_t stream) {
   switch (G) {
-    case 1: return launch_one<D, 1>(prm, blocks, stream);
-    case 2: return launch_one<D, 2>(prm, blocks, stream);
-    case 4: return launch_one<D, 4>(prm, blocks, stream);
-    case 8: return launch_one<D, 8>(prm, blocks, stream);
+    case 1: return launch_one<D, 1>(prm, apart, blocks, stream);
+    case 2: return launch_one<D, 2>(prm, apart, blocks, stream);
+    case 4: return launch_one<D, 4>(prm, apart, blocks, stream);
+    case 8: return launch_one<D, 8>(prm, apart, blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -892,9 +961,9 @@ bool decode_shape_supported(int head_dim, int group, int threads, int rows_per_t
 }
 
 hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeWork& work,
-                         const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
-                         const float* score_leaving, uint16_t* out, float scale_log2e,
-                         hipStream_t stream) {
+                         int32_t n_layers, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, const float* score_leaving, uint16_t* out,
+                         float scale_log2e, hipStream_t stream) {
   DecodeParams prm;
   prm.q = q;
   prm.k_new = k_new;
@@ -911,23 +980,23 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
   prm.part_ml = work.part_ml;
   prm.part_min = work.part_min;
   prm.tickets = work.tickets;
-  prm.n_heads = geo.batch * geo.n_kv_heads;
+  prm.n_heads = n_layers * geo.batch * geo.n_kv_heads;
   prm.budget = geo.budget;
   prm.n_sink = geo.n_sink;
   prm.n_scored = geo.n_scored + geo.slack;  // the Dynamic backend grows into its slack
   prm.n_recent = geo.n_recent;
   prm.nsplit = work.nsplit;
   prm.rows_per_split = work.rows_per_split;
-  prm.finish_apart = (work.nsplit > 1 && work.finish_apart) ? 1 : 0;
   prm.scale_log2e = scale_log2e;
   const int G = geo.n_q_heads / geo.n_kv_heads;
-  if (work.nsplit < 1 || work.nsplit > MAX_SPLITS ||
+  if (n_layers < 1 || work.nsplit < 1 || work.nsplit > MAX_SPLITS ||
       int64_t(work.nsplit) * work.rows_per_split < geo.budget ||
       !decode_shape_supported(geo.head_dim, G, work.threads, work.rows_per_thread))
     return hipErrorInvalidValue;
+  const bool apart = work.nsplit > 1 && work.finish_apart;
   const int64_t blocks = static_cast<int64_t>(prm.n_heads) * work.nsplit;
-  if (geo.head_dim == 128) return launch_d<128>(G, prm, blocks, stream);
-  return launch_d<64>(G, prm, blocks, stream);
+  if (geo.head_dim == 128) return launch_d<128>(G, prm, apart, blocks, stream);
+  return launch_d<64>(G, prm, apart, blocks, stream);
 }
 
 }  // namespace kvpop

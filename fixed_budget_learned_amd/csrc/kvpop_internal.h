@@ -63,9 +63,9 @@ constexpr int TICKET_STRIDE = 64;
 
 // Decode workspace, shared by every layer (calls are stream-ordered).
 struct DecodeWork {
-  float* part_acc;     // [B*Hkv][nsplit][2][G*D/4] float2: (x, y) pairs, then (z, w)
-  float* part_ml;      // [B*Hkv][nsplit][G][2]  (running max in log2 units, sum)
-  MinPart* part_min;   // [B*Hkv][nsplit]
+  float* part_acc;     // [heads][nsplit][G*D] unnormalised accumulators
+  float* part_ml;      // [heads][nsplit][G][2]  (running max in log2 units, sum)
+  MinPart* part_min;   // [heads][nsplit]  least important key of the split and its slot
   uint32_t* tickets;   // [B*Hkv][TICKET_STRIDE], element 0 used; zero between calls
   int32_t nsplit;
   int32_t rows_per_split;
@@ -124,10 +124,14 @@ hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uin
 int decode_max_splits();
 bool decode_shape_supported(int head_dim, int group, int threads, int rows_per_thread);
 
+// One decode step of n_layers consecutive layers starting at lv (their heads
+// are contiguous in the cache), in one launch; q/k_new/v_new/score_leaving/
+// out carry a leading layer dimension.  The workspace must hold
+// n_layers * batch * Hkv heads of partials.
 hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeWork& work,
-                         const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
-                         const float* score_leaving, uint16_t* out, float scale_log2e,
-                         hipStream_t stream);
+                         int32_t n_layers, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, const float* score_leaving, uint16_t* out,
+                         float scale_log2e, hipStream_t stream);
 // Dynamic backend: cut every head of the layer whose scored region holds
 // more than n_scored tokens back to its top n_scored, compacting the rows
 // into [0, count).  slack <= PRUNE_SLACK_MAX.

@@ -17,14 +17,14 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvpop.so")
 
-KVPOP_OK, KVPOP_EINVAL, KVPOP_ENOMEM, KVPOP_EHIP, KVPOP_ESTATE = 0, -1, -2, -3, -4
+KVPOP_OK, KVPOP_EINVAL, KVPOP_ENOMEM, KVPOP_EHIP, KVPOP_ESTATE, KVPOP_ERANGE = 0, -1, -2, -3, -4, -5
 KVPOP_FLAG_NAN_SCORE = 1
 
 EXPORTED = ("kvpop_cache_required_bytes", "kvpop_cache_create", "kvpop_cache_destroy",
             "kvpop_cache_reset", "kvpop_prefill_compact", "kvpop_decode_step",
             "kvpop_cache_state", "kvpop_strerror",
             "kvpop_prefix_thresholds", "kvpop_future_attention_target", "kvpop_cache_prune",
-            "kvpop_prefill_compact_batch")
+            "kvpop_prefill_compact_batch", "kvpop_future_attention_target_noalloc")
 
 
 class KVpopLibraryMissing(RuntimeError):
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.kvpop_prefix_thresholds.restype = ctypes.c_int
     lib.kvpop_future_attention_target.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.kvpop_future_attention_target.restype = ctypes.c_int
+    lib.kvpop_future_attention_target_noalloc.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.kvpop_future_attention_target_noalloc.restype = ctypes.c_int
     lib.kvpop_prefill_compact_batch.argtypes = [vp, i32, ctypes.POINTER(PrefillItem), vp]
     lib.kvpop_prefill_compact_batch.restype = ctypes.c_int
     lib.kvpop_cache_prune.argtypes = [vp, i32, vp]
@@ -258,6 +260,20 @@ class KVpopCache:
         _check(load().kvpop_future_attention_target(self._h, T, qp, kp, wp, yp,
                                                     _stream_ptr(stream)),
                "kvpop_future_attention_target")
+
+    def future_attention_target_noalloc(self, q, k, y, stream=None):
+        """The future-attention target with the library's static workspace
+        instead of a caller-provided one (see the header): q bf16 [Hq][T][D],
+        k bf16 [Hkv][T][D], y float32 [Hkv][T] out."""
+        import torch
+        c = self.cfg
+        T = int(q.shape[1]) if q is not None and q.dim() == 3 else 0
+        qp = _dev_ptr(q, torch.bfloat16, (c.n_q_heads, T, c.head_dim), "q")
+        kp = _dev_ptr(k, torch.bfloat16, (c.n_kv_heads, T, c.head_dim), "k")
+        yp = _dev_ptr(y, torch.float32, (c.n_kv_heads, T), "y")
+        _check(load().kvpop_future_attention_target_noalloc(self._h, T, qp, kp, yp,
+                                                            _stream_ptr(stream)),
+               "kvpop_future_attention_target_noalloc")
 
     def state(self, layer: int, seq: int, stream=None) -> HeadState:
         c = self.cfg

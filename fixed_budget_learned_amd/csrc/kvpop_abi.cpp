@@ -159,6 +159,7 @@ struct kvpop_cache {
   bool poisoned = false;
   char* base = nullptr;
   float scale_log2e = 0.f;
+  float* scratch = nullptr;     // this device's static future-target workspace
   std::vector<int32_t> n_host;  // [L][B], newest processed position
   std::vector<int64_t> steps;   // [L] decode steps taken (the Dynamic backend's prune clock)
 
@@ -280,6 +281,12 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
     if (c->owns) (void)hipFree(c->base);
     delete c;
     return KVPOP_EHIP;
+  }
+  // device address of the static workspace of the no-allocation entry
+  // point; without it only that entry point is unavailable
+  if (kvpop::future_scratch_address(&c->scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    c->scratch = nullptr;
   }
   *out = c;
   return KVPOP_OK;
@@ -440,6 +447,30 @@ int kvpop_future_attention_target(kvpop_cache* cache, int32_t n_tokens, const ui
   return KVPOP_OK;
 }
 
+int kvpop_future_attention_target_noalloc(kvpop_cache* cache, int32_t n_tokens,
+                                          const uint16_t* q, const uint16_t* k, float* y,
+                                          void* stream) {
+  if (cache == nullptr || n_tokens < 0) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  if (n_tokens > c.max_positions) return KVPOP_ESTATE;
+  if (size_t(2) * size_t(c.n_q_heads) * size_t(n_tokens) * sizeof(float) >
+      kvpop::FUTURE_SCRATCH_BYTES)
+    return KVPOP_ERANGE;
+  if (n_tokens == 0) return KVPOP_OK;
+  if (q == nullptr || k == nullptr || y == nullptr) return KVPOP_EINVAL;
+  if (cache->scratch == nullptr) return KVPOP_EHIP;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  hipError_t e = kvpop::launch_future_target(cache->geo(), n_tokens, q, k, cache->scale_log2e,
+                                             cache->scratch, y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  return KVPOP_OK;
+}
+
 int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, const float* score_leaving, uint16_t* out,
                       void* stream) {
@@ -544,6 +575,7 @@ const char* kvpop_strerror(int code) {
     case KVPOP_ENOMEM: return "out of device memory or arena too small";
     case KVPOP_EHIP: return "HIP runtime error";
     case KVPOP_ESTATE: return "call out of order, cache poisoned, or position limit reached";
+    case KVPOP_ERANGE: return "input larger than the static workspace of a no-allocation entry point";
     default: return "unknown error";
   }
 }

@@ -34,10 +34,40 @@
 // 8*(r/4) + 4*(l/32) + r%4.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
 namespace kvpop {
+
+// Workspace of kvpop_future_attention_target_noalloc: a static device array
+// (every device the library runs on holds its own copy until the process
+// ends), for callers that cannot allocate.  Host code never passes its name
+// to a kernel: it stands for a host-side shadow, not a device address; the
+// device address comes from future_scratch_address().
+static __device__ __align__(256) float scratch[FUTURE_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t future_scratch_address(float** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static float* addr[MAX_DEVICES] = {};
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(a);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

@@ -119,6 +119,11 @@ hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const
 hipError_t launch_future_target(const Geometry& geo, int32_t n_tokens, const uint16_t* q,
                                 const uint16_t* k, float scale_log2e, float* work, float* y,
                                 hipStream_t stream);
+// Static workspace of the no-allocation future-target entry point, in bytes
+// ([2][Hq][n_tokens] float32 must fit), and its device address on the
+// current device (looked up once per device).
+constexpr size_t FUTURE_SCRATCH_BYTES = size_t(32) << 20;
+hipError_t future_scratch_address(float** ptr);
 // Largest split count the decode kernel accepts, and whether a launch shape
 // (head_dim, group size, workgroup size, rows per thread) is compiled.
 int decode_max_splits();

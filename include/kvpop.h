@@ -69,6 +69,8 @@ extern "C" {
 #define KVPOP_EHIP (-3)   /* HIP runtime or launch error (cache poisoned)   */
 #define KVPOP_ESTATE (-4) /* call out of order, cache poisoned, or position
                              limit reached                                   */
+#define KVPOP_ERANGE (-5) /* input larger than the static workspace of a
+                             no-allocation entry point                       */
 
 /* kvpop_state.flags bits */
 #define KVPOP_FLAG_NAN_SCORE 1 /* a NaN score reached the cache */
@@ -258,6 +260,25 @@ KVPOP_API int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, cons
  * max_positions or poisoned), KVPOP_EHIP. */
 KVPOP_API int kvpop_future_attention_target(kvpop_cache* cache, int32_t n_tokens, const uint16_t* q,
                                             const uint16_t* k, float* work, float* y, void* stream);
+
+/* kvpop_future_attention_target without the workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same inputs, output,
+ * kernels and result as kvpop_future_attention_target, bit for bit; the
+ * [2][Hq][n_tokens] float32 workspace is a static device array of 32 MiB
+ * that the library holds on every device it runs on until the process
+ * ends, so 2 * Hq * n_tokens * 4 bytes must not exceed 32 MiB (Hq = 32:
+ * n_tokens <= 131,072).  The call allocates nothing.  Every call on one
+ * device shares that device's array: calls that overlap on one device (two
+ * streams, or two host threads) race and give undefined results; order
+ * them on one stream.  Nothing in the array needs clearing between calls
+ * (every element read is written first by the same call).  Errors: as
+ * kvpop_future_attention_target, plus KVPOP_ERANGE when the workspace would
+ * exceed the array (checked before anything is enqueued) and KVPOP_EHIP
+ * when the array's device address could not be obtained at cache creation. */
+KVPOP_API int kvpop_future_attention_target_noalloc(kvpop_cache* cache, int32_t n_tokens,
+                                                    const uint16_t* q, const uint16_t* k,
+                                                    float* y, void* stream);
 
 /* Static description of a return code. */
 KVPOP_API const char* kvpop_strerror(int code);

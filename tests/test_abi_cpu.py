@@ -43,18 +43,18 @@ def test_error_codes_match_header():
     text = open(HEADER).read()
     for name, val in (("KVPOP_OK", abi.KVPOP_OK), ("KVPOP_EINVAL", abi.KVPOP_EINVAL),
                       ("KVPOP_ENOMEM", abi.KVPOP_ENOMEM), ("KVPOP_EHIP", abi.KVPOP_EHIP),
-                      ("KVPOP_ESTATE", abi.KVPOP_ESTATE)):
+                      ("KVPOP_ESTATE", abi.KVPOP_ESTATE), ("KVPOP_ERANGE", abi.KVPOP_ERANGE)):
         m = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, text)
         assert m and int(m.group(1)) == val, name
 
 
 def test_strerror_strings(lib):
     seen = set()
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         s = abi.strerror(code)
         assert isinstance(s, str) and s
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7
 
 
 def _cfg(**kw):
@@ -128,3 +128,11 @@ def test_create_without_gpu_reports_hip_error(lib):
     h = ctypes.c_void_p()
     assert lib.kvpop_cache_create(ctypes.byref(c), None, 0, ctypes.byref(h)) == abi.KVPOP_EHIP
     assert h.value is None
+
+
+def test_noalloc_entry_point_validates_before_the_runtime(lib):
+    """The no-allocation future target rejects a NULL cache before touching
+    the HIP runtime (the size limit needs a cache and is checked on the GPU)."""
+    vp = ctypes.c_void_p
+    assert lib.kvpop_future_attention_target_noalloc(None, 16, vp(1), vp(1), vp(1), None) == \
+        abi.KVPOP_EINVAL

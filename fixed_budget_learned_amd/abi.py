@@ -24,7 +24,8 @@ EXPORTED = ("kvpop_cache_required_bytes", "kvpop_cache_create", "kvpop_cache_des
             "kvpop_cache_reset", "kvpop_prefill_compact", "kvpop_decode_step",
             "kvpop_cache_state", "kvpop_strerror",
             "kvpop_prefix_thresholds", "kvpop_future_attention_target", "kvpop_cache_prune",
-            "kvpop_prefill_compact_batch", "kvpop_future_attention_target_noalloc")
+            "kvpop_prefill_compact_batch", "kvpop_future_attention_target_noalloc",
+            "kvpop_decode_step_layers")
 
 
 class KVpopLibraryMissing(RuntimeError):
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.kvpop_prefix_thresholds.restype = ctypes.c_int
     lib.kvpop_future_attention_target.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.kvpop_future_attention_target.restype = ctypes.c_int
+    lib.kvpop_decode_step_layers.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.kvpop_decode_step_layers.restype = ctypes.c_int
     lib.kvpop_future_attention_target_noalloc.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.kvpop_future_attention_target_noalloc.restype = ctypes.c_int
     lib.kvpop_prefill_compact_batch.argtypes = [vp, i32, ctypes.POINTER(PrefillItem), vp]
@@ -228,6 +231,23 @@ class KVpopCache:
         op = _dev_ptr(out, torch.bfloat16, (B, c.n_q_heads, c.head_dim), "out")
         _check(load().kvpop_decode_step(self._h, layer, qp, kp, vp, sp, op, _stream_ptr(stream)),
                "kvpop_decode_step")
+
+    def decode_step_layers(self, layer0: int, q, k_new, v_new, score_leaving, out, stream=None):
+        """One decode step of layers layer0 .. layer0 + n - 1 in one launch (n
+        = q.shape[0]); every tensor of decode_step with a leading layer
+        dimension.  Only for layers whose inputs are independent of each
+        other's outputs (see the header)."""
+        import torch
+        c = self.cfg
+        B = c.batch
+        n = int(q.shape[0]) if q is not None and q.dim() == 4 else 0
+        qp = _dev_ptr(q, torch.bfloat16, (n, B, c.n_q_heads, c.head_dim), "q")
+        kp = _dev_ptr(k_new, torch.bfloat16, (n, B, c.n_kv_heads, c.head_dim), "k_new")
+        vp = _dev_ptr(v_new, torch.bfloat16, (n, B, c.n_kv_heads, c.head_dim), "v_new")
+        sp = _dev_ptr(score_leaving, torch.float32, (n, B, c.n_kv_heads), "score_leaving")
+        op = _dev_ptr(out, torch.bfloat16, (n, B, c.n_q_heads, c.head_dim), "out")
+        _check(load().kvpop_decode_step_layers(self._h, layer0, n, qp, kp, vp, sp, op,
+                                               _stream_ptr(stream)), "kvpop_decode_step_layers")
 
     def prune(self, layer: int, stream=None):
         """Dynamic backend: prune every head of `layer` back to the budget now."""

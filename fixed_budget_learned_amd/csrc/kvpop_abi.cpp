@@ -68,26 +68,52 @@ bool config_valid(const kvpop_config* c) {
 // unless the configuration asks for the second launch: with each head's
 // ticket on its own cache line the in-launch merge measured faster on every
 // shape from 1 to 24 sequences (4x layer at batch 1: 10.7 against 12.4 us).
-void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
-                         int32_t* threads, int32_t* rows_per_thread, int32_t* finish_apart) {
+//
+// A launch over several layers (kvpop_decode_step_layers) has many heads and
+// is bound by bandwidth, not latency: there each head gets about 1,536 /
+// heads splits (6 for 36 layers of 8 heads: 1,728 workgroups, 3.4 per
+// compute unit), merged in a second launch.  Measured on 36 layers at batch
+// 1, 4,032 slots: 1 split 121.6 us, 2 108.2, 4 102.3, 6 (second launch)
+// 98.7, 16 107.0; 2,048 slots: 1 split 65.2, 3 57.9, 5 (second launch)
+// 56.2, 6 (second launch) 56.5.  In-launch tickets cost each workgroup a
+// store acknowledgement and an atomic round trip while it holds its slot
+// (6 splits: 102.0 against 98.7 us).
+int64_t decode_splits_for(const kvpop_config& c, int64_t heads, bool layers) {
   const int64_t budget = capacity_of(c);
-  const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
-  const int nt = 256, np = 2;
-  const int64_t rpp = nt / (c.head_dim / 16);
   int64_t ns = c.decode_splits;
   if (ns == 0) {
-    ns = std::max<int64_t>(1, 256 / heads);
+    ns = layers ? (1536 + heads - 1) / heads : 256 / heads;
     ns = std::min<int64_t>(ns, (budget + 127) / 128);
     ns = std::min<int64_t>(ns, kvpop::decode_max_splits());
     ns = std::max<int64_t>(ns, 1);
   }
-  int64_t rows = (budget + ns - 1) / ns;
-  rows = (rows + rpp - 1) / rpp * rpp;
+  return ns;
+}
+
+int32_t rows_per_split_for(const kvpop_config& c, int64_t ns) {
+  const int64_t rpp = 256 / (c.head_dim / 16);  // rows per pass of a workgroup
+  int64_t rows = (capacity_of(c) + ns - 1) / ns;
+  return int32_t((rows + rpp - 1) / rpp * rpp);
+}
+
+void choose_decode_shape(const kvpop_config& c, int32_t* nsplit, int32_t* rows_per_split,
+                         int32_t* threads, int32_t* rows_per_thread, int32_t* finish_apart) {
+  const int64_t ns = decode_splits_for(c, int64_t(c.batch) * c.n_kv_heads, false);
   *nsplit = int32_t(ns);
-  *rows_per_split = int32_t(rows);
-  *threads = nt;
-  *rows_per_thread = np;
+  *rows_per_split = rows_per_split_for(c, ns);
+  *threads = 256;
+  *rows_per_thread = 2;
   *finish_apart = (c.decode_finish == 2) ? 1 : 0;
+}
+
+// Partial-result entries the decode workspace needs: the largest of one
+// layer's launch and every launch over 1 .. n_layers layers.
+size_t decode_parts(const kvpop_config& c) {
+  const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
+  int64_t parts = heads * decode_splits_for(c, heads, false);
+  for (int64_t n = 2; n <= c.n_layers; ++n)
+    parts = std::max(parts, n * heads * decode_splits_for(c, n * heads, true));
+  return size_t(parts);
 }
 
 bool compute_layout(const kvpop_config& c, Layout* L) {
@@ -126,11 +152,12 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
                                                                 (size_t(128) << 20) / slice_one)));
   ok = ok && take(slice_one * size_t(L->slice_items), &L->slice_keys);
   ok = ok && take(size_t(L->slice_items) * c.n_kv_heads * kvpop::SLICE_MAX * 4, &L->slice_nan);
-  const size_t parts = heads * size_t(L->nsplit);
+  const size_t parts = decode_parts(c);
   ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
   ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
   ok = ok && mul_ok(parts, sizeof(kvpop::MinPart), &tmp) && take(tmp, &L->part_min);
-  ok = ok && take(heads * 4 * kvpop::TICKET_STRIDE, &L->tickets);
+  // tickets: every head of the cache (a launch over all layers)
+  ok = ok && take(heads_all * 4 * kvpop::TICKET_STRIDE, &L->tickets);
   L->total = off;
   return ok;
 }
@@ -275,7 +302,7 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
   hipError_t e = kvpop::launch_init_ctl(reinterpret_cast<kvpop::HeadCtl*>(c->base + L.ctl),
                                         int64_t(heads_all),
                                         reinterpret_cast<uint32_t*>(c->base + L.tickets),
-                                        int64_t(heads) * kvpop::TICKET_STRIDE, nullptr);
+                                        int64_t(heads_all) * kvpop::TICKET_STRIDE, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) {
     if (c->owns) (void)hipFree(c->base);
@@ -501,6 +528,47 @@ int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, cons
     if (e != hipSuccess) {
       cache->poisoned = true;
       return KVPOP_EHIP;
+    }
+  }
+  return KVPOP_OK;
+}
+
+int kvpop_decode_step_layers(kvpop_cache* cache, int32_t layer0, int32_t n_layers,
+                             const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                             const float* score_leaving, uint16_t* out, void* stream) {
+  if (cache == nullptr) return KVPOP_EINVAL;
+  const kvpop_config& c = cache->cfg;
+  if (layer0 < 0 || n_layers < 1 || int64_t(layer0) + n_layers > c.n_layers) return KVPOP_EINVAL;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || score_leaving == nullptr ||
+      out == nullptr)
+    return KVPOP_EINVAL;
+  if (cache->poisoned) return KVPOP_ESTATE;
+  int32_t* nh = cache->n_host.data() + size_t(layer0) * c.batch;
+  for (int64_t i = 0; i < int64_t(n_layers) * c.batch; ++i)
+    if (int64_t(nh[i]) + 1 >= c.max_positions) return KVPOP_ESTATE;
+  DeviceGuard dg(cache->device);
+  if (!dg.ok) return KVPOP_EHIP;
+  kvpop::DecodeWork w = cache->work();
+  const int64_t ns = decode_splits_for(c, int64_t(n_layers) * c.batch * c.n_kv_heads, true);
+  w.nsplit = int32_t(ns);
+  w.rows_per_split = rows_per_split_for(c, ns);
+  w.finish_apart = (c.decode_finish == 1) ? 0 : 1;  // the second launch unless asked
+  hipError_t e = kvpop::launch_decode(cache->geo(), cache->layer(layer0), w, n_layers, q, k_new,
+                                      v_new, score_leaving, out, cache->scale_log2e,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    cache->poisoned = true;
+    return KVPOP_EHIP;
+  }
+  for (int64_t i = 0; i < int64_t(n_layers) * c.batch; ++i) nh[i] += 1;
+  if (c.prune_interval > 0) {
+    for (int32_t l = layer0; l < layer0 + n_layers; ++l) {
+      if (++cache->steps[size_t(l)] % c.prune_interval != 0) continue;
+      e = kvpop::launch_prune(cache->geo(), cache->layer(l), static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) {
+        cache->poisoned = true;
+        return KVPOP_EHIP;
+      }
     }
   }
   return KVPOP_OK;

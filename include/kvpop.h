@@ -105,7 +105,9 @@ typedef struct kvpop_config {
                             Both hold the same rows right after a prune. */
   int32_t decode_finish; /* how a decode step merges a head's splits (no
                             effect with one split):
-                            0 = the library's default, currently 1;
+                            0 = the library's default: 1 for
+                                kvpop_decode_step, 2 for
+                                kvpop_decode_step_layers;
                             1 = the last split's workgroup, in the same launch;
                             2 = a second launch, one workgroup per head.
                             The outputs and cache updates are identical. */
@@ -201,6 +203,31 @@ KVPOP_API int kvpop_prefill_compact_batch(kvpop_cache* cache, int32_t n_items,
 KVPOP_API int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, const float* score_leaving, uint16_t* out,
                       void* stream);
+
+/* One decode step of `n_layers` consecutive layers (layer0 .. layer0 +
+ * n_layers - 1) in a single launch: exactly what n_layers calls of
+ * kvpop_decode_step, one per layer in order, would do, with every per-layer
+ * tensor given a leading layer dimension:
+ *   q            device [n_layers][batch][Hq][D] bf16
+ *   k_new, v_new device [n_layers][batch][Hkv][D] bf16
+ *   score_leaving device [n_layers][batch][Hkv] float32
+ *   out          device [n_layers][batch][Hq][D] bf16
+ * Valid only when no layer's inputs depend on another layer's output of the
+ * same step: independent per-layer streams, as in the synthetic multi-layer
+ * benchmarks.  In a transformer, layer l+1's query comes from layer l's
+ * output, so a model decodes one layer at a time with kvpop_decode_step.
+ * Every (layer, sequence, KV head) keeps its own bounded cache ("Qwen3-8B-
+ * KVpop-4x" model card, intro), so the layers' heads are independent and
+ * share one grid; with many heads the launch keeps every compute unit busy
+ * where one layer at batch 1 (8 KV heads) cannot.  The Dynamic backend's
+ * prune runs for each layer whose step count reaches the interval.
+ * Errors: KVPOP_EINVAL (NULL pointers, layer range outside the cache),
+ * KVPOP_ESTATE (poisoned, or a sequence of one of the layers would reach
+ * max_positions), KVPOP_EHIP (launch failed). */
+KVPOP_API int kvpop_decode_step_layers(kvpop_cache* cache, int32_t layer0, int32_t n_layers,
+                                       const uint16_t* q, const uint16_t* k_new,
+                                       const uint16_t* v_new, const float* score_leaving,
+                                       uint16_t* out, void* stream);
 
 /* Dynamic backend: prune every sequence's heads of `layer` now.  A head whose
  * scored region holds more than n_scored tokens keeps its n_scored most

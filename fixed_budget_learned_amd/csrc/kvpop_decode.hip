@@ -694,29 +694,27 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         m_run[h] = mnew;
       }
     }
-    // P V on row pairs: bf16 probabilities, v_dot2 over the two rows
+    // P V in fp32: each V element widened from bf16 (exact) and multiplied
+    // by the fp32 probability; the sum of probabilities adds the same values
 #pragma unroll
-    for (int i = 0; i < NP; i += 2) {
-      uint32_t ph[G];
+    for (int i = 0; i < NP; ++i) {
+      float pr[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float ms = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
-        float2_t pf = {fast_exp2(x[i][h] - ms), fast_exp2(x[i + 1][h] - ms)};
-        ph[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2_t));
-        l_run[h] = dot2_bf16(ph[h], BF16_ONE_PAIR, l_run[h]);
+        pr[h] = fast_exp2(x[i][h] - ms);
+        l_run[h] += pr[h];
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const uint32_t a[4] = {vv[i][hf].x, vv[i][hf].y, vv[i][hf].z, vv[i][hf].w};
-        const uint32_t b[4] = {vv[i + 1][hf].x, vv[i + 1][hf].y, vv[i + 1][hf].z, vv[i + 1][hf].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t lo2 = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
-          const uint32_t hi2 = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+          const float lo = bf16_lo(a[j]), hi = bf16_hi(a[j]);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            acc[h][hf * 8 + 2 * j] = dot2_bf16(lo2, ph[h], acc[h][hf * 8 + 2 * j]);
-            acc[h][hf * 8 + 2 * j + 1] = dot2_bf16(hi2, ph[h], acc[h][hf * 8 + 2 * j + 1]);
+            acc[h][hf * 8 + 2 * j] = fmaf(lo, pr[h], acc[h][hf * 8 + 2 * j]);
+            acc[h][hf * 8 + 2 * j + 1] = fmaf(hi, pr[h], acc[h][hf * 8 + 2 * j + 1]);
           }
         }
       }

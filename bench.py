@@ -384,22 +384,30 @@ def layered_config(w, steps: int, reps: int):
                 cache.decode_step(layer, q[i, layer], kn[i, layer], vn[i, layer], sl[i, layer],
                                   out[layer])
 
-    with torch.cuda.stream(stream):
-        dec()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        dec()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1)
+    def dec_one_launch():
+        for i in range(steps):
+            cache.decode_step_layers(0, q[i], kn[i], vn[i], sl[i], out)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / (reps * steps)
+
+    us = timed(dec)
+    us1 = timed(dec_one_launch) if L > 1 else None
     cache.close()
-    us = dec_ms * 1e3 / (reps * steps)
     # decode bytes per step: every layer reads its kept rows; a cache started
     # empty holds at least P + steps rows during the timed replays
     kept = min(w.budget, P + steps + 1)
@@ -408,7 +416,17 @@ def layered_config(w, steps: int, reps: int):
            "decode_us_per_step": us, "decode_steps_per_s": 1e6 / us,
            "decode_GBps": dbytes / (us * 1e-6) / 1e9,
            "decode_frac": dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+           "decode_launch": "one kvpop_decode_step launch per layer-step",
            "decode_bytes_per_step": dbytes, "decode_steps_timed": reps * steps}
+    if us1 is not None:
+        res["decode_one_launch"] = {
+            "us_per_step": us1, "steps_per_s": 1e6 / us1,
+            "GBps": dbytes / (us1 * 1e-6) / 1e9,
+            "frac": dbytes / (us1 * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "launch": "kvpop_decode_step_layers: every layer in one launch",
+            "valid_for": "independent per-layer inputs only (these synthetic layers); a model "
+                         "decodes layer by layer, since layer l+1's query depends on layer l's "
+                         "output"}
     if P > 0:
         pbytes = L * prefill_bytes(w, P)
         res.update({"prefill_us_all_layers": pre_batch_ms * 1e3,
@@ -418,6 +436,34 @@ def layered_config(w, steps: int, reps: int):
                     "prefill_bytes": pbytes,
                     "prefill_launch": "all layers in one kvpop_prefill_compact_batch call",
                     "prefill_us_one_call_per_layer": pre_ms * 1e3})
+    return res
+
+
+def memory_context():
+    """Device bytes of the fixed-budget caches of the 36-layer workloads
+    against a dense cache of the same model at 131,072 tokens, beside the
+    pages' peak-VRAM figures (quoted as context, not as a target: they are
+    whole-model measurements on unstated hardware)."""
+    from fixed_budget_learned_amd import abi
+    from fixed_budget_learned_amd.configs import LONG_131K_8X, QWEN3_8B_36L_4X
+    res = {}
+    for w, positions in ((LONG_131K_8X, 131072 + 2048), (QWEN3_8B_36L_4X, 16384 + 4096)):
+        cfg = abi.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sink,
+                              w.n_scored, w.n_recent, max_positions=positions)
+        rows = w.n_layers * w.n_kv_heads * w.budget
+        res[w.name] = {"budget_per_head": w.budget,
+                       "kv_rows_bytes": rows * w.head_dim * 2 * 2,
+                       "arena_bytes": abi.required_bytes(cfg),
+                       "arena_note": "kvpop_cache_required_bytes: K/V rows, slot metadata and the "
+                                     "prefill/decode workspaces, allocated once at creation"}
+    w = LONG_131K_8X
+    res["dense_cache_131k_bytes"] = w.n_layers * w.n_kv_heads * 131072 * w.head_dim * 2 * 2
+    res["pages_context"] = {
+        "dense_peak_vram_GB": 36, "kvpop_peak_vram_GB": 19,
+        "what": "whole-model peak VRAM, Qwen3-8B at batch 1 decoding to 131k tokens; hardware "
+                "not stated",
+        "source": "English aiweekly article, third paragraph (also the French article, first and "
+                  "third paragraphs)"}
     return res
 
 
@@ -662,11 +708,12 @@ def main():
     ap.add_argument("--batched-only", action="store_true",
                     help="run only the batch-64 serving measurement (for profiles)")
     ap.add_argument("--only", choices=("future", "thresholds", "dynamic", "long_context",
-                                       "stack_16k"),
+                                       "stack_16k", "cold"),
                     default=None,
-                    help="run only this section (for profiles): future, thresholds and dynamic "
-                         "on the one-layer workload, long_context the 36-layer 131k-token one, "
-                         "stack_16k the 36-layer 16k-token one")
+                    help="run only this section (for profiles): future, thresholds, dynamic and "
+                         "cold (decode with the cache evicted from every cache level between "
+                         "steps) on the one-layer workload, long_context the 36-layer "
+                         "131k-token one, stack_16k the 36-layer 16k-token one")
     ap.add_argument("--no-dense-sweep", action="store_true",
                     help="skip the fixed-budget vs dense decode comparison at 16k-131k context")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -705,6 +752,8 @@ def main():
             r = layered_config(LONG_131K_8X, args.decode_steps or 32, max(1, args.steps))
         elif args.only == "stack_16k":
             r = layered_config(QWEN3_8B_36L_4X, args.decode_steps or 32, max(1, args.steps))
+        elif args.only == "cold":
+            r = decode_cold(QWEN3_8B_LAYER_4X, args.decode_steps or 32)
         else:
             r = dynamic_backend(args.decode_steps or 1024, max(1, args.steps))
         print(json.dumps({args.only: r}), flush=True)
@@ -855,6 +904,7 @@ def main():
                              layered_config(QWEN3_8B_36L_4X, 32, 2),
                              layered_config(LONG_131K_8X, 32, 2),
                              layered_config(TP8_SHARE_4X, 256, 2)]
+    result["memory"] = memory_context()
     if not args.no_dense_sweep:
         result["dense_vs_kvpop"] = dense_vs_kvpop((16384, 32768, 65536, 131072), 64, 3)
         result["dynamic_backend"] = dynamic_backend(1024, 3)

@@ -70,19 +70,21 @@ bool config_valid(const kvpop_config* c) {
 // shape from 1 to 24 sequences (4x layer at batch 1: 10.7 against 12.4 us).
 //
 // A launch over several layers (kvpop_decode_step_layers) has many heads and
-// is bound by bandwidth, not latency: there each head gets about 1,536 /
-// heads splits (6 for 36 layers of 8 heads: 1,728 workgroups, 3.4 per
+// is bound by bandwidth, not latency: there each head gets about 1,440 /
+// heads splits (5 for 36 layers of 8 heads: 1,440 workgroups, 2.8 per
 // compute unit), merged in a second launch.  Measured on 36 layers at batch
-// 1, 4,032 slots: 1 split 121.6 us, 2 108.2, 4 102.3, 6 (second launch)
-// 98.7, 16 107.0; 2,048 slots: 1 split 65.2, 3 57.9, 5 (second launch)
-// 56.2, 6 (second launch) 56.5.  In-launch tickets cost each workgroup a
-// store acknowledgement and an atomic round trip while it holds its slot
-// (6 splits: 102.0 against 98.7 us).
+// 1, 4,032 slots: 1 split 121.6 us, 2 108.2, 4 102.3, 5 (second launch)
+// 100.0, 6 (second launch) 98.7, 16 107.0; 2,048 slots: 1 split 65.2, 3
+// 57.9, 5 (second launch) 56.2, 6 (second launch) 56.5, 8 (second launch)
+// 60.9 (bf16 probabilities; with fp32 ones 5 splits take 101.7 and 58.3
+// us).  In-launch tickets cost each workgroup a store acknowledgement and an
+// atomic round trip while it holds its slot (6 splits: 102.0 against 98.7
+// us).
 int64_t decode_splits_for(const kvpop_config& c, int64_t heads, bool layers) {
   const int64_t budget = capacity_of(c);
   int64_t ns = c.decode_splits;
   if (ns == 0) {
-    ns = layers ? (1536 + heads - 1) / heads : 256 / heads;
+    ns = layers ? (1440 + heads - 1) / heads : 256 / heads;
     ns = std::min<int64_t>(ns, (budget + 127) / 128);
     ns = std::min<int64_t>(ns, kvpop::decode_max_splits());
     ns = std::max<int64_t>(ns, 1);

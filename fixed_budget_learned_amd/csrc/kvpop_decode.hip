@@ -885,6 +885,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           0, CP);
     if (holds_min && wg_minkey != KEY_NONE)
       __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(msl), r_min, 8, 0, CP);
+    // the second launch reads the next leaving token's slot here instead of
+    // a ring lookup that would wait for the control block
+    if (APART && split == 0 && tid == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(ring_next), r_min, 12, 0, 0);
   }
   if (APART) return;
 
@@ -914,8 +918,9 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   const int head = blockIdx.x;
   const HeadCtl c = p.ctl[head];
   const float sg = p.score_leaving[head];
+  const int32_t ring_next = p.part_min[static_cast<int64_t>(head) * p.nsplit].pad;
   const Decision dc = decide(c, sg, p.n_sink, p.n_scored, p.n_recent);
-  finish_head<D, G, false>(p, head, dc, read_ring_next(p, head, dc), s_fin);
+  finish_head<D, G, false>(p, head, dc, ring_next, s_fin);
 }
 
 template <int D, int G>

@@ -28,7 +28,9 @@ struct HeadCtl {
 };
 static_assert(sizeof(HeadCtl) == 32, "HeadCtl layout");
 
-// Partial minimum of one split of a head's slot range.
+// Partial minimum of one split of a head's slot range.  pad: in split 0's
+// record, the slot of the next token to leave the window (for a
+// second-launch merge).
 struct MinPart {
   uint64_t key;
   int32_t slot;

@@ -190,6 +190,12 @@ struct kvpop_cache {
   float scale_log2e = 0.f;
   float* scratch = nullptr;     // this device's static future-target workspace
   std::vector<int32_t> n_host;  // [L][B], newest processed position
+  // [L][B]: reset since the control blocks were last written.  A reset
+  // enqueues nothing: a non-empty prefill overwrites the blocks anyway, and
+  // every other call that reads them first initialises the stale ones
+  // (flush_resets) on its own stream.
+  std::vector<uint8_t> stale;
+  int64_t n_stale = 0;
   std::vector<int64_t> steps;   // [L] decode steps taken (the Dynamic backend's prune clock)
 
   kvpop::Geometry geo() const {
@@ -246,6 +252,47 @@ struct kvpop_cache {
   }
 };
 
+namespace {
+
+// Initialise the control blocks of the reset sequences among layers
+// [l0, l1) x sequences [s0, s1): one launch per run of adjacent ones.
+int flush_resets(kvpop_cache* cache, int32_t l0, int32_t l1, int32_t s0, int32_t s1,
+                 hipStream_t stream) {
+  if (cache->n_stale == 0) return KVPOP_OK;
+  const int32_t B = cache->cfg.batch, Hkv = cache->cfg.n_kv_heads;
+  for (int32_t l = l0; l < l1; ++l) {
+    for (int32_t b = s0; b < s1;) {
+      const size_t slot = size_t(l) * B + b;
+      if (!cache->stale[slot]) {
+        ++b;
+        continue;
+      }
+      int32_t e = b;
+      while (e < s1 && cache->stale[size_t(l) * B + e]) ++e;
+      hipError_t err = kvpop::launch_init_ctl(cache->layer(l).ctl + size_t(b) * Hkv,
+                                              int64_t(e - b) * Hkv, nullptr, 0, stream);
+      if (err != hipSuccess) {
+        cache->poisoned = true;
+        return KVPOP_EHIP;
+      }
+      for (int32_t x = b; x < e; ++x) cache->stale[size_t(l) * B + x] = 0;
+      cache->n_stale -= e - b;
+      b = e;
+    }
+  }
+  return KVPOP_OK;
+}
+
+// A non-empty prefill writes every control block of its sequence.
+void mark_written(kvpop_cache* cache, size_t slot) {
+  if (cache->stale[slot]) {
+    cache->stale[slot] = 0;
+    --cache->n_stale;
+  }
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t kvpop_cache_required_bytes(const kvpop_config* cfg) {
@@ -275,6 +322,7 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
   if (c == nullptr) return KVPOP_ENOMEM;
   try {
     c->n_host.assign(size_t(cfg->n_layers) * cfg->batch, -1);
+    c->stale.assign(size_t(cfg->n_layers) * cfg->batch, 0);
     c->steps.assign(size_t(cfg->n_layers), 0);
   } catch (...) {
     delete c;
@@ -332,21 +380,17 @@ void kvpop_cache_destroy(kvpop_cache* cache) {
 }
 
 int kvpop_cache_reset(kvpop_cache* cache, int32_t layer, int32_t seq, void* stream) {
+  (void)stream;  // nothing is enqueued here
   if (cache == nullptr) return KVPOP_EINVAL;
   if (layer < 0 || layer >= cache->cfg.n_layers || seq < 0 || seq >= cache->cfg.batch)
     return KVPOP_EINVAL;
   if (cache->poisoned) return KVPOP_ESTATE;
-  DeviceGuard dg(cache->device);
-  if (!dg.ok) return KVPOP_EHIP;
-  kvpop::LayerView lv = cache->layer(layer);
-  hipError_t e = kvpop::launch_init_ctl(lv.ctl + size_t(seq) * cache->cfg.n_kv_heads,
-                                        cache->cfg.n_kv_heads, nullptr, 0,
-                                        static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    cache->poisoned = true;
-    return KVPOP_EHIP;
+  const size_t slot = size_t(layer) * cache->cfg.batch + seq;
+  cache->n_host[slot] = -1;
+  if (!cache->stale[slot]) {
+    cache->stale[slot] = 1;
+    ++cache->n_stale;
   }
-  cache->n_host[size_t(layer) * cache->cfg.batch + seq] = -1;
   return KVPOP_OK;
 }
 
@@ -379,6 +423,7 @@ int kvpop_prefill_compact(kvpop_cache* cache, int32_t layer, int32_t seq, int32_
     return KVPOP_EHIP;
   }
   nh = n_tokens - 1;
+  mark_written(cache, size_t(layer) * c.batch + seq);
   return KVPOP_OK;
 }
 
@@ -428,7 +473,10 @@ int kvpop_prefill_compact_batch(kvpop_cache* cache, int32_t n_items,
     return KVPOP_EHIP;
   }
   for (int32_t i = 0; i < n_items; ++i)
-    if (items[i].n_tokens > 0) cache->n_host[slots[size_t(i)]] = items[i].n_tokens - 1;
+    if (items[i].n_tokens > 0) {
+      cache->n_host[slots[size_t(i)]] = items[i].n_tokens - 1;
+      mark_written(cache, slots[size_t(i)]);
+    }
   return KVPOP_OK;
 }
 
@@ -515,6 +563,8 @@ int kvpop_decode_step(kvpop_cache* cache, int32_t layer, const uint16_t* q, cons
     if (int64_t(nh[b]) + 1 >= c.max_positions) return KVPOP_ESTATE;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
+  if (int r = flush_resets(cache, layer, layer + 1, 0, c.batch, static_cast<hipStream_t>(stream)))
+    return r;
   hipError_t e = kvpop::launch_decode(cache->geo(), cache->layer(layer), cache->work(), 1, q,
                                       k_new, v_new, score_leaving, out, cache->scale_log2e,
                                       static_cast<hipStream_t>(stream));
@@ -550,6 +600,9 @@ int kvpop_decode_step_layers(kvpop_cache* cache, int32_t layer0, int32_t n_layer
     if (int64_t(nh[i]) + 1 >= c.max_positions) return KVPOP_ESTATE;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
+  if (int r = flush_resets(cache, layer0, layer0 + n_layers, 0, c.batch,
+                           static_cast<hipStream_t>(stream)))
+    return r;
   kvpop::DecodeWork w = cache->work();
   const int64_t ns = decode_splits_for(c, int64_t(n_layers) * c.batch * c.n_kv_heads, true);
   w.nsplit = int32_t(ns);
@@ -584,6 +637,8 @@ int kvpop_cache_prune(kvpop_cache* cache, int32_t layer, void* stream) {
   if (c.prune_interval == 0) return KVPOP_OK;  // Static: never above the budget
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
+  if (int r = flush_resets(cache, layer, layer + 1, 0, c.batch, static_cast<hipStream_t>(stream)))
+    return r;
   hipError_t e =
       kvpop::launch_prune(cache->geo(), cache->layer(layer), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -600,6 +655,12 @@ int kvpop_cache_state(kvpop_cache* cache, int32_t layer, int32_t seq, kvpop_stat
   if (layer < 0 || layer >= c.n_layers || seq < 0 || seq >= c.batch) return KVPOP_EINVAL;
   DeviceGuard dg(cache->device);
   if (!dg.ok) return KVPOP_EHIP;
+  if (cache->stale[size_t(layer) * c.batch + seq]) {
+    if (cache->poisoned) return KVPOP_ESTATE;
+    if (int r = flush_resets(cache, layer, layer + 1, seq, seq + 1,
+                             static_cast<hipStream_t>(stream)))
+      return r;
+  }
   const int32_t Hkv = c.n_kv_heads;
   const size_t budget = size_t(capacity_of(c));
   std::vector<kvpop::HeadCtl> ctl;

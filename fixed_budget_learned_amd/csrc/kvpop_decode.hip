@@ -85,8 +85,6 @@ constexpr int MAX_SPLITS = 256;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Raw buffer descriptor, last word: 32-bit data format (untyped access).
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
 // Cache-policy operand of buffer accesses: SC1, coherent at agent scope
 // (stores write through to the device's point of coherence; loads do not
 // hit stale L2 lines).

@@ -11,6 +11,10 @@ namespace kvpop {
 
 constexpr int WAVE = 64;
 
+// Raw buffer descriptor, last word: 32-bit data format (untyped access).
+// Loads past the descriptor's byte count return 0 without a memory access.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+
 // Order-preserving code of a float32 score: flipping all bits of negatives
 // and setting the sign bit of non-negatives makes unsigned order equal float
 // order.  -0 is folded onto +0 first so the two compare equal.
@@ -42,13 +46,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 // ---- wavefront reductions --------------------------------------------------
 
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4 and 8
+// lanes within each row of 16, then the row broadcasts of lane 15 (into rows
+// 1 and 3) and lane 31 (into rows 2 and 3).  Lanes without a source add the
+// `old` operand, 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_add_src(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROWS, 0xF, false));
+}
 __device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t x) {
-  const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    uint32_t y = __shfl_up(x, d, WAVE);
-    if (lane >= d) x += y;
-  }
+  x += dpp_add_src<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_add_src<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_add_src<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_add_src<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_add_src<0x142, 0xA>(x);  // row_bcast:15
+  x += dpp_add_src<0x143, 0xC>(x);  // row_bcast:31
   return x;
 }
 

@@ -64,11 +64,10 @@ __host__ __device__ inline PrefillShape prefill_shape(int32_t P, int32_t s, int3
   return r;
 }
 
-// Radix digits over the 32-bit code: 12, 12 and 8 bits (4096-bin histogram),
-// or 11, 11 and 10 bits (2048 bins) where the smaller histogram lets two
-// workgroups share a compute unit's LDS (16 codes per thread, not the list
-// mode).
-constexpr int NBINS = 4096;
+// Radix digits over the 32-bit code: 12, 12 and 8 bits.
+constexpr int NB0 = 4096, NB1 = 4096, NB2 = 256;
+constexpr int SH0 = 20, SH1 = 8;
+constexpr int NBINS = NB0;
 constexpr int TILE_LG = 5;   // streamed compaction: tiles of 32 candidates per thread
 
 // Coalesced load of candidates [0, n) at `sc` into LDS as order codes, laid
@@ -159,12 +158,10 @@ __device__ __forceinline__ void radix_pass(Visit&& visit, uint32_t prefix, uint3
   __syncthreads();
 }
 
+
+
 // Select kernels.  1024 threads per workgroup; MODE:
 //   SEL_HEAD   one workgroup per KV head selects from all its candidates.
-//              VPT 16 / 32: each thread holds a contiguous block of at most
-//              VPT candidate codes in registers (staged through LDS from
-//              coalesced loads); VPT 0: the scores are streamed on every pass
-//              and compacted in LDS-staged tiles (fallback for any length).
 //   SEL_SLICE  first level for long prompts: workgroup (head, slice) selects
 //              the top min(k, slice length) of a slice of the candidates and
 //              writes their keys, ascending in position, padded with key 0 to
@@ -174,17 +171,6 @@ __device__ __forceinline__ void radix_pass(Visit&& visit, uint32_t prefix, uint3
 //              union (read as keys, in position order) and writes positions
 //              and the control block like SEL_HEAD.
 constexpr int SEL_HEAD = 0, SEL_SLICE = 1, SEL_LIST = 2;
-
-struct SelectArgs {
-  const float* scores;   // [Hkv][P] of this prompt
-  PrefillShape sh;
-  int32_t k;             // scored slots (stride of the selection buffers)
-  int32_t* sel;          // [Hkv][k] kept candidate positions, ascending
-  HeadCtl* ctl;          // [Hkv]
-  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level keys
-  int32_t* slice_nan;    // [Hkv][SLICE_MAX] first-level NaN flags
-  int32_t n_slices, slice_len;
-};
 
 // One prompt of a select launch.  head0: the cache-wide index of its
 // (layer, sequence)'s first KV head.
@@ -206,38 +192,375 @@ struct SelectBatch {
   SelectItem item[NB];
 };
 
-// Occupancy hint: with 16 codes per thread (and not the list mode, whose
-// 64-bit staging allows one workgroup per compute unit) two workgroups share
-// a compute unit, 8 waves per SIMD.  They fit that many without the hint, but
-// with it the compiler schedules for it: the two-level first level of a
-// 131k-token prompt ran 134 -> 89 us in a 36-layer batched launch.
+// Wave 0 of a workgroup: the bin of histogram `h` (NB counts, bin order =
+// code order) that holds the krem-th largest counted code.  Lane l sums the
+// NB/64 bins NB-(l+1)*NB/64 .. NB-l*NB/64-1 (the highest in lane 0, read in a
+// lane-rotated order so that the lanes spread over the banks); a prefix sum
+// over the lanes finds the lane whose range reaches krem; the wave then reads
+// that lane's bins, one per lane from the highest down, and a second prefix
+// sum finds the bin.  s_pick receives (bin, counted codes in higher bins,
+// codes in the bin).  1 <= krem <= the counted total.
+template <int NB>
+__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t krem, uint32_t* s_pick) {
+  constexpr int PER = NB / WAVE;
+  static_assert(PER >= 1 && (PER & (PER - 1)) == 0, "bins per lane: a power of two");
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int base = NB - (lane + 1) * PER;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) sum += h[base + ((r + lane) & (PER - 1))];
+  const uint32_t incl = wave_inclusive_scan_u32(sum);
+  const uint32_t ex = incl - sum;
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(ex < krem && krem <= incl);
+  const int L = hit ? __builtin_ctzll(hit) : 0;
+  const uint32_t exL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ex), L));
+  const int top = NB - L * PER - 1;  // highest bin of lane L
+  const uint32_t v = lane < PER ? h[top - lane] : 0u;
+  const uint32_t iv = wave_inclusive_scan_u32(v);
+  const uint64_t hit2 = __builtin_amdgcn_ballot_w64(lane < PER && exL + iv >= krem);
+  const int r = hit2 ? __builtin_ctzll(hit2) : 0;
+  if (lane == r) {
+    s_pick[0] = static_cast<uint32_t>(top - r);
+    s_pick[1] = exL + iv - v;
+    s_pick[2] = v;
+  }
+}
+
+// The same search by the whole workgroup, for NB = 4 x 1024 bins: thread t
+// sums its 4 bins NB-4(t+1) .. NB-4t-1 (one 16-byte read) and keeps its
+// inclusive prefix within its wave; after a barrier wave 0 finds the wave,
+// then the thread, then the bin whose range reaches krem.  All threads call
+// it; s_pick is written by wave 0 (read it after a barrier).
+template <int NB>
+__device__ __forceinline__ void block_find_bin(const uint32_t* h, uint32_t krem, uint32_t* s_pick,
+                                               uint32_t* s_wsum, uint32_t* s_lincl) {
+  constexpr int PT = NB / SEL_THREADS;
+  constexpr int NWAVE = SEL_THREADS / WAVE;
+  static_assert(PT == 4, "four bins per thread");
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wid = tid / WAVE;
+  const uint4 b = *reinterpret_cast<const uint4*>(h + NB - (tid + 1) * PT);
+  const uint32_t sum = b.x + b.y + b.z + b.w;
+  const uint32_t incl = wave_inclusive_scan_u32(sum);
+  s_lincl[tid] = incl;
+  if (lane == WAVE - 1) s_wsum[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    const uint32_t ws = lane < NWAVE ? s_wsum[lane] : 0u;
+    const uint32_t wi = wave_inclusive_scan_u32(ws);
+    const uint64_t hw = __builtin_amdgcn_ballot_w64(lane < NWAVE && wi - ws < krem && krem <= wi);
+    const int W = hw ? __builtin_ctzll(hw) : 0;
+    const uint32_t wbase = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wi - ws), W));
+    const uint32_t li = s_lincl[W * WAVE + lane];
+    const uint32_t lprev = lane > 0 ? s_lincl[W * WAVE + lane - 1] : 0u;
+    const uint64_t hl = __builtin_amdgcn_ballot_w64(wbase + lprev < krem && krem <= wbase + li);
+    const int L = hl ? __builtin_ctzll(hl) : 0;
+    const uint32_t base = wbase + static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lprev), L));
+    const int top = NB - (W * WAVE + L) * PT - 1;  // highest bin of that thread
+    const uint32_t v = lane < PT ? h[top - lane] : 0u;
+    const uint32_t iv = wave_inclusive_scan_u32(v);
+    const uint64_t hb = __builtin_amdgcn_ballot_w64(lane < PT && base + iv >= krem);
+    const int r = hb ? __builtin_ctzll(hb) : 0;
+    if (lane == r) {
+      s_pick[0] = static_cast<uint32_t>(top - r);
+      s_pick[1] = base + iv - v;
+      s_pick[2] = v;
+    }
+  }
+}
+
+// Lanes below this one whose bit is set in the wave mask m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Register-resident select (VPT = 16 or 32 entries per thread; every mode).
+// Entry i of the workgroup lives in thread i % 1024, register i / 1024, so
+// the loads go straight from coalesced reads into registers and each wave's
+// lanes hold consecutive entries of every register row.  Three radix passes
+// (12, 12 and 8-bit digits, histograms in LDS, all cleared while the loads
+// are in flight; wave 0 locates each pass's bin) find the kk-th largest code
+// thr and how many entries carrying it are kept (the newest ones).  The
+// ordered compaction then ranks every kept entry in position order from
+// wave ballots: per register row, each wave's counts of codes above thr and
+// equal to it go into a table whose exclusive prefix (row-major, then wave)
+// gives each wave its base, and a lane's rank adds the ballot bits below it.
+//
+// Occupancy hint: two 1024-thread workgroups per compute unit (8 waves per
+// SIMD, at most 64 registers) for 16 entries per thread.
 template <int VPT, int MODE, int NB>
 __global__ __launch_bounds__(SEL_THREADS)
-__attribute__((amdgpu_waves_per_eu(VPT == 16 && MODE != SEL_LIST ? 8 : 1)))
+__attribute__((amdgpu_waves_per_eu(VPT == 16 ? 8 : 1)))
 void prefill_select_kernel(SelectBatch<NB> batch) {
-  const SelectItem& it = batch.item[blockIdx.z];
-  SelectArgs a;
-  a.scores = it.scores;
-  a.sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
-  a.k = batch.k;
-  a.sel = it.sel;
-  a.ctl = batch.ctl + it.head0;
-  a.slice_keys = it.slice_keys;
-  a.slice_nan = it.slice_nan;
-  a.n_slices = it.n_slices;
-  a.slice_len = it.slice_len;
-  // a batch launch covers its longest prompt's slices: shorter ones have none here
-  if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= a.n_slices) return;
-  static_assert(MODE != SEL_LIST || VPT == 16, "list mode stages 64-bit keys: at most 16 per thread");
-  static_assert(MODE == SEL_HEAD || VPT > 0, "slice and list modes keep codes in registers");
+  static_assert(VPT == 16 || VPT == 32, "register select: 16 or 32 entries per thread");
+  static_assert(MODE != SEL_LIST || VPT == 16, "list mode: at most 16 keys per thread");
   constexpr int NWAVE = SEL_THREADS / WAVE;
-  constexpr int LMAX = VPT > 0 ? VPT : (1 << TILE_LG);
-  constexpr int STAGE_WORDS = (MODE == SEL_LIST ? 2 : 1) * SEL_THREADS * (LMAX + 1);
-  constexpr bool NARROW = (VPT == 16 && MODE != SEL_LIST);
-  constexpr int HBINS = NARROW ? NBINS / 2 : NBINS;
-  constexpr int SH0 = NARROW ? 21 : 20, SH1 = NARROW ? 10 : 8, LAST = NARROW ? 1024 : 256;
-  __shared__ uint32_t hist[HBINS];
-  __shared__ __align__(16) uint32_t stage[STAGE_WORDS];
+  constexpr int HTOT = NB0 + NB1 + NB2;
+  constexpr int TAB = VPT * NWAVE;
+  __shared__ __align__(16) uint32_t hist[HTOT];
+  __shared__ uint32_t s_tab[TAB];
+  __shared__ uint32_t s_lincl[SEL_THREADS];
+  __shared__ uint32_t s_wsum[NWAVE];
+  __shared__ uint32_t s_pick[3];
+  __shared__ uint32_t s_nan;
+  __shared__ int32_t s_minslot;
+  __shared__ uint64_t s_minkey;
+  __shared__ uint64_t s_wmk[NWAVE];
+  __shared__ int32_t s_wmp[NWAVE];
+
+  const SelectItem& it = batch.item[blockIdx.z];
+  // a batch launch covers its longest prompt's slices: shorter ones have none here
+  if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= it.n_slices) return;
+  const PrefillShape sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wid = tid / WAVE;
+  const int32_t kst = batch.k > 0 ? batch.k : 1;  // stride of the per-head buffers
+  int32_t* out = it.sel + static_cast<int64_t>(g) * kst;
+  // this workgroup's entries: candidates [cb, cb + C) of the head's range, or
+  // (SEL_LIST) the head's first-level key list
+  int32_t cb = 0, C = sh.c1 - sh.c0, kk = sh.kk;
+  if constexpr (MODE == SEL_SLICE) {
+    cb = static_cast<int32_t>(blockIdx.y) * it.slice_len;
+    C = min(it.slice_len, sh.c1 - sh.c0 - cb);
+    kk = min(batch.k, C);
+  } else if constexpr (MODE == SEL_LIST) {
+    C = it.n_slices * batch.k;
+  }
+  const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * batch.k;
+  uint64_t* outk = it.slice_keys + list0 + static_cast<int64_t>(blockIdx.y) * batch.k;
+  const int32_t pos0 = sh.c0 + cb;  // position of entry 0 (not SEL_LIST)
+
+  // ---- entries into registers (loads first, then the LDS set-up) -----------
+  // valid entries of this thread: registers 0 .. nvalid-1
+  const int nvalid = C > tid ? min(VPT, (C - tid + SEL_THREADS - 1) / SEL_THREADS) : 0;
+  uint32_t code[VPT];
+  int32_t lpos[MODE == SEL_LIST ? VPT : 1];
+  bool nan = false;
+  if (kk > 0) {
+    // range-checked buffer loads: entries past C read as 0
+    if constexpr (MODE == SEL_LIST) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          it.slice_keys + list0, 0, C * 8, BUF_RSRC_WORD3);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 key[VPT];
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        key[j] = __builtin_amdgcn_raw_buffer_load_b64(r, (j * SEL_THREADS + tid) * 8, 0, 0);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        code[j] = key[j].y;
+        lpos[j] = static_cast<int32_t>(key[j].x);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(it.scores + static_cast<int64_t>(g) * sh.P + pos0), 0, C * 4,
+          BUF_RSRC_WORD3);
+      float x[VPT];
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        x[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (j * SEL_THREADS + tid) * 4, 0, 0));
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        code[j] = j < nvalid ? score_code(x[j]) : 0u;
+        nan |= score_is_nan(x[j]);  // entries past C read as +0
+      }
+    }
+  }
+  // Entries past C carry code 0 and are counted by the radix passes like any
+  // other; bin 0 of a pass starts at -n_pad (mod 2^32) whenever they match
+  // its prefix, so every count is exact once the pass's atomics are done.
+  const uint32_t n_pad = static_cast<uint32_t>(VPT * SEL_THREADS - C);
+  for (int i = tid; i < HTOT; i += SEL_THREADS) hist[i] = 0u;
+  if (tid == 0) {
+    hist[0] = 0u - n_pad;
+    s_nan = 0;
+    s_minslot = -1;
+    s_minkey = KEY_NONE;
+  }
+  __syncthreads();
+  if (nan) s_nan = 1;
+  if constexpr (MODE == SEL_LIST) {
+    if (tid < it.n_slices && it.slice_nan[g * SLICE_MAX + tid]) s_nan = 1;
+  }
+
+  auto pos_of = [&](int j) -> int32_t {
+    if constexpr (MODE == SEL_LIST)
+      return lpos[j];
+    else
+      return pos0 + j * SEL_THREADS + tid;
+  };
+  // where the kept entry of rank idx goes
+  auto emit = [&](uint32_t idx, int32_t pos, uint32_t o) {
+    if (idx >= static_cast<uint32_t>(kk)) return;  // never taken: ranks are < kk
+    if constexpr (MODE == SEL_SLICE)
+      outk[idx] = make_key(o, pos);
+    else
+      out[idx] = pos;
+  };
+
+  if (kk > 0 && kk == C) {
+    // every entry is kept, in order; the least important one is the smallest
+    // (code, position)
+    uint64_t mk = KEY_NONE;
+    int32_t mpos = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      if (j < nvalid) {
+        const int32_t pos = pos_of(j);
+        emit(static_cast<uint32_t>(j * SEL_THREADS + tid), pos, code[j]);
+        const uint64_t key = make_key(code[j], pos);
+        if (key < mk) {
+          mk = key;
+          mpos = pos;
+        }
+      }
+    }
+    if constexpr (MODE != SEL_SLICE) {
+      wave_min_key(mk, mpos);
+      if (lane == 0) {
+        s_wmk[wid] = mk;
+        s_wmp[wid] = mpos;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 1; w < NWAVE; ++w)
+          if (s_wmk[w] < mk) {
+            mk = s_wmk[w];
+            mpos = s_wmp[w];
+          }
+        s_minkey = mk;
+        s_minslot = sh.s_eff + (mpos - sh.c0);  // all kept: rank = position - c0
+      }
+    }
+  } else if (kk > 0) {
+    // ---- radix select of the kk-th largest code ---------------------------
+    uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk), neq = 0;
+    auto pass = [&](uint32_t* h, int shift, uint32_t nbm1, uint32_t* h_next, auto find) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if ((code[j] & mask) == prefix) atomicAdd(&h[(code[j] >> shift) & nbm1], 1u);
+      __syncthreads();
+      find(h, krem);
+      __syncthreads();
+      const uint32_t bin = s_pick[0];
+      krem -= s_pick[1];
+      neq = s_pick[2];
+      prefix |= bin << shift;
+      mask |= nbm1 << shift;
+      // the padding (code 0) still matches: pre-subtract it from the next pass
+      if (h_next != nullptr && prefix == 0u && tid == 0) atomicSub(&h_next[0], n_pad);
+    };
+    pass(hist, SH0, NB0 - 1, hist + NB0, [&](const uint32_t* h, uint32_t kr) {
+      block_find_bin<NB0>(h, kr, s_pick, s_wsum, s_lincl);
+    });
+    pass(hist + NB0, SH1, NB1 - 1, hist + NB0 + NB1, [&](const uint32_t* h, uint32_t kr) {
+      block_find_bin<NB1>(h, kr, s_pick, s_wsum, s_lincl);
+    });
+    pass(hist + NB0 + NB1, 0, NB2 - 1, static_cast<uint32_t*>(nullptr),
+         [&](const uint32_t* h, uint32_t kr) {
+           if (wid == 0) find_bin<NB2>(h, kr, s_pick);
+         });
+    // ---- ordered compaction: codes above thr, then the newest krem of those
+    // equal to it (the oldest `drop` tied entries lose) ----------------------
+    const uint32_t thr = prefix;
+    const uint32_t drop = neq - krem;
+    // only a threshold of 0 can tie with the padding; lane j collects row j's
+    // counts of this wave
+    uint32_t mycnt = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const bool v = thr != 0u || j < nvalid;
+      const uint64_t gm = __builtin_amdgcn_ballot_w64(code[j] > thr);
+      const uint64_t em = __builtin_amdgcn_ballot_w64(v && code[j] == thr);
+      const uint32_t cnt = (static_cast<uint32_t>(__builtin_popcountll(em)) << 16) |
+                           static_cast<uint32_t>(__builtin_popcountll(gm));
+      mycnt = lane == j ? cnt : mycnt;
+    }
+    if (lane < VPT) s_tab[lane * NWAVE + wid] = mycnt;
+    __syncthreads();
+    if (wid == 0) {
+      // exclusive prefix of the table, row-major then wave: lane l owns
+      // entries l*E .. l*E+E-1 (16-bit halves: above thr, equal to thr)
+      constexpr int E = TAB / WAVE;
+      uint32_t t[E], sum = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        t[e] = s_tab[lane * E + e];
+        sum += t[e];
+      }
+      uint32_t ex = wave_inclusive_scan_u32(sum) - sum;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        s_tab[lane * E + e] = ex;
+        ex += t[e];
+      }
+    }
+    __syncthreads();
+    uint32_t base[VPT];  // uniform over the wave: kept in scalar registers
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      base[j] = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<int>(s_tab[j * NWAVE + wid])));
+    int32_t min_rank = -1, min_pos = 0;  // the least important kept entry, if here
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const bool v = thr != 0u || j < nvalid;
+      const bool is_gt = code[j] > thr, is_eq = v && code[j] == thr;
+      const uint64_t gm = __builtin_amdgcn_ballot_w64(is_gt);
+      const uint64_t em = __builtin_amdgcn_ballot_w64(is_eq);
+      const uint32_t gt_before = (base[j] & 0xFFFFu) + lanes_below(gm);
+      const uint32_t eq_before = (base[j] >> 16) + lanes_below(em);
+      if (is_gt || (is_eq && eq_before >= drop)) {
+        const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
+        const int32_t pos = pos_of(j);
+        emit(idx, pos, code[j]);
+        if (is_eq && eq_before == drop) {
+          min_rank = static_cast<int32_t>(idx);
+          min_pos = pos;
+        }
+      }
+    }
+    if (min_rank >= 0) {
+      s_minslot = sh.s_eff + min_rank;
+      s_minkey = make_key(thr, min_pos);
+    }
+  }
+  if constexpr (MODE == SEL_SLICE) {
+    // pad the slice's list to k entries with the smallest key; record NaNs
+    for (int32_t j = kk + tid; j < batch.k; j += SEL_THREADS) outk[j] = 0ull;
+    __syncthreads();
+    if (tid == 0) it.slice_nan[g * SLICE_MAX + blockIdx.y] = s_nan ? 1 : 0;
+    return;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    HeadCtl c;
+    c.n = sh.P - 1;
+    c.count = sh.count;
+    c.nscored = sh.kk;
+    c.minslot = s_minslot;
+    c.minkey = s_minkey;
+    c.flags = s_nan ? 1 : 0;
+    c.leave_slot = sh.leave;
+    (batch.ctl + it.head0)[g] = c;
+  }
+}
+
+// Streaming select (SEL_HEAD, any prompt length): one workgroup per KV head
+// reads the scores again on every radix pass and compacts in LDS-staged
+// tiles of 32 candidates per thread, so that each thread walks a contiguous
+// block in position order.  The fallback for prompts whose candidates fit
+// neither the registers nor two levels.
+template <int NB>
+__global__ __launch_bounds__(SEL_THREADS) void prefill_select_stream_kernel(SelectBatch<NB> batch) {
+  constexpr int NWAVE = SEL_THREADS / WAVE;
+  constexpr int TL = 1 << TILE_LG;
+  __shared__ uint32_t hist[NBINS];
+  __shared__ __align__(16) uint32_t stage[SEL_THREADS * (TL + 1)];
   __shared__ uint32_t scan_buf[NWAVE + 1];
   __shared__ uint32_t s_bin, s_above, s_nan, s_neq;
   __shared__ int32_t s_minslot;
@@ -245,25 +568,15 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
   __shared__ uint64_t s_wmk[NWAVE];
   __shared__ int32_t s_wmp[NWAVE];
 
-  const PrefillShape& sh = a.sh;
+  const SelectItem& it = batch.item[blockIdx.z];
+  const PrefillShape sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int wid = tid / WAVE;
-  const int32_t kst = a.k > 0 ? a.k : 1;  // stride of the per-head buffers
-  int32_t* out = a.sel + static_cast<int64_t>(g) * kst;
-  // this workgroup's candidates: [cb, cb + C) of the head's candidate range
-  // (SEL_LIST: entries of the head's first-level key list)
-  int32_t cb = 0, C = sh.c1 - sh.c0, kk = sh.kk;
-  if constexpr (MODE == SEL_SLICE) {
-    cb = static_cast<int32_t>(blockIdx.y) * a.slice_len;
-    C = min(a.slice_len, sh.c1 - sh.c0 - cb);
-    kk = min(a.k, C);
-  } else if constexpr (MODE == SEL_LIST) {
-    C = a.n_slices * a.k;
-  }
-  const float* sc = a.scores + static_cast<int64_t>(g) * sh.P + sh.c0 + cb;  // candidate 0
-  const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * a.k;
-  uint64_t* outk = a.slice_keys + list0 + static_cast<int64_t>(blockIdx.y) * a.k;
+  const int32_t kst = batch.k > 0 ? batch.k : 1;
+  int32_t* out = it.sel + static_cast<int64_t>(g) * kst;
+  const int32_t C = sh.c1 - sh.c0, kk = sh.kk;
+  const float* sc = it.scores + static_cast<int64_t>(g) * sh.P + sh.c0;  // candidate 0
 
   if (tid == 0) {
     s_nan = 0;
@@ -271,12 +584,21 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
     s_minkey = KEY_NONE;
   }
   __syncthreads();
-  if constexpr (MODE == SEL_LIST) {
-    if (tid < a.n_slices && a.slice_nan[g * SLICE_MAX + tid]) s_nan = 1;
-  }
-
-  // smallest (code, position) over the workgroup -> s_minkey and its slot
-  auto publish_min = [&](uint64_t mk, int32_t mpos) {
+  bool nan = false;
+  if (kk > 0 && kk == C) {
+    uint64_t mk = KEY_NONE;
+    int32_t mpos = 0x7FFFFFFF;
+    for (int32_t i = tid; i < C; i += SEL_THREADS) {
+      const float x = sc[i];
+      nan |= score_is_nan(x);
+      out[i] = sh.c0 + i;
+      const uint64_t key = make_key(score_code(x), sh.c0 + i);
+      if (key < mk) {
+        mk = key;
+        mpos = sh.c0 + i;
+      }
+    }
+    if (nan) s_nan = 1;
     wave_min_key(mk, mpos);
     if ((tid & (WAVE - 1)) == 0) {
       s_wmk[wid] = mk;
@@ -292,205 +614,62 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
       s_minkey = mk;
       s_minslot = sh.s_eff + (mpos - sh.c0);
     }
-  };
-  // where the kept candidate of rank idx goes
-  auto emit = [&](uint32_t idx, int32_t pos, uint32_t code) {
-    if constexpr (MODE == SEL_SLICE)
-      outk[idx] = make_key(code, pos);
-    else
-      out[idx] = pos;
-  };
-
-  if (kk > 0 && VPT > 0) {
-    // ---- codes (and list positions) into registers: thread-contiguous
-    // blocks of L = 2^lg entries ----------------------------------------------
-    int lg = 0;
-    while ((SEL_THREADS << lg) < C) ++lg;
-    const int32_t L = 1 << lg;
-    uint32_t code[LMAX];
-    int32_t lpos[MODE == SEL_LIST ? LMAX : 1];
-    if constexpr (MODE == SEL_LIST) {
-      // coalesced loads of the keys, transposed through LDS like the codes
-      uint64_t* st64 = reinterpret_cast<uint64_t*>(stage);
-      const uint64_t* lk = a.slice_keys + list0;
-      constexpr int U = 16;
-      for (int32_t i0 = tid; i0 < C; i0 += SEL_THREADS * U) {
-        uint64_t x[U];
+  } else if (kk > 0) {
+    uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
+    const int shifts[3] = {SH0, SH1, 0}, nbins[3] = {NB0, NB1, NB2};
 #pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = lk[min(i0 + u * SEL_THREADS, C - 1)];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int32_t i = i0 + u * SEL_THREADS;
-          if (i < C) st64[(i >> lg) * (L + 1) + (i & (L - 1))] = x[u];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < LMAX; ++j) {
-        const uint64_t key = (j < L) ? st64[tid * (L + 1) + j] : 0ull;
-        code[j] = static_cast<uint32_t>(key >> 32);
-        lpos[j] = static_cast<int32_t>(static_cast<uint32_t>(key));
-      }
-    } else {
-      const bool nan = stage_codes<LMAX>(sc, C, lg, stage);
-      if (nan) s_nan = 1;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < LMAX; ++j) code[j] = (j < L) ? stage[tid * (L + 1) + j] : 0u;
+    for (int ps = 0; ps < 3; ++ps) {
+      auto visit = [&](auto&& f) { stream_codes<16>(sc, C, ps == 0, &nan, f); };
+      radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
+                 &s_above, &s_neq);
+      krem -= s_above;
+      prefix |= s_bin << shifts[ps];
+      mask |= static_cast<uint32_t>(nbins[ps] - 1) << shifts[ps];
     }
-    const int32_t lo = min(tid * L, C), hi = min(lo + L, C);  // workgroup-relative
-    auto for_each = [&](auto&& f) {
+    if (nan) s_nan = 1;
+    const uint32_t thr = prefix;
+    const uint32_t drop = s_neq - krem;
+    uint32_t gt_base = 0, eq_base = 0;
+    for (int32_t t0 = 0; t0 < C; t0 += SEL_THREADS * TL) {
+      const int32_t n = min(SEL_THREADS * TL, C - t0);
+      stage_codes<16>(sc + t0, n, TILE_LG, stage);
+      __syncthreads();
+      uint32_t tcode[TL];
 #pragma unroll
-      for (int j = 0; j < LMAX; ++j) {
-        if (lo + j < hi) {
-          int32_t pos;
-          if constexpr (MODE == SEL_LIST)
-            pos = lpos[j];
-          else
-            pos = sh.c0 + cb + lo + j;
-          f(lo + j, pos, code[j]);
-        }
-      }
-    };
-
-    if (kk == C) {
-      // every candidate is kept: positions in order; the least important one
-      // is the smallest (code, position)
-      uint64_t mk = KEY_NONE;
-      int32_t mpos = 0x7FFFFFFF;
-      for_each([&](int32_t r, int32_t i, uint32_t o) {
-        emit(static_cast<uint32_t>(r), i, o);
-        const uint64_t key = make_key(o, i);
-        if (key < mk) {
-          mk = key;
-          mpos = i;
-        }
-      });
-      if constexpr (MODE != SEL_SLICE) publish_min(mk, mpos);
-    } else {
-      // ---- radix select of the kk-th largest code: three digits --------
-      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
-      auto visit = [&](auto&& f) { for_each([&](int32_t, int32_t, uint32_t o) { f(o); }); };
-      const int shifts[3] = {SH0, SH1, 0}, nbins[3] = {HBINS, HBINS, LAST};
-#pragma unroll
-      for (int ps = 0; ps < 3; ++ps) {
-        radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
-                   &s_above, &s_neq);
-        krem -= s_above;
-        prefix |= s_bin << shifts[ps];
-        mask |= static_cast<uint32_t>(nbins[ps] - 1) << shifts[ps];
-      }
-      // ---- ordered compaction: codes above the threshold, then the newest
-      // krem tokens carrying it (ties: the older ones lose) ------------------
-      const uint32_t thr = prefix;
-      const uint32_t drop = s_neq - krem;
+      for (int j = 0; j < TL; ++j) tcode[j] = stage[tid * (TL + 1) + j];
+      const int32_t lo = min(tid * TL, n), hi = min(lo + TL, n);  // tile-relative
       uint32_t gt = 0, eq = 0;
-      for_each([&](int32_t, int32_t, uint32_t o) {
-        gt += o > thr;
-        eq += o == thr;
-      });
+#pragma unroll
+      for (int j = 0; j < TL; ++j)
+        if (lo + j < hi) {
+          gt += tcode[j] > thr;
+          eq += tcode[j] == thr;
+        }
       uint32_t tot;
       const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
-      uint32_t eq_before = ex >> 16, gt_before = ex & 0xFFFFu;
-      for_each([&](int32_t, int32_t i, uint32_t o) {
-        const bool is_gt = o > thr, is_eq = o == thr;
-        if (is_gt || (is_eq && eq_before >= drop)) {
-          const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
-          emit(idx, i, o);
-          if (is_eq && eq_before == drop) {  // the least important kept token
-            s_minslot = sh.s_eff + static_cast<int32_t>(idx);
-            s_minkey = make_key(thr, i);
-          }
-        }
-        gt_before += is_gt;
-        eq_before += is_eq;
-      });
-    }
-  } else if (kk > 0) {
-    // ---- SEL_HEAD, long prompts: stream the scores on every pass -----------
-    bool nan = false;
-    if (kk == C) {
-      uint64_t mk = KEY_NONE;
-      int32_t mpos = 0x7FFFFFFF;
-      for (int32_t i = tid; i < C; i += SEL_THREADS) {
-        const float x = sc[i];
-        nan |= score_is_nan(x);
-        out[i] = sh.c0 + i;
-        const uint64_t key = make_key(score_code(x), sh.c0 + i);
-        if (key < mk) {
-          mk = key;
-          mpos = sh.c0 + i;
-        }
-      }
-      if (nan) s_nan = 1;
-      publish_min(mk, mpos);
-    } else {
-      uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk);
-      const int shifts[3] = {SH0, SH1, 0}, nbins[3] = {HBINS, HBINS, LAST};
+      uint32_t eq_before = eq_base + (ex >> 16), gt_before = gt_base + (ex & 0xFFFFu);
 #pragma unroll
-      for (int ps = 0; ps < 3; ++ps) {
-        auto visit = [&](auto&& f) { stream_codes<16>(sc, C, ps == 0, &nan, f); };
-        radix_pass(visit, prefix, mask, shifts[ps], nbins[ps], krem, hist, scan_buf, &s_bin,
-                   &s_above, &s_neq);
-        krem -= s_above;
-        prefix |= s_bin << shifts[ps];
-        mask |= static_cast<uint32_t>(nbins[ps] - 1) << shifts[ps];
-      }
-      if (nan) s_nan = 1;
-      const uint32_t thr = prefix;
-      const uint32_t drop = s_neq - krem;
-      // ordered compaction in tiles of 32 candidates per thread, staged
-      // through LDS so that each thread walks a contiguous block
-      constexpr int TL = 1 << TILE_LG;
-      uint32_t gt_base = 0, eq_base = 0;
-      for (int32_t t0 = 0; t0 < C; t0 += SEL_THREADS * TL) {
-        const int32_t n = min(SEL_THREADS * TL, C - t0);
-        stage_codes<16>(sc + t0, n, TILE_LG, stage);
-        __syncthreads();
-        uint32_t tcode[TL];
-#pragma unroll
-        for (int j = 0; j < TL; ++j) tcode[j] = stage[tid * (TL + 1) + j];
-        const int32_t lo = min(tid * TL, n), hi = min(lo + TL, n);  // tile-relative
-        uint32_t gt = 0, eq = 0;
-#pragma unroll
-        for (int j = 0; j < TL; ++j)
-          if (lo + j < hi) {
-            gt += tcode[j] > thr;
-            eq += tcode[j] == thr;
-          }
-        uint32_t tot;
-        const uint32_t ex = block_exclusive_scan_u32<SEL_THREADS>((eq << 16) | gt, scan_buf, &tot);
-        uint32_t eq_before = eq_base + (ex >> 16), gt_before = gt_base + (ex & 0xFFFFu);
-#pragma unroll
-        for (int j = 0; j < TL; ++j) {
-          if (lo + j < hi) {
-            const uint32_t o = tcode[j];
-            const int32_t i = sh.c0 + t0 + lo + j;
-            const bool is_gt = o > thr, is_eq = o == thr;
-            if (is_gt || (is_eq && eq_before >= drop)) {
-              const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
-              out[idx] = i;
-              if (is_eq && eq_before == drop) {
-                s_minslot = sh.s_eff + static_cast<int32_t>(idx);
-                s_minkey = make_key(thr, i);
-              }
+      for (int j = 0; j < TL; ++j) {
+        if (lo + j < hi) {
+          const uint32_t o = tcode[j];
+          const int32_t i = sh.c0 + t0 + lo + j;
+          const bool is_gt = o > thr, is_eq = o == thr;
+          if (is_gt || (is_eq && eq_before >= drop)) {
+            const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
+            out[idx] = i;
+            if (is_eq && eq_before == drop) {
+              s_minslot = sh.s_eff + static_cast<int32_t>(idx);
+              s_minkey = make_key(thr, i);
             }
-            gt_before += is_gt;
-            eq_before += is_eq;
           }
+          gt_before += is_gt;
+          eq_before += is_eq;
         }
-        gt_base += tot & 0xFFFFu;
-        eq_base += tot >> 16;
-        __syncthreads();  // the stage is refilled by the next tile
       }
+      gt_base += tot & 0xFFFFu;
+      eq_base += tot >> 16;
+      __syncthreads();  // the stage is refilled by the next tile
     }
-  }
-  if constexpr (MODE == SEL_SLICE) {
-    // pad the slice's list to k entries with the smallest key; record NaNs
-    for (int32_t j = kk + tid; j < a.k; j += SEL_THREADS) outk[j] = 0ull;
-    __syncthreads();
-    if (tid == 0) a.slice_nan[g * SLICE_MAX + blockIdx.y] = s_nan ? 1 : 0;
-    return;
   }
   __syncthreads();
   if (tid == 0) {
@@ -502,7 +681,7 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
     c.minkey = s_minkey;
     c.flags = s_nan ? 1 : 0;
     c.leave_slot = sh.leave;
-    a.ctl[g] = c;
+    (batch.ctl + it.head0)[g] = c;
   }
 }
 
@@ -819,8 +998,7 @@ hipError_t launch_streaming(const Geometry& geo, const LayerView& all, const Pre
   sb.item[0] = select_item(it, pw.sel, pw);
   gb.item[0] = gather_item(it, pw.sel);
   const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads));
-  hipLaunchKernelGGL((prefill_select_kernel<0, SEL_HEAD, 1>), heads, dim3(SEL_THREADS), 0, stream,
-                     sb);
+  hipLaunchKernelGGL((prefill_select_stream_kernel<1>), heads, dim3(SEL_THREADS), 0, stream, sb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gather<1>(geo, gb, 1, stream);

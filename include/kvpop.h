@@ -141,8 +141,12 @@ KVPOP_API int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, si
  * finish using it.  NULL is a no-op. */
 KVPOP_API void kvpop_cache_destroy(kvpop_cache* cache);
 
-/* Mark (layer, seq) empty again (n = -1), stream-ordered.  The rows are not
- * cleared; they are unreachable until refilled. */
+/* Mark (layer, seq) empty again (n = -1).  Nothing is enqueued and `stream`
+ * is unused: a following non-empty prefill of the sequence writes its control
+ * blocks anyway, and any other call that reads them (decode of the layer,
+ * prune, state) first re-initialises them on its own stream.  The rows are
+ * not cleared; they are unreachable until refilled.  Errors: KVPOP_EINVAL
+ * (bad indices), KVPOP_ESTATE (poisoned). */
 KVPOP_API int kvpop_cache_reset(kvpop_cache* cache, int32_t layer, int32_t seq, void* stream);
 
 /* Prefill compaction: fill the empty (layer, seq) from an n_tokens-long

@@ -589,6 +589,69 @@ def test_state_machine_errors_and_reset():
     cache.close()
 
 
+def test_reset_is_applied_by_the_next_reader():
+    """A reset enqueues nothing: the next decode (or state read) of the layer
+    initialises the sequence's control blocks, a non-empty prefill overwrites
+    them.  Sequence 1 of a batch of 3 is reset mid-stream and restarts from an
+    empty prompt while sequences 0 and 2 carry on; then sequence 2 is reset and
+    refilled by a prefill."""
+    geo = Geo(8, 2, 64, 2, 12, 6)
+    B, P, T1, T2 = 3, 40, 25, 30
+    cache = make_cache(geo, batch=B)
+    streams = [Stream(geo, P + T1 + T2 + P, 40 + b) for b in range(B)]
+    orcs = [make_oracle(geo) for _ in range(B)]
+    for b in range(B):
+        s = streams[b]
+        cache.prefill_compact(0, b, to_dev_bf16(s.k[:, :P]), to_dev_bf16(s.v[:, :P]),
+                              to_dev_f32(s.scores[:, :P]))
+        orcs[b].prefill(s.k[:, :P], s.v[:, :P], s.scores[:, :P])
+    pos = [P] * B  # next position of each sequence
+    out = torch.empty((B, geo.n_q_heads, geo.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def step(last):
+        q = np.stack([streams[b].q[pos[b]] for b in range(B)])
+        kn = np.stack([streams[b].k[:, pos[b]] for b in range(B)])
+        vn = np.stack([streams[b].v[:, pos[b]] for b in range(B)])
+        sl = np.stack([streams[b].leaving(pos[b]) for b in range(B)])
+        cache.decode_step(0, to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn), to_dev_f32(sl), out)
+        got = out_to_f64(out)
+        for b in range(B):
+            s = streams[b]
+            ref = orcs[b].decode(s.q[pos[b]], s.k[:, pos[b]], s.v[:, pos[b]], s.leaving(pos[b]),
+                                 attend=last)
+            if last:
+                check_output(got[b], ref, f"seq {b} position {pos[b]}")
+            pos[b] += 1
+
+    for i in range(T1):
+        step(i == T1 - 1)
+    cache.reset(0, 1)
+    orcs[1] = make_oracle(geo)
+    pos[1] = 0
+    for i in range(T2):
+        step(i == T2 - 1)
+    for b in range(B):
+        _cmp_kept(cache.state(0, b), orcs[b], f"seq {b} after the reset of seq 1")
+    # reset + non-empty prefill: the prefill writes the blocks itself
+    cache.reset(0, 2)
+    s = streams[2]
+    cache.prefill_compact(0, 2, to_dev_bf16(s.k[:, :P]), to_dev_bf16(s.v[:, :P]),
+                          to_dev_f32(s.scores[:, :P]))
+    orcs[2] = make_oracle(geo)
+    orcs[2].prefill(s.k[:, :P], s.v[:, :P], s.scores[:, :P])
+    pos[2] = P
+    step(True)
+    for b in range(B):
+        _cmp_kept(cache.state(0, b), orcs[b], f"seq {b} after the refill of seq 2")
+    # reset + empty prompt, then the state: empty
+    cache.reset(0, 0)
+    cache.prefill_compact(0, 0, to_dev_bf16(s.k[:, :0]), to_dev_bf16(s.v[:, :0]),
+                          to_dev_f32(s.scores[:, :0]))
+    st = cache.state(0, 0)
+    assert st.n == -1 and all(int(c) == 0 for c in st.counts)
+    cache.close()
+
+
 def test_nan_score_sets_flag():
     geo = Geo(4, 1, 64, 2, 10, 4)
     cache = make_cache(geo)

@@ -149,7 +149,7 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   // first-level keys of long prompts: up to PREFILL_NB prompts, within 128 MiB
   // (all 36 layers of a 131k-token prompt at k = 1,788 take 66 MB)
   const size_t slice_one = size_t(c.n_kv_heads) * kvpop::SLICE_MAX *
-                           size_t(std::max(c.n_scored, 1)) * 8;
+                           size_t(kvpop::slice_stride(c.n_scored)) * 8;
   L->slice_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
                                                                 (size_t(128) << 20) / slice_one)));
   ok = ok && take(slice_one * size_t(L->slice_items), &L->slice_keys);
@@ -494,7 +494,7 @@ int kvpop_prefix_thresholds(kvpop_cache* cache, int32_t n_tokens, const float* s
   // the first-level prefill buffer (free between calls) holds the segment starts
   const kvpop::PrefillWork pw = cache->prefill_work();
   const int64_t ws_keys = int64_t(pw.slice_items) * c.n_kv_heads * kvpop::SLICE_MAX *
-                          std::max(c.n_scored, 1);
+                          kvpop::slice_stride(c.n_scored);
   hipError_t e = kvpop::launch_prefix_thresholds(cache->geo(), n_tokens, scores, thr,
                                                  pw.slice_keys, ws_keys,
                                                  static_cast<hipStream_t>(stream));

@@ -84,12 +84,16 @@ hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int
 // select in two levels: up to SLICE_MAX slices per head first keep their own
 // top k, then one workgroup per head selects from the union.
 constexpr int SLICE_MAX = 16;
+// A first-level slice may keep up to SLICE_SLACK entries beyond its top k
+// (whole histogram bins); its key list is padded to slice_stride(k).
+constexpr int SLICE_SLACK = 64;
+constexpr int32_t slice_stride(int32_t k) { return (k > 0 ? k : 1) + SLICE_SLACK; }
 // A batch of prompts shares launches, up to PREFILL_NB prompts per launch.
 constexpr int PREFILL_NB = 64;
 struct PrefillWork {
   int32_t* sel;          // [sel_items][Hkv][k] kept candidate positions
   int32_t sel_items;     // prompts the selection buffer holds (1 .. PREFILL_NB)
-  uint64_t* slice_keys;  // [slice_items][Hkv][SLICE_MAX][k] first-level keys
+  uint64_t* slice_keys;  // [slice_items][Hkv][SLICE_MAX][slice_stride(k)] first-level keys
   int32_t* slice_nan;    // [slice_items][Hkv][SLICE_MAX] first-level NaN flags
   int32_t slice_items;   // long prompts the first-level buffers hold (1 .. PREFILL_NB)
 };

@@ -327,11 +327,12 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
     cb = static_cast<int32_t>(blockIdx.y) * it.slice_len;
     C = min(it.slice_len, sh.c1 - sh.c0 - cb);
     kk = min(batch.k, C);
-  } else if constexpr (MODE == SEL_LIST) {
-    C = it.n_slices * batch.k;
   }
-  const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * batch.k;
-  uint64_t* outk = it.slice_keys + list0 + static_cast<int64_t>(blockIdx.y) * batch.k;
+  const int32_t ks = slice_stride(batch.k);  // entries per slice in the key lists
+  if constexpr (MODE == SEL_LIST) C = it.n_slices * ks;
+  const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * ks;
+  uint64_t* outk = it.slice_keys + list0 + static_cast<int64_t>(blockIdx.y) * ks;
+  int32_t n_out = kk;  // entries this workgroup emits
   const int32_t pos0 = sh.c0 + cb;  // position of entry 0 (not SEL_LIST)
 
   // ---- entries into registers (loads first, then the LDS set-up) -----------
@@ -395,7 +396,7 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
   };
   // where the kept entry of rank idx goes
   auto emit = [&](uint32_t idx, int32_t pos, uint32_t o) {
-    if (idx >= static_cast<uint32_t>(kk)) return;  // never taken: ranks are < kk
+    if (idx >= static_cast<uint32_t>(n_out)) return;  // never taken: ranks are < n_out
     if constexpr (MODE == SEL_SLICE)
       outk[idx] = make_key(o, pos);
     else
@@ -460,78 +461,92 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
     pass(hist + NB0, SH1, NB1 - 1, hist + NB0 + NB1, [&](const uint32_t* h, uint32_t kr) {
       block_find_bin<NB1>(h, kr, s_pick, s_wsum, s_lincl);
     });
-    pass(hist + NB0 + NB1, 0, NB2 - 1, static_cast<uint32_t*>(nullptr),
-         [&](const uint32_t* h, uint32_t kr) {
-           if (wid == 0) find_bin<NB2>(h, kr, s_pick);
-         });
-    // ---- ordered compaction: codes above thr, then the newest krem of those
-    // equal to it (the oldest `drop` tied entries lose) ----------------------
-    const uint32_t thr = prefix;
-    const uint32_t drop = neq - krem;
-    // only a threshold of 0 can tie with the padding; lane j collects row j's
-    // counts of this wave
-    uint32_t mycnt = 0;
+    // ---- ordered compaction.  Kept: entries `above` the cut, then the
+    // newest of those `tied` at it (the oldest `drop` tied entries lose).
+    // Ranks in position order: per register row, each wave's counts (16-bit
+    // halves: above, tied) go into a table whose exclusive prefix, row-major
+    // then wave, is the wave's base; a lane adds the ballot bits below it.
+    auto compact = [&](auto above, auto tied, uint32_t drop, uint32_t thr) {
+      uint32_t mycnt = 0;  // lane j: row j's counts of this wave
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const bool v = thr != 0u || j < nvalid;
-      const uint64_t gm = __builtin_amdgcn_ballot_w64(code[j] > thr);
-      const uint64_t em = __builtin_amdgcn_ballot_w64(v && code[j] == thr);
-      const uint32_t cnt = (static_cast<uint32_t>(__builtin_popcountll(em)) << 16) |
-                           static_cast<uint32_t>(__builtin_popcountll(gm));
-      mycnt = lane == j ? cnt : mycnt;
-    }
-    if (lane < VPT) s_tab[lane * NWAVE + wid] = mycnt;
-    __syncthreads();
-    if (wid == 0) {
-      // exclusive prefix of the table, row-major then wave: lane l owns
-      // entries l*E .. l*E+E-1 (16-bit halves: above thr, equal to thr)
-      constexpr int E = TAB / WAVE;
-      uint32_t t[E], sum = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        t[e] = s_tab[lane * E + e];
-        sum += t[e];
+      for (int j = 0; j < VPT; ++j) {
+        const uint64_t gm = __builtin_amdgcn_ballot_w64(above(j));
+        const uint64_t em = __builtin_amdgcn_ballot_w64(tied(j));
+        const uint32_t cnt = (static_cast<uint32_t>(__builtin_popcountll(em)) << 16) |
+                             static_cast<uint32_t>(__builtin_popcountll(gm));
+        mycnt = lane == j ? cnt : mycnt;
       }
-      uint32_t ex = wave_inclusive_scan_u32(sum) - sum;
+      if (lane < VPT) s_tab[lane * NWAVE + wid] = mycnt;
+      __syncthreads();
+      if (wid == 0) {
+        // lane l owns table entries l*E .. l*E+E-1
+        constexpr int E = TAB / WAVE;
+        uint32_t t[E], sum = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        s_tab[lane * E + e] = ex;
-        ex += t[e];
-      }
-    }
-    __syncthreads();
-    uint32_t base[VPT];  // uniform over the wave: kept in scalar registers
+        for (int e = 0; e < E; ++e) {
+          t[e] = s_tab[lane * E + e];
+          sum += t[e];
+        }
+        uint32_t ex = wave_inclusive_scan_u32(sum) - sum;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j)
-      base[j] = static_cast<uint32_t>(
-          __builtin_amdgcn_readfirstlane(static_cast<int>(s_tab[j * NWAVE + wid])));
-    int32_t min_rank = -1, min_pos = 0;  // the least important kept entry, if here
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const bool v = thr != 0u || j < nvalid;
-      const bool is_gt = code[j] > thr, is_eq = v && code[j] == thr;
-      const uint64_t gm = __builtin_amdgcn_ballot_w64(is_gt);
-      const uint64_t em = __builtin_amdgcn_ballot_w64(is_eq);
-      const uint32_t gt_before = (base[j] & 0xFFFFu) + lanes_below(gm);
-      const uint32_t eq_before = (base[j] >> 16) + lanes_below(em);
-      if (is_gt || (is_eq && eq_before >= drop)) {
-        const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
-        const int32_t pos = pos_of(j);
-        emit(idx, pos, code[j]);
-        if (is_eq && eq_before == drop) {
-          min_rank = static_cast<int32_t>(idx);
-          min_pos = pos;
+        for (int e = 0; e < E; ++e) {
+          s_tab[lane * E + e] = ex;
+          ex += t[e];
         }
       }
-    }
-    if (min_rank >= 0) {
-      s_minslot = sh.s_eff + min_rank;
-      s_minkey = make_key(thr, min_pos);
+      __syncthreads();
+      uint32_t base[VPT];  // uniform over the wave: kept in scalar registers
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        base[j] = static_cast<uint32_t>(
+            __builtin_amdgcn_readfirstlane(static_cast<int>(s_tab[j * NWAVE + wid])));
+      int32_t min_rank = -1, min_pos = 0;  // the least important kept entry, if here
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const bool is_gt = above(j), is_eq = tied(j);
+        const uint64_t gm = __builtin_amdgcn_ballot_w64(is_gt);
+        const uint64_t em = __builtin_amdgcn_ballot_w64(is_eq);
+        const uint32_t gt_before = (base[j] & 0xFFFFu) + lanes_below(gm);
+        const uint32_t eq_before = (base[j] >> 16) + lanes_below(em);
+        if (is_gt || (is_eq && eq_before >= drop)) {
+          const uint32_t idx = gt_before + (eq_before > drop ? eq_before - drop : 0u);
+          const int32_t pos = pos_of(j);
+          emit(idx, pos, code[j]);
+          if (is_eq && eq_before == drop) {
+            min_rank = static_cast<int32_t>(idx);
+            min_pos = pos;
+          }
+        }
+      }
+      if (min_rank >= 0) {
+        s_minslot = sh.s_eff + min_rank;
+        s_minkey = make_key(thr, min_pos);
+      }
+    };
+    // A slice may keep whole bins: every entry whose code reaches the pass-2
+    // bin, a superset of its top kk by neq - krem <= SLICE_SLACK entries (the
+    // second level selects exactly, in position order, from the union).
+    bool superset = false;
+    if constexpr (MODE == SEL_SLICE) superset = neq - krem <= static_cast<uint32_t>(SLICE_SLACK);
+    if (superset) {
+      const uint32_t cut = prefix;  // low 8 bits 0: codes in or above the bin
+      n_out = kk - static_cast<int32_t>(krem) + static_cast<int32_t>(neq);
+      compact([&](int j) { return (cut != 0u || j < nvalid) && code[j] >= cut; },
+              [&](int) { return false; }, 0u, cut);
+    } else {
+      pass(hist + NB0 + NB1, 0, NB2 - 1, static_cast<uint32_t*>(nullptr),
+           [&](const uint32_t* h, uint32_t kr) {
+             if (wid == 0) find_bin<NB2>(h, kr, s_pick);
+           });
+      const uint32_t thr = prefix;
+      // only a threshold of 0 can tie with the padding
+      compact([&](int j) { return code[j] > thr; },
+              [&](int j) { return (thr != 0u || j < nvalid) && code[j] == thr; }, neq - krem, thr);
     }
   }
   if constexpr (MODE == SEL_SLICE) {
-    // pad the slice's list to k entries with the smallest key; record NaNs
-    for (int32_t j = kk + tid; j < batch.k; j += SEL_THREADS) outk[j] = 0ull;
+    // pad the slice's list to its stride with the smallest key; record NaNs
+    for (int32_t j = n_out + tid; j < ks; j += SEL_THREADS) outk[j] = 0ull;
     __syncthreads();
     if (tid == 0) it.slice_nan[g * SLICE_MAX + blockIdx.y] = s_nan ? 1 : 0;
     return;
@@ -935,7 +950,7 @@ struct LongPlan {
 
 LongPlan long_plan(const Geometry& geo, const PrefillShape& sh) {
   const int32_t C = sh.c1 - sh.c0;
-  const int64_t k64 = geo.n_scored;
+  const int64_t k64 = slice_stride(geo.n_scored);  // the second level holds n_slices of these
   const int32_t ns16 = (C + 16383) / 16384, ns32 = (C + 32767) / 32768;
   if (sh.kk < C && ns16 <= SLICE_MAX && ns16 * k64 <= 16384) return {16, ns16, 16384};
   if (sh.kk < C && ns32 <= SLICE_MAX && ns32 * k64 <= 16384) return {32, ns32, 32768};
@@ -949,7 +964,8 @@ hipError_t launch_two_level(const Geometry& geo, const LayerView& all,
                             const PrefillItem* const* its, int32_t m, const PrefillWork& pw,
                             hipStream_t stream) {
   const int64_t kcap = geo.n_scored > 0 ? geo.n_scored : 1;
-  const int64_t slice_one = static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX * kcap;
+  const int64_t slice_one =
+      static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX * slice_stride(geo.n_scored);
   SelectBatch<NB> sb;
   GatherBatch<NB> gb;
   fill_shared(sb, gb, geo, all);

@@ -8,23 +8,25 @@
 // token leaves it, per the card's "Delayed scoring").
 //
 // Two kernels per call:
-//   select  one 1024-thread workgroup per KV head; each thread owns a
-//           contiguous block of candidate positions (kept in registers when
-//           it is at most 32 long).  A radix select with 12, 12 and 8-bit
-//           digits over the order-preserving score codes (one 4096-bin LDS
-//           histogram) finds the threshold code and how many tokens carrying
-//           it survive; one workgroup scan of per-thread (greater, equal)
-//           counts then places every code above the threshold and the newest
-//           of the tied ones, writing the kept positions in ascending order
-//           plus the head's control block (count, min key and its slot).
+//   select  one 1024-thread workgroup per KV head; entry i of the head's
+//           candidates sits in thread i % 1024, register i / 1024 (up to 16
+//           or 32 per thread).  A radix select with 12, 12 and 8-bit digits
+//           over the order-preserving score codes finds the threshold code
+//           and how many tokens carrying it survive (the newest); the kept
+//           positions get ranks from per-wave ballots, and the head's control
+//           block (count, min key and its slot) is written.  Prompts longer
+//           than the registers hold select in two levels (slices, then their
+//           union) or, failing that, stream the scores on every pass.
 //   gather  many 256-thread workgroups per head copy the kept K/V rows into
 //           slots [0, count) with 16-byte coalesced loads/stores and write
 //           per-slot position and key, and the window ring.
 // A batch of (layer, sequence) prompts shares one select and one gather
 // launch: the grid's z is the prompt, each reading its own descriptor from
 // the kernel arguments (up to PREFILL_NB = 64 per launch, 3.6 KB of arguments).
-// Slot layout after prefill: sinks, then selected candidates in ascending
-// position, then the window in ascending position.
+// Slot layout after prefill: sinks, then the selected candidates in
+// ascending position (with at most 64 tied at the threshold code: those
+// above it in ascending position, then the kept ties in ascending
+// position), then the window in ascending position.
 #include <hip/hip_runtime.h>
 
 #include "kvpop_device.h"
@@ -305,6 +307,8 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
   __shared__ uint32_t s_wsum[NWAVE];
   __shared__ uint32_t s_pick[3];
   __shared__ uint32_t s_nan;
+  __shared__ int32_t s_tpos[WAVE];  // sparse ties: their positions, unordered
+  __shared__ uint32_t s_ntie;
   __shared__ int32_t s_minslot;
   __shared__ uint64_t s_minkey;
   __shared__ uint64_t s_wmk[NWAVE];
@@ -539,9 +543,39 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
              if (wid == 0) find_bin<NB2>(h, kr, s_pick);
            });
       const uint32_t thr = prefix;
-      // only a threshold of 0 can tie with the padding
-      compact([&](int j) { return code[j] > thr; },
-              [&](int j) { return (thr != 0u || j < nvalid) && code[j] == thr; }, neq - krem, thr);
+      const uint32_t drop = neq - krem;
+      if (MODE != SEL_SLICE && neq <= static_cast<uint32_t>(WAVE) && thr != 0u) {
+        // Few ties (and none with the padding): the entries above thr take
+        // ranks 0 .. kk-krem-1 in position order, the kept ties the ranks
+        // after them, ordered by position by wave 0 from a list of at most
+        // 64.  A final selection's ranks (cache slots) only have to be
+        // distinct and reproducible; a first-level slice keeps position
+        // order, which the second level's tie order relies on.
+        if (tid == 0) s_ntie = 0;
+        compact([&](int j) { return code[j] > thr; }, [&](int) { return false; }, 0u, thr);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+          if (code[j] == thr) s_tpos[atomicAdd(&s_ntie, 1u)] = pos_of(j);
+        __syncthreads();
+        if (wid == 0) {
+          const uint32_t n = s_ntie;  // == neq
+          const int32_t mine = lane < static_cast<int>(n) ? s_tpos[lane] : 0x7FFFFFFF;
+          uint32_t rank = 0;
+          for (uint32_t t = 0; t < n; ++t) rank += s_tpos[t] < mine ? 1u : 0u;
+          if (lane < static_cast<int>(n) && rank >= drop) {
+            const uint32_t idx = static_cast<uint32_t>(kk) - krem + (rank - drop);
+            emit(idx, mine, thr);
+            if (rank == drop) {  // the least important kept entry
+              s_minslot = sh.s_eff + static_cast<int32_t>(idx);
+              s_minkey = make_key(thr, mine);
+            }
+          }
+        }
+      } else {
+        // only a threshold of 0 can tie with the padding
+        compact([&](int j) { return code[j] > thr; },
+                [&](int j) { return (thr != 0u || j < nvalid) && code[j] == thr; }, drop, thr);
+      }
     }
   }
   if constexpr (MODE == SEL_SLICE) {

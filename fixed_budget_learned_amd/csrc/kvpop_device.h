@@ -24,6 +24,11 @@ __device__ __forceinline__ uint32_t score_code(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score of an order code (the inverse of score_code; -0 comes back as +0).
+__device__ __forceinline__ float code_value(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 __device__ __forceinline__ bool score_is_nan(float s) {
   return (__float_as_uint(s) & 0x7FFFFFFFu) > 0x7F800000u;
 }

@@ -52,6 +52,7 @@ constexpr int THR_THREADS = 1024;
 constexpr int THR_ARR = 1024;      // entrants one chunk can hold
 constexpr int THR_VMAX = 4;        // candidates per thread
 constexpr int THR_ETARGET = 192;   // expected entrants per chunk
+constexpr int THR_BUCKET = 64;     // segment starts: largest bucket ranked by counting
 
 // Segment plan of a prompt: candidate ranges [b[j], b[j+1]) for j < S.
 struct ThrPlan {
@@ -126,9 +127,11 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     uint64_t* __restrict__ ws) {
   constexpr int NWAVE = THR_THREADS / WAVE;
   __shared__ uint32_t hist[4096];
+  __shared__ uint32_t cur[4096];
   __shared__ uint64_t keys[THR_KMAX];
+  __shared__ uint64_t keys2[THR_KMAX];
   __shared__ uint32_t scan_buf[NWAVE + 1];
-  __shared__ uint32_t s_bin, s_above, s_neq, s_n;
+  __shared__ uint32_t s_bin, s_above, s_neq, s_n, s_cmax, s_bmax;
   __shared__ int32_t s_pcut;
   const int j = blockIdx.x;
   const int g = blockIdx.y;
@@ -204,11 +207,16 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
       }
     }
   }
-  if (tid == 0) s_n = 0u;
+  if (tid == 0) {
+    s_n = 0u;
+    s_cmax = 0u;
+    s_bmax = 0u;
+  }
   __syncthreads();
   const int32_t pcut = s_pcut;
 
   // ---- gather the k keys that reach the k-th largest key ------------------
+  uint32_t cmax = 0;  // this thread's largest kept code
   stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
     const bool keep = i < b && (o > t || (o == t && i >= pcut));
     const uint64_t m = __ballot(keep);
@@ -220,16 +228,85 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
         const uint32_t below = __builtin_amdgcn_mbcnt_hi(
             static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
         keys[base + below] = make_key(o, s + i);
+        cmax = o > cmax ? o : cmax;
       }
     }
   });
+  uint64_t* dst = ws + (static_cast<int64_t>(g) * plan.S + j) * k;
+  // the largest kept code: a wave maximum, then one LDS atomic per wave
+#pragma unroll
+  for (int d = WAVE / 2; d >= 1; d >>= 1) {
+    const uint32_t y = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cmax), d, WAVE));
+    cmax = y > cmax ? y : cmax;
+  }
+  if (lane == 0) atomicMax(&s_cmax, cmax);
+
+  // ---- sort the k keys ascending.  Buckets: 4096 equal ranges of the
+  // scores from the threshold's up to the largest kept one (of the codes,
+  // when either is not finite); a key's place is its bucket's start plus its
+  // rank among the (few) keys of its bucket.  A bucket of more than
+  // THR_BUCKET keys (many equal scores) sends the sort to a bitonic network.
+  for (int i = tid; i < 4096; i += THR_THREADS) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t cmx = s_cmax;
+  const float vlo = code_value(t), vhi = code_value(cmx);
+  const float scale = 4096.0f / (vhi - vlo);
+  const bool by_value = __builtin_isfinite(vlo) && __builtin_isfinite(vhi) && vhi > vlo &&
+                        __builtin_isfinite(scale);
+  const uint32_t span = cmx - t;
+  const int sh = span >> 12 ? 20 - __builtin_clz(span) : 0;  // (code - t) >> sh < 4096
+  // monotone in the code: the order of the buckets is the order of the keys
+  auto bucket = [&](uint32_t o) -> uint32_t {
+    if (by_value) {
+      const float f = (code_value(o) - vlo) * scale;
+      return f < 4095.0f ? static_cast<uint32_t>(f) : 4095u;
+    }
+    return (o - t) >> sh;
+  };
+  for (int32_t i = tid; i < k; i += THR_THREADS)
+    atomicAdd(&hist[bucket(static_cast<uint32_t>(keys[i] >> 32))], 1u);
+  __syncthreads();
+  {
+    // thread t owns buckets 4t .. 4t+3: hist <- starts, cur <- cursors
+    uint32_t c[4], sum = 0, mx = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hist[4 * tid + q];
+      sum += c[q];
+      mx = c[q] > mx ? c[q] : mx;
+    }
+    uint32_t tot;
+    uint32_t ex = block_exclusive_scan_u32<THR_THREADS>(sum, scan_buf, &tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hist[4 * tid + q] = ex;
+      cur[4 * tid + q] = ex;
+      ex += c[q];
+    }
+    atomicMax(&s_bmax, mx);
+  }
+  __syncthreads();
+  if (s_bmax <= static_cast<uint32_t>(THR_BUCKET)) {
+    for (int32_t i = tid; i < k; i += THR_THREADS) {
+      const uint64_t key = keys[i];
+      keys2[atomicAdd(&cur[bucket(static_cast<uint32_t>(key >> 32))], 1u)] = key;
+    }
+    __syncthreads();
+    for (int32_t i = tid; i < k; i += THR_THREADS) {
+      const uint64_t key = keys2[i];
+      const uint32_t d = bucket(static_cast<uint32_t>(key >> 32));
+      const uint32_t lo = hist[d], hi = cur[d];  // the bucket, now filled
+      uint32_t rank = 0;
+      for (uint32_t x = lo; x < hi; ++x) rank += keys2[x] < key ? 1u : 0u;
+      dst[lo + rank] = key;
+    }
+    return;
+  }
   int32_t p2 = 1;
   while (p2 < k) p2 <<= 1;
-  __syncthreads();
   for (int32_t i = k + tid; i < p2; i += THR_THREADS) keys[i] = ~0ull;  // sorts past the keys
   __syncthreads();
   bitonic_sort_lds(keys, p2);
-  uint64_t* dst = ws + (static_cast<int64_t>(g) * plan.S + j) * k;
   for (int32_t i = tid; i < k; i += THR_THREADS) dst[i] = keys[i];
 }
 

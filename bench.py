@@ -32,6 +32,9 @@ if ROOT not in sys.path:
 
 METRIC = "decode steps/sec + achieved HBM GB/s, 4032-entry/head cache, Qwen3-8B layer shapes"
 HBM_PEAK_GBPS = 8000.0
+# one 32-bit VALU operation per lane per clock: 157.3 TFLOP/s of packed fp32
+# FMA is 4 flops per lane-clock, so 39.3 T lane-operations per second
+ALU_PEAK_GOPS = 157.3e3 / 4
 PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_kernel_qwen3_8b_layer_4x_traffic.json")
 PROFILE_PMC_B64 = os.path.join(ROOT, "profiles", "decode_kernel_batched_serving_b64_traffic.json")
 
@@ -546,9 +549,25 @@ def prefix_thresholds_rate(w, reps: int):
     cache.close()
     us = e0.elapsed_time(e1) * 1e3 / reps
     nbytes = Hkv * (P - w.n_sink - w.n_recent) * 4 + Hkv * P * 8
+    # Compute side: a streaming top-k compares every candidate with the
+    # current threshold and inserts each entrant into the sorted k kept keys
+    # (ceil(log2 k) compares).  Entrants: k * (1 + ln(C / k)) for candidates
+    # in random order (the expected number of prefix top-k changes).
+    import math
+    C, k = P - w.n_sink - w.n_recent, w.n_scored
+    entrants = k * (1 + math.log(C / k)) if C > k else C
+    compares = Hkv * (C + entrants * math.ceil(math.log2(max(k, 2))))
+    gops = compares / (us * 1e-6) / 1e9
     return {"workload": w.name, "prompt_len": P, "us_per_call": us,
-            "positions_per_s": P / (us * 1e-6), "GBps": nbytes / (us * 1e-6) / 1e9,
-            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "bytes": nbytes}
+            "positions_per_s": P / (us * 1e-6),
+            "roofline": {"bound": "alu", "achieved": gops, "peak": ALU_PEAK_GOPS,
+                         "unit": "G compares/s", "frac": gops / ALU_PEAK_GOPS,
+                         "work_per_call": compares,
+                         "note": "latency-bound: per (segment, KV head) one workgroup sweeps "
+                                 "its candidates in dependent chunks; neither compares, LDS nor "
+                                 "HBM bytes bind it"},
+            "hbm": {"GBps": nbytes / (us * 1e-6) / 1e9,
+                    "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "bytes": nbytes}}
 
 
 def future_target_rate(w, reps: int):

@@ -292,50 +292,67 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 //
 // Occupancy hint: two 1024-thread workgroups per compute unit (8 waves per
 // SIMD, at most 64 registers) for 16 entries per thread.
-template <int VPT, int MODE, int NB>
-__global__ __launch_bounds__(SEL_THREADS)
-__attribute__((amdgpu_waves_per_eu(VPT == 16 ? 8 : 1)))
-void prefill_select_kernel(SelectBatch<NB> batch) {
+// LDS of one register-select workgroup.
+template <int VPT>
+struct SelLds {
+  static constexpr int NWAVE = SEL_THREADS / WAVE;
+  __align__(16) uint32_t hist[NB0 + NB1 + NB2];
+  uint32_t tab[VPT * NWAVE];
+  uint32_t lincl[SEL_THREADS];
+  uint32_t wsum[NWAVE];
+  uint32_t pick[3];
+  uint32_t nan;
+  int32_t tpos[WAVE];  // sparse ties: their positions, unordered
+  uint32_t ntie;
+  int32_t minslot;
+  uint64_t minkey;
+  uint64_t wmk[NWAVE];
+  int32_t wmp[NWAVE];
+};
+
+// One register-select workgroup: KV head g of prompt `it` (SEL_SLICE: its
+// slice y).  ctl: the cache-wide control blocks; s, k, W: sinks, scored
+// slots, window.
+template <int VPT, int MODE>
+__device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restrict__ ctl,
+                                          int32_t s_sink, int32_t k_sc, int32_t W_rec, int g,
+                                          int y, SelLds<VPT>& L) {
   static_assert(VPT == 16 || VPT == 32, "register select: 16 or 32 entries per thread");
   static_assert(MODE != SEL_LIST || VPT == 16, "list mode: at most 16 keys per thread");
   constexpr int NWAVE = SEL_THREADS / WAVE;
   constexpr int HTOT = NB0 + NB1 + NB2;
   constexpr int TAB = VPT * NWAVE;
-  __shared__ __align__(16) uint32_t hist[HTOT];
-  __shared__ uint32_t s_tab[TAB];
-  __shared__ uint32_t s_lincl[SEL_THREADS];
-  __shared__ uint32_t s_wsum[NWAVE];
-  __shared__ uint32_t s_pick[3];
-  __shared__ uint32_t s_nan;
-  __shared__ int32_t s_tpos[WAVE];  // sparse ties: their positions, unordered
-  __shared__ uint32_t s_ntie;
-  __shared__ int32_t s_minslot;
-  __shared__ uint64_t s_minkey;
-  __shared__ uint64_t s_wmk[NWAVE];
-  __shared__ int32_t s_wmp[NWAVE];
+  uint32_t* hist = L.hist;
+  uint32_t* s_tab = L.tab;
+  uint32_t* s_lincl = L.lincl;
+  uint32_t* s_wsum = L.wsum;
+  uint32_t* s_pick = L.pick;
+  uint32_t& s_nan = L.nan;
+  int32_t* s_tpos = L.tpos;
+  uint32_t& s_ntie = L.ntie;
+  int32_t& s_minslot = L.minslot;
+  uint64_t& s_minkey = L.minkey;
+  uint64_t* s_wmk = L.wmk;
+  int32_t* s_wmp = L.wmp;
 
-  const SelectItem& it = batch.item[blockIdx.z];
-  // a batch launch covers its longest prompt's slices: shorter ones have none here
-  if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= it.n_slices) return;
-  const PrefillShape sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
-  const int g = blockIdx.x;
+  const PrefillShape sh = prefill_shape(it.P, s_sink, k_sc, W_rec);
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wid = tid / WAVE;
-  const int32_t kst = batch.k > 0 ? batch.k : 1;  // stride of the per-head buffers
+  const int32_t kst = k_sc > 0 ? k_sc : 1;  // stride of the per-head buffers
   int32_t* out = it.sel + static_cast<int64_t>(g) * kst;
   // this workgroup's entries: candidates [cb, cb + C) of the head's range, or
   // (SEL_LIST) the head's first-level key list
   int32_t cb = 0, C = sh.c1 - sh.c0, kk = sh.kk;
   if constexpr (MODE == SEL_SLICE) {
-    cb = static_cast<int32_t>(blockIdx.y) * it.slice_len;
+    cb = y * it.slice_len;
     C = min(it.slice_len, sh.c1 - sh.c0 - cb);
-    kk = min(batch.k, C);
+    kk = min(k_sc, C);
   }
-  const int32_t ks = slice_stride(batch.k);  // entries per slice in the key lists
+  const int32_t ks = slice_stride(k_sc);  // entries per slice in the key lists
   if constexpr (MODE == SEL_LIST) C = it.n_slices * ks;
   const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * ks;
-  uint64_t* outk = it.slice_keys + list0 + static_cast<int64_t>(blockIdx.y) * ks;
+  uint64_t* outk = it.slice_keys + list0 + static_cast<int64_t>(y) * ks;
   int32_t n_out = kk;  // entries this workgroup emits
   const int32_t pos0 = sh.c0 + cb;  // position of entry 0 (not SEL_LIST)
 
@@ -582,7 +599,7 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
     // pad the slice's list to its stride with the smallest key; record NaNs
     for (int32_t j = n_out + tid; j < ks; j += SEL_THREADS) outk[j] = 0ull;
     __syncthreads();
-    if (tid == 0) it.slice_nan[g * SLICE_MAX + blockIdx.y] = s_nan ? 1 : 0;
+    if (tid == 0) it.slice_nan[g * SLICE_MAX + y] = s_nan ? 1 : 0;
     return;
   }
   __syncthreads();
@@ -595,8 +612,20 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
     c.minkey = s_minkey;
     c.flags = s_nan ? 1 : 0;
     c.leave_slot = sh.leave;
-    (batch.ctl + it.head0)[g] = c;
+    (ctl + it.head0)[g] = c;
   }
+}
+
+template <int VPT, int MODE, int NB>
+__global__ __launch_bounds__(SEL_THREADS)
+__attribute__((amdgpu_waves_per_eu(VPT == 16 ? 8 : 1)))
+void prefill_select_kernel(SelectBatch<NB> batch) {
+  __shared__ SelLds<VPT> L;
+  const SelectItem& it = batch.item[blockIdx.z];
+  // a batch launch covers its longest prompt's slices: shorter ones have none here
+  if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= it.n_slices) return;
+  select_wg<VPT, MODE>(it, batch.ctl, batch.s, batch.k, batch.W, static_cast<int>(blockIdx.x),
+                       static_cast<int>(blockIdx.y), L);
 }
 
 // Streaming select (SEL_HEAD, any prompt length): one workgroup per KV head
@@ -745,14 +774,21 @@ struct GatherItem {
   int32_t P;
 };
 
-template <int NB>
-struct GatherBatch {
-  uint16_t* kc;          // cache-wide rows and slot metadata
+// Where gathered rows go: the cache-wide rows and slot metadata, and the
+// cache geometry.
+struct GatherDst {
+  uint16_t* kc;
   uint16_t* vc;
   uint64_t* keys;
   int32_t* pos;
   int32_t* ring;
-  int32_t s, k, W, budget, rows_per_block;
+  int32_t s, k, W, budget;
+};
+
+template <int NB>
+struct GatherBatch {
+  GatherDst dst;
+  int32_t rows_per_block;
   GatherItem item[NB];
 };
 
@@ -768,31 +804,31 @@ __device__ __forceinline__ void nt_store16(uint4 x, uint4* p) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
 }
 
-// One gather workgroup: 256 threads, D/8 lanes of 16 bytes per kept row.
-template <int D, int NB>
-__global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBatch<NB> batch) {
-  constexpr int LPR = D / 8;                   // lanes per row (16 B each)
-  constexpr int RPP = GATHER_THREADS / LPR;    // rows per pass
-  const GatherItem& it = batch.item[blockIdx.z];
-  const PrefillShape sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
-  const int32_t kcap = batch.k > 0 ? batch.k : 1;
-  const int32_t budget = batch.budget, W = batch.W, rows_per_block = batch.rows_per_block;
-  const int g = blockIdx.y;
+// Rows [r0, r1) of KV head g of prompt `it` into its slots, by NT threads
+// (D/8 lanes of 16 bytes per row; RPT rows per thread have their loads in
+// flight before their stores): K and V, and per slot its position and key;
+// window rows also enter the ring.
+template <int D, int NT, int RPT>
+__device__ __forceinline__ void gather_rows(const GatherItem& it, const GatherDst& d, int g,
+                                            int32_t r0, int32_t r1) {
+  constexpr int LPR = D / 8;        // lanes per row (16 B each)
+  constexpr int RPP = NT / LPR;     // rows per pass
+  const PrefillShape sh = prefill_shape(it.P, d.s, d.k, d.W);
+  const int32_t kcap = d.k > 0 ? d.k : 1;
+  const int32_t budget = d.budget, W = d.W;
   const int tid = threadIdx.x;
   const int rg = tid / LPR;
   const int c = tid % LPR;
-  const int32_t r0 = blockIdx.x * rows_per_block;
-  const int32_t r1 = min(r0 + rows_per_block, sh.count);  // empty past this prompt's rows
   const uint16_t* __restrict__ k = it.k;
   const uint16_t* __restrict__ v = it.v;
   const float* __restrict__ scores = it.scores;
   const int32_t* __restrict__ sel = it.sel;
   const int64_t row0 = it.head0 * budget;
-  uint16_t* __restrict__ kc = batch.kc + row0 * D;
-  uint16_t* __restrict__ vc = batch.vc + row0 * D;
-  uint64_t* __restrict__ keys = batch.keys + row0;
-  int32_t* __restrict__ pos = batch.pos + row0;
-  int32_t* __restrict__ ring = batch.ring + it.head0 * W;
+  uint16_t* __restrict__ kc = d.kc + row0 * D;
+  uint16_t* __restrict__ vc = d.vc + row0 * D;
+  uint64_t* __restrict__ keys = d.keys + row0;
+  int32_t* __restrict__ pos = d.pos + row0;
+  int32_t* __restrict__ ring = d.ring + it.head0 * W;
 
   const uint4* ksrc = reinterpret_cast<const uint4*>(k + static_cast<int64_t>(g) * sh.P * D);
   const uint4* vsrc = reinterpret_cast<const uint4*>(v + static_cast<int64_t>(g) * sh.P * D);
@@ -801,7 +837,6 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBa
   const int32_t* selg = sel + static_cast<int64_t>(g) * kcap;
   const float* scg = scores + static_cast<int64_t>(g) * sh.P;
 
-  constexpr int RPT = 1;  // rows per thread per batch: loads issued before stores
   for (int32_t rb = r0 + rg; rb < r1; rb += RPT * RPP) {
     int32_t pos_r[RPT];
     bool scored_r[RPT];
@@ -844,6 +879,17 @@ __global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBa
       }
     }
   }
+}
+
+// One gather workgroup: 256 threads, rows_per_block rows of one head.
+template <int D, int NB>
+__global__ __launch_bounds__(GATHER_THREADS) void prefill_gather_kernel(GatherBatch<NB> batch) {
+  const GatherItem& it = batch.item[blockIdx.z];
+  const GatherDst& d = batch.dst;
+  const int32_t count = prefill_shape(it.P, d.s, d.k, d.W).count;
+  const int32_t r0 = static_cast<int32_t>(blockIdx.x) * batch.rows_per_block;
+  const int32_t r1 = min(r0 + batch.rows_per_block, count);  // empty past this prompt's rows
+  gather_rows<D, GATHER_THREADS, 1>(it, d, static_cast<int>(blockIdx.y), r0, r1);
 }
 
 __global__ void init_ctl_kernel(HeadCtl* __restrict__ ctl, int64_t n_heads,
@@ -906,15 +952,15 @@ template <int NB>
 void fill_shared(SelectBatch<NB>& sb, GatherBatch<NB>& gb, const Geometry& geo,
                  const LayerView& all) {
   sb.ctl = all.ctl;
-  sb.s = gb.s = geo.n_sink;
-  sb.k = gb.k = geo.n_scored;
-  sb.W = gb.W = geo.n_recent;
-  gb.kc = all.kc;
-  gb.vc = all.vc;
-  gb.keys = all.keys;
-  gb.pos = all.pos;
-  gb.ring = all.ring;
-  gb.budget = geo.budget;
+  sb.s = gb.dst.s = geo.n_sink;
+  sb.k = gb.dst.k = geo.n_scored;
+  sb.W = gb.dst.W = geo.n_recent;
+  gb.dst.kc = all.kc;
+  gb.dst.vc = all.vc;
+  gb.dst.keys = all.keys;
+  gb.dst.pos = all.pos;
+  gb.dst.ring = all.ring;
+  gb.dst.budget = geo.budget;
 }
 
 // Rows per gather workgroup: one pass of its threads, one row per thread

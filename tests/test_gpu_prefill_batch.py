@@ -129,6 +129,22 @@ def test_long_prompts_two_level_batched():
     _run(geo, 1, 6, prompts, 3, seed=23)
 
 
+def test_many_long_prompts():
+    """16 two-level prompts of 8 KV heads each (128 heads) in one call.
+    Compared with the oracle and, bit for bit, with one prompt at a time."""
+    geo = Geo(16, 8, 64, 4, 900, 32)
+    prompts = {(l, 0): 33000 + 1700 * l for l in range(16)}
+    _run(geo, 16, 1, prompts, 3, seed=37)
+
+
+def test_many_long_prompts_ties_d128():
+    """65 tie-heavy two-level prompts at head_dim 128 (the exact first level
+    where whole bins do not fit): one launch pair of 64, then one of 1."""
+    geo = Geo(2, 2, 128, 4, 600, 16)
+    prompts = {(0, b): 34000 + 977 * b for b in range(65)}
+    _run(geo, 1, 65, prompts, 2, seed=41, kind="ties", check_oracle=False)
+
+
 def test_long_prompts_small_slice_buffer_and_streaming():
     """Two-level prompts beyond what the first-level buffer holds at once
     (16), and, in another cache, a prompt only the streaming select can take."""

@@ -392,13 +392,12 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
       }
     }
   }
-  // Entries past C carry code 0 and are counted by the radix passes like any
-  // other; bin 0 of a pass starts at -n_pad (mod 2^32) whenever they match
-  // its prefix, so every count is exact once the pass's atomics are done.
-  const uint32_t n_pad = static_cast<uint32_t>(VPT * SEL_THREADS - C);
+  // Entries past C carry code 0.  Register rows at or past nrows hold only
+  // those and are skipped (a uniform test); in the last row a lane past C
+  // counts nothing.
+  const int nrows = (C + SEL_THREADS - 1) / SEL_THREADS;
   for (int i = tid; i < HTOT; i += SEL_THREADS) hist[i] = 0u;
   if (tid == 0) {
-    hist[0] = 0u - n_pad;
     s_nan = 0;
     s_minslot = -1;
     s_minkey = KEY_NONE;
@@ -461,10 +460,11 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
   } else if (kk > 0) {
     // ---- radix select of the kk-th largest code ---------------------------
     uint32_t prefix = 0, mask = 0, krem = static_cast<uint32_t>(kk), neq = 0;
-    auto pass = [&](uint32_t* h, int shift, uint32_t nbm1, uint32_t* h_next, auto find) {
+    auto pass = [&](uint32_t* h, int shift, uint32_t nbm1, auto find) {
 #pragma unroll
       for (int j = 0; j < VPT; ++j)
-        if ((code[j] & mask) == prefix) atomicAdd(&h[(code[j] >> shift) & nbm1], 1u);
+        if (j < nrows && j * SEL_THREADS + tid < C && (code[j] & mask) == prefix)
+          atomicAdd(&h[(code[j] >> shift) & nbm1], 1u);
       __syncthreads();
       find(h, krem);
       __syncthreads();
@@ -473,13 +473,11 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
       neq = s_pick[2];
       prefix |= bin << shift;
       mask |= nbm1 << shift;
-      // the padding (code 0) still matches: pre-subtract it from the next pass
-      if (h_next != nullptr && prefix == 0u && tid == 0) atomicSub(&h_next[0], n_pad);
     };
-    pass(hist, SH0, NB0 - 1, hist + NB0, [&](const uint32_t* h, uint32_t kr) {
+    pass(hist, SH0, NB0 - 1, [&](const uint32_t* h, uint32_t kr) {
       block_find_bin<NB0>(h, kr, s_pick, s_wsum, s_lincl);
     });
-    pass(hist + NB0, SH1, NB1 - 1, hist + NB0 + NB1, [&](const uint32_t* h, uint32_t kr) {
+    pass(hist + NB0, SH1, NB1 - 1, [&](const uint32_t* h, uint32_t kr) {
       block_find_bin<NB1>(h, kr, s_pick, s_wsum, s_lincl);
     });
     // ---- ordered compaction.  Kept: entries `above` the cut, then the
@@ -491,6 +489,7 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
       uint32_t mycnt = 0;  // lane j: row j's counts of this wave
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
+        if (j >= nrows) break;
         const uint64_t gm = __builtin_amdgcn_ballot_w64(above(j));
         const uint64_t em = __builtin_amdgcn_ballot_w64(tied(j));
         const uint32_t cnt = (static_cast<uint32_t>(__builtin_popcountll(em)) << 16) |
@@ -524,6 +523,7 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
       int32_t min_rank = -1, min_pos = 0;  // the least important kept entry, if here
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
+        if (j >= nrows) break;
         const bool is_gt = above(j), is_eq = tied(j);
         const uint64_t gm = __builtin_amdgcn_ballot_w64(is_gt);
         const uint64_t em = __builtin_amdgcn_ballot_w64(is_eq);
@@ -555,7 +555,7 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
       compact([&](int j) { return (cut != 0u || j < nvalid) && code[j] >= cut; },
               [&](int) { return false; }, 0u, cut);
     } else {
-      pass(hist + NB0 + NB1, 0, NB2 - 1, static_cast<uint32_t*>(nullptr),
+      pass(hist + NB0 + NB1, 0, NB2 - 1,
            [&](const uint32_t* h, uint32_t kr) {
              if (wid == 0) find_bin<NB2>(h, kr, s_pick);
            });
@@ -572,7 +572,7 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
         compact([&](int j) { return code[j] > thr; }, [&](int) { return false; }, 0u, thr);
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
-          if (code[j] == thr) s_tpos[atomicAdd(&s_ntie, 1u)] = pos_of(j);
+          if (j < nrows && code[j] == thr) s_tpos[atomicAdd(&s_ntie, 1u)] = pos_of(j);
         __syncthreads();
         if (wid == 0) {
           const uint32_t n = s_ntie;  // == neq

@@ -20,7 +20,7 @@ constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t kc, vc, keys, pos, ring, ctl, sel, slice_keys, slice_nan, part_acc, part_ml, part_min,
+  size_t kc, vc, keys, pos, ring, ctl, sel, slice_keys, slice_meta, slice_tau, part_acc, part_ml, part_min,
       tickets, total;
   int32_t nsplit, rows_per_split, threads, rows_per_thread, finish_apart;
   int32_t sel_items;    // prompts one batched prefill launch can select at once
@@ -153,7 +153,9 @@ bool compute_layout(const kvpop_config& c, Layout* L) {
   L->slice_items = int32_t(std::max<size_t>(1, std::min<size_t>(kvpop::PREFILL_NB,
                                                                 (size_t(128) << 20) / slice_one)));
   ok = ok && take(slice_one * size_t(L->slice_items), &L->slice_keys);
-  ok = ok && take(size_t(L->slice_items) * c.n_kv_heads * kvpop::SLICE_MAX * 4, &L->slice_nan);
+  ok = ok && take(size_t(L->slice_items) * c.n_kv_heads * kvpop::SLICE_MAX *
+                       sizeof(kvpop::SliceMeta), &L->slice_meta);
+  ok = ok && take(size_t(L->slice_items) * c.n_kv_heads * 4, &L->slice_tau);
   const size_t parts = decode_parts(c);
   ok = ok && mul_ok(parts, G * size_t(c.head_dim) * 4, &tmp) && take(tmp, &L->part_acc);
   ok = ok && mul_ok(parts, G * 2 * 4, &tmp) && take(tmp, &L->part_ml);
@@ -233,7 +235,8 @@ struct kvpop_cache {
     pw.sel = reinterpret_cast<int32_t*>(base + lay.sel);
     pw.sel_items = lay.sel_items;
     pw.slice_keys = reinterpret_cast<uint64_t*>(base + lay.slice_keys);
-    pw.slice_nan = reinterpret_cast<int32_t*>(base + lay.slice_nan);
+    pw.slice_meta = reinterpret_cast<kvpop::SliceMeta*>(base + lay.slice_meta);
+    pw.slice_tau = reinterpret_cast<uint32_t*>(base + lay.slice_tau);
     pw.slice_items = lay.slice_items;
     return pw;
   }

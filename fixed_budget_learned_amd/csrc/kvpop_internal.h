@@ -81,20 +81,28 @@ struct DecodeWork {
 hipError_t launch_init_ctl(HeadCtl* ctl, int64_t n_heads, uint32_t* tickets, int64_t n_tickets,
                            hipStream_t stream);
 // Prefill workspace (one per cache; calls are stream-ordered).  Long prompts
-// select in two levels: up to SLICE_MAX slices per head first keep their own
-// top k, then one workgroup per head selects from the union.
+// select in two levels: up to SLICE_MAX slices per head first keep a
+// superset of their share of the head's top k, then one workgroup per head
+// selects from the union.
 constexpr int SLICE_MAX = 16;
-// A first-level slice may keep up to SLICE_SLACK entries beyond its top k
-// (whole histogram bins); its key list is padded to slice_stride(k).
+// A first-level slice keeps at most slice_stride(k) entries: its top k plus
+// up to SLICE_SLACK more (whole histogram bins), or every entry at or above
+// the head's sampled threshold when there are no more than that.
 constexpr int SLICE_SLACK = 64;
 constexpr int32_t slice_stride(int32_t k) { return (k > 0 ? k : 1) + SLICE_SLACK; }
+// What a first-level slice reports: a NaN seen, the keys it wrote, and how
+// many of its entries reach the head's sampled threshold.
+struct SliceMeta {
+  int32_t nan, n_out, n_ge, pad;
+};
 // A batch of prompts shares launches, up to PREFILL_NB prompts per launch.
 constexpr int PREFILL_NB = 64;
 struct PrefillWork {
   int32_t* sel;          // [sel_items][Hkv][k] kept candidate positions
   int32_t sel_items;     // prompts the selection buffer holds (1 .. PREFILL_NB)
   uint64_t* slice_keys;  // [slice_items][Hkv][SLICE_MAX][slice_stride(k)] first-level keys
-  int32_t* slice_nan;    // [slice_items][Hkv][SLICE_MAX] first-level NaN flags
+  SliceMeta* slice_meta; // [slice_items][Hkv][SLICE_MAX]
+  uint32_t* slice_tau;   // [slice_items][Hkv] sampled threshold codes
   int32_t slice_items;   // long prompts the first-level buffers hold (1 .. PREFILL_NB)
 };
 // One prompt to compact into an empty (layer, sequence).

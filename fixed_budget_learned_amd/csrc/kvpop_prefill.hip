@@ -160,18 +160,25 @@ __device__ __forceinline__ void radix_pass(Visit&& visit, uint32_t prefix, uint3
   __syncthreads();
 }
 
-
-
 // Select kernels.  1024 threads per workgroup; MODE:
 //   SEL_HEAD   one workgroup per KV head selects from all its candidates.
-//   SEL_SLICE  first level for long prompts: workgroup (head, slice) selects
-//              the top min(k, slice length) of a slice of the candidates and
-//              writes their keys, ascending in position, padded with key 0 to
-//              k entries.  The global top-k lies in the union of the slices'
-//              top-k, since a slice contributes at most k of it.
-//   SEL_LIST   second level: one workgroup per head selects the top k of that
-//              union (read as keys, in position order) and writes positions
-//              and the control block like SEL_HEAD.
+//   SEL_SLICE  first level for long prompts: workgroup (head, slice) writes
+//              the keys of a superset of the slice's share of the head's top
+//              k, ascending in position, and its SliceMeta.  With a sampled
+//              threshold tau for the head (prefill_tau_kernel), a slice whose
+//              entries at or above tau number at most slice_stride(k) keeps
+//              exactly those.  Otherwise it keeps its own top min(k, slice
+//              length), or every entry of the radix bin that holds its k-th
+//              largest when that overshoots by at most SLICE_SLACK.  A slice's
+//              own top k holds its share of the head's top k (it contributes
+//              at most k); the entries at or above tau hold it whenever at
+//              least k of the head's entries reach tau, since tau is then at
+//              or below the head's k-th largest code.
+//   SEL_LIST   second level: one workgroup per head reads the union of its
+//              slices' keys (in position order) and selects the top k, writing
+//              positions and the control block like SEL_HEAD.  When fewer than
+//              k of the head's entries reach tau, the workgroup first has
+//              each slice keep its own top k, one after another.
 constexpr int SEL_HEAD = 0, SEL_SLICE = 1, SEL_LIST = 2;
 
 // One prompt of a select launch.  head0: the cache-wide index of its
@@ -179,17 +186,20 @@ constexpr int SEL_HEAD = 0, SEL_SLICE = 1, SEL_LIST = 2;
 struct SelectItem {
   const float* scores;   // [Hkv][P]
   int32_t* sel;          // [Hkv][k] selection slot of the prompt
-  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][k] first-level slot of the prompt
-  int32_t* slice_nan;    // [Hkv][SLICE_MAX]
+  uint64_t* slice_keys;  // [Hkv][SLICE_MAX][slice_stride(k)] first-level slot of the prompt
+  SliceMeta* meta;       // [Hkv][SLICE_MAX]
   int64_t head0;
   int32_t P, n_slices, slice_len;
 };
 
 // Descriptors of the prompts of one launch (grid z = prompt), with what they
 // share; kept small enough for the kernel arguments.
+// tau: the sampled thresholds of prompt z at tau + z * Hkv, or null (no
+// sampling: the slices keep their own top k).
 template <int NB>
 struct SelectBatch {
   HeadCtl* ctl;          // cache-wide control blocks
+  uint32_t* tau;
   int32_t s, k, W;
   SelectItem item[NB];
 };
@@ -282,8 +292,8 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 // Entry i of the workgroup lives in thread i % 1024, register i / 1024, so
 // the loads go straight from coalesced reads into registers and each wave's
 // lanes hold consecutive entries of every register row.  Three radix passes
-// (12, 12 and 8-bit digits, histograms in LDS, all cleared while the loads
-// are in flight; wave 0 locates each pass's bin) find the kk-th largest code
+// (12, 12 and 8-bit digits, histograms in LDS, all cleared once at the
+// start; the workgroup locates each pass's bin) find the kk-th largest code
 // thr and how many entries carrying it are kept (the newest ones).  The
 // ordered compaction then ranks every kept entry in position order from
 // wave ballots: per register row, each wave's counts of codes above thr and
@@ -308,15 +318,19 @@ struct SelLds {
   uint64_t minkey;
   uint64_t wmk[NWAVE];
   int32_t wmp[NWAVE];
+  uint32_t total;              // rank table: the workgroup's totals
+  int32_t nout[SLICE_MAX];     // SEL_LIST: keys of each slice
+  int32_t cum[SLICE_MAX + 1];  // SEL_LIST: keys of the slices before each
 };
 
 // One register-select workgroup: KV head g of prompt `it` (SEL_SLICE: its
 // slice y).  ctl: the cache-wide control blocks; s, k, W: sinks, scored
-// slots, window.
+// slots, window; tau: the prompt's sampled thresholds or null.  Returns the
+// number of entries written (SEL_SLICE: keys; else the kept count).
 template <int VPT, int MODE>
-__device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restrict__ ctl,
-                                          int32_t s_sink, int32_t k_sc, int32_t W_rec, int g,
-                                          int y, SelLds<VPT>& L) {
+__device__ __forceinline__ int32_t select_wg(const SelectItem& it, HeadCtl* __restrict__ ctl,
+                                             const uint32_t* tau, int32_t s_sink, int32_t k_sc,
+                                             int32_t W_rec, int g, int y, SelLds<VPT>& L) {
   static_assert(VPT == 16 || VPT == 32, "register select: 16 or 32 entries per thread");
   static_assert(MODE != SEL_LIST || VPT == 16, "list mode: at most 16 keys per thread");
   constexpr int NWAVE = SEL_THREADS / WAVE;
@@ -350,11 +364,39 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
     kk = min(k_sc, C);
   }
   const int32_t ks = slice_stride(k_sc);  // entries per slice in the key lists
-  if constexpr (MODE == SEL_LIST) C = it.n_slices * ks;
   const int64_t list0 = (static_cast<int64_t>(g) * SLICE_MAX) * ks;
   uint64_t* outk = it.slice_keys + list0 + static_cast<int64_t>(y) * ks;
   int32_t n_out = kk;  // entries this workgroup emits
   const int32_t pos0 = sh.c0 + cb;  // position of entry 0 (not SEL_LIST)
+
+  // SEL_LIST: the union is slice y's n_out[y] keys at y * ks, for each y.
+  // With sampling, the entries of the union are numbered densely (L.cum:
+  // keys of the slices before each); slices that kept their own top k
+  // padded their lists to ks with key 0, which is read as it stands.
+  bool packed = false, any_nan = false;
+  if constexpr (MODE == SEL_LIST) {
+    const SliceMeta* mh = it.meta + static_cast<int64_t>(g) * SLICE_MAX;
+    for (int j = 0; j < it.n_slices; ++j) any_nan |= mh[j].nan != 0;
+    // tau is passed only when at least kk of the head's entries reach it
+    // (the kernel checks before calling)
+    packed = tau != nullptr;
+    if (tid < SLICE_MAX) L.nout[tid] = tid < it.n_slices ? mh[tid].n_out : 0;
+    if (packed) {
+      __syncthreads();
+      if (tid == 0) {
+        int32_t c = 0;
+        for (int j = 0; j < SLICE_MAX; ++j) {
+          L.cum[j] = c;
+          c += L.nout[j];
+        }
+        L.cum[SLICE_MAX] = c;
+      }
+      __syncthreads();
+      C = L.cum[SLICE_MAX];
+    } else {
+      C = it.n_slices * ks;
+    }
+  }
 
   // ---- entries into registers (loads first, then the LDS set-up) -----------
   // valid entries of this thread: registers 0 .. nvalid-1
@@ -365,13 +407,22 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
   if (kk > 0) {
     // range-checked buffer loads: entries past C read as 0
     if constexpr (MODE == SEL_LIST) {
+      const int32_t nbytes = it.n_slices * ks * 8;
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          it.slice_keys + list0, 0, C * 8, BUF_RSRC_WORD3);
+          it.slice_keys + list0, 0, nbytes, BUF_RSRC_WORD3);
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       u32x2 key[VPT];
+      int q = 0;  // packed: the slice of this thread's current entry
 #pragma unroll
-      for (int j = 0; j < VPT; ++j)
-        key[j] = __builtin_amdgcn_raw_buffer_load_b64(r, (j * SEL_THREADS + tid) * 8, 0, 0);
+      for (int j = 0; j < VPT; ++j) {
+        const int32_t e = j * SEL_THREADS + tid;  // entry of the union
+        int32_t a = e;                             // its place in the lists
+        if (packed && e < C) {
+          while (e >= L.cum[q + 1]) ++q;
+          a = q * ks + (e - L.cum[q]);
+        }
+        key[j] = __builtin_amdgcn_raw_buffer_load_b64(r, e < C ? a * 8 : nbytes, 0, 0);
+      }
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         code[j] = key[j].y;
@@ -405,8 +456,17 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
   __syncthreads();
   if (nan) s_nan = 1;
   if constexpr (MODE == SEL_LIST) {
-    if (tid < it.n_slices && it.slice_nan[g * SLICE_MAX + tid]) s_nan = 1;
+    if (any_nan) s_nan = 1;
   }
+  // SEL_SLICE with a sampled threshold: the slice's entries at or above it
+  // (n_ge of them); when no more than a key list holds, the slice keeps
+  // exactly those (by_tau).  Lanes past C carry code 0 and reach the
+  // threshold only if it is 0.
+  uint32_t t_cut = 0, n_ge = 0;
+  bool by_tau = false;
+  if constexpr (MODE == SEL_SLICE && VPT == 16)
+    if (tau != nullptr) t_cut = tau[g];
+  auto reaches = [&](int j) { return (t_cut != 0u || j < nvalid) && code[j] >= t_cut; };
 
   auto pos_of = [&](int j) -> int32_t {
     if constexpr (MODE == SEL_LIST)
@@ -426,6 +486,18 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
   if (kk > 0 && kk == C) {
     // every entry is kept, in order; the least important one is the smallest
     // (code, position)
+    if (MODE == SEL_SLICE && VPT == 16 && tau != nullptr) {
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if (j < nrows && reaches(j)) ++mine;
+      const uint32_t incl = wave_inclusive_scan_u32(mine);
+      if (lane == WAVE - 1) s_wsum[wid] = incl;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) n_ge += s_wsum[w];
+      __syncthreads();
+    }
     uint64_t mk = KEY_NONE;
     int32_t mpos = 0x7FFFFFFF;
 #pragma unroll
@@ -474,18 +546,14 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
       prefix |= bin << shift;
       mask |= nbm1 << shift;
     };
-    pass(hist, SH0, NB0 - 1, [&](const uint32_t* h, uint32_t kr) {
-      block_find_bin<NB0>(h, kr, s_pick, s_wsum, s_lincl);
-    });
-    pass(hist + NB0, SH1, NB1 - 1, [&](const uint32_t* h, uint32_t kr) {
-      block_find_bin<NB1>(h, kr, s_pick, s_wsum, s_lincl);
-    });
     // ---- ordered compaction.  Kept: entries `above` the cut, then the
     // newest of those `tied` at it (the oldest `drop` tied entries lose).
     // Ranks in position order: per register row, each wave's counts (16-bit
     // halves: above, tied) go into a table whose exclusive prefix, row-major
     // then wave, is the wave's base; a lane adds the ballot bits below it.
-    auto compact = [&](auto above, auto tied, uint32_t drop, uint32_t thr) {
+    // rank_table builds the table and returns the workgroup's totals (same
+    // packing); emit then places every kept entry.
+    auto rank_table = [&](auto above, auto tied) -> uint32_t {
       uint32_t mycnt = 0;  // lane j: row j's counts of this wave
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
@@ -507,14 +575,19 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
           t[e] = s_tab[lane * E + e];
           sum += t[e];
         }
-        uint32_t ex = wave_inclusive_scan_u32(sum) - sum;
+        const uint32_t incl = wave_inclusive_scan_u32(sum);
+        uint32_t ex = incl - sum;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           s_tab[lane * E + e] = ex;
           ex += t[e];
         }
+        if (lane == WAVE - 1) L.total = incl;
       }
       __syncthreads();
+      return L.total;
+    };
+    auto emit_ranked = [&](auto above, auto tied, uint32_t drop, uint32_t thr) {
       uint32_t base[VPT];  // uniform over the wave: kept in scalar registers
 #pragma unroll
       for (int j = 0; j < VPT; ++j)
@@ -544,63 +617,95 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
         s_minkey = make_key(thr, min_pos);
       }
     };
-    // A slice may keep whole bins: every entry whose code reaches the pass-2
-    // bin, a superset of its top kk by neq - krem <= SLICE_SLACK entries (the
-    // second level selects exactly, in position order, from the union).
-    bool superset = false;
-    if constexpr (MODE == SEL_SLICE) superset = neq - krem <= static_cast<uint32_t>(SLICE_SLACK);
-    if (superset) {
-      const uint32_t cut = prefix;  // low 8 bits 0: codes in or above the bin
-      n_out = kk - static_cast<int32_t>(krem) + static_cast<int32_t>(neq);
-      compact([&](int j) { return (cut != 0u || j < nvalid) && code[j] >= cut; },
-              [&](int) { return false; }, 0u, cut);
+    auto compact = [&](auto above, auto tied, uint32_t drop, uint32_t thr) {
+      rank_table(above, tied);
+      emit_ranked(above, tied, drop, thr);
+    };
+    if constexpr (MODE == SEL_SLICE && VPT == 16) {
+      if (tau != nullptr) {
+        // at most 16,384 entries: the count fits the low half
+        n_ge = rank_table(reaches, [&](int) { return false; }) & 0xFFFFu;
+        by_tau = n_ge <= static_cast<uint32_t>(ks);
+      }
+    }
+    if (by_tau) {
+      // every entry at or above the sampled threshold, in position order
+      n_out = static_cast<int32_t>(n_ge);
+      emit_ranked(reaches, [&](int) { return false; }, 0u, t_cut);
     } else {
-      pass(hist + NB0 + NB1, 0, NB2 - 1,
-           [&](const uint32_t* h, uint32_t kr) {
-             if (wid == 0) find_bin<NB2>(h, kr, s_pick);
-           });
-      const uint32_t thr = prefix;
-      const uint32_t drop = neq - krem;
-      if (MODE != SEL_SLICE && neq <= static_cast<uint32_t>(WAVE) && thr != 0u) {
-        // Few ties (and none with the padding): the entries above thr take
-        // ranks 0 .. kk-krem-1 in position order, the kept ties the ranks
-        // after them, ordered by position by wave 0 from a list of at most
-        // 64.  A final selection's ranks (cache slots) only have to be
-        // distinct and reproducible; a first-level slice keeps position
-        // order, which the second level's tie order relies on.
-        if (tid == 0) s_ntie = 0;
-        compact([&](int j) { return code[j] > thr; }, [&](int) { return false; }, 0u, thr);
-#pragma unroll
-        for (int j = 0; j < VPT; ++j)
-          if (j < nrows && code[j] == thr) s_tpos[atomicAdd(&s_ntie, 1u)] = pos_of(j);
-        __syncthreads();
-        if (wid == 0) {
-          const uint32_t n = s_ntie;  // == neq
-          const int32_t mine = lane < static_cast<int>(n) ? s_tpos[lane] : 0x7FFFFFFF;
-          uint32_t rank = 0;
-          for (uint32_t t = 0; t < n; ++t) rank += s_tpos[t] < mine ? 1u : 0u;
-          if (lane < static_cast<int>(n) && rank >= drop) {
-            const uint32_t idx = static_cast<uint32_t>(kk) - krem + (rank - drop);
-            emit(idx, mine, thr);
-            if (rank == drop) {  // the least important kept entry
-              s_minslot = sh.s_eff + static_cast<int32_t>(idx);
-              s_minkey = make_key(thr, mine);
+      pass(hist, SH0, NB0 - 1, [&](const uint32_t* h, uint32_t kr) {
+        block_find_bin<NB0>(h, kr, s_pick, s_wsum, s_lincl);
+      });
+      pass(hist + NB0, SH1, NB1 - 1, [&](const uint32_t* h, uint32_t kr) {
+        block_find_bin<NB1>(h, kr, s_pick, s_wsum, s_lincl);
+      });
+      // A slice may keep whole bins: every entry whose code reaches the pass-2
+      // bin, a superset of its top kk by neq - krem <= SLICE_SLACK entries (the
+      // second level selects exactly, in position order, from the union).
+      bool superset = false;
+      if constexpr (MODE == SEL_SLICE) superset = neq - krem <= static_cast<uint32_t>(SLICE_SLACK);
+      if (superset) {
+        const uint32_t cut = prefix;  // low 8 bits 0: codes in or above the bin
+        n_out = kk - static_cast<int32_t>(krem) + static_cast<int32_t>(neq);
+        compact([&](int j) { return (cut != 0u || j < nvalid) && code[j] >= cut; },
+                [&](int) { return false; }, 0u, cut);
+      } else {
+        pass(hist + NB0 + NB1, 0, NB2 - 1,
+             [&](const uint32_t* h, uint32_t kr) {
+               if (wid == 0) find_bin<NB2>(h, kr, s_pick);
+             });
+        const uint32_t thr = prefix;
+        const uint32_t drop = neq - krem;
+        if (MODE != SEL_SLICE && neq <= static_cast<uint32_t>(WAVE) && thr != 0u) {
+          // Few ties (and none with the padding): the entries above thr take
+          // ranks 0 .. kk-krem-1 in position order, the kept ties the ranks
+          // after them, ordered by position by wave 0 from a list of at most
+          // 64.  A final selection's ranks (cache slots) only have to be
+          // distinct and reproducible; a first-level slice keeps position
+          // order, which the second level's tie order relies on.
+          if (tid == 0) s_ntie = 0;
+          compact([&](int j) { return code[j] > thr; }, [&](int) { return false; }, 0u, thr);
+  #pragma unroll
+          for (int j = 0; j < VPT; ++j)
+            if (j < nrows && code[j] == thr) s_tpos[atomicAdd(&s_ntie, 1u)] = pos_of(j);
+          __syncthreads();
+          if (wid == 0) {
+            const uint32_t n = s_ntie;  // == neq
+            const int32_t mine = lane < static_cast<int>(n) ? s_tpos[lane] : 0x7FFFFFFF;
+            uint32_t rank = 0;
+            for (uint32_t t = 0; t < n; ++t) rank += s_tpos[t] < mine ? 1u : 0u;
+            if (lane < static_cast<int>(n) && rank >= drop) {
+              const uint32_t idx = static_cast<uint32_t>(kk) - krem + (rank - drop);
+              emit(idx, mine, thr);
+              if (rank == drop) {  // the least important kept entry
+                s_minslot = sh.s_eff + static_cast<int32_t>(idx);
+                s_minkey = make_key(thr, mine);
+              }
             }
           }
+        } else {
+          // only a threshold of 0 can tie with the padding
+          compact([&](int j) { return code[j] > thr; },
+                  [&](int j) { return (thr != 0u || j < nvalid) && code[j] == thr; }, drop, thr);
         }
-      } else {
-        // only a threshold of 0 can tie with the padding
-        compact([&](int j) { return code[j] > thr; },
-                [&](int j) { return (thr != 0u || j < nvalid) && code[j] == thr; }, drop, thr);
       }
     }
   }
   if constexpr (MODE == SEL_SLICE) {
-    // pad the slice's list to its stride with the smallest key; record NaNs
-    for (int32_t j = n_out + tid; j < ks; j += SEL_THREADS) outk[j] = 0ull;
+    // Without sampling, pad the list to its stride with the smallest key
+    // (the second level reads the lists whole); record what the slice did.
+    if (tau == nullptr)
+      for (int32_t j = n_out + tid; j < ks; j += SEL_THREADS) outk[j] = 0ull;
     __syncthreads();
-    if (tid == 0) it.slice_nan[g * SLICE_MAX + y] = s_nan ? 1 : 0;
-    return;
+    if (tid == 0) {
+      SliceMeta m;
+      m.nan = s_nan ? 1 : 0;
+      m.n_out = n_out;
+      m.n_ge = static_cast<int32_t>(n_ge);
+      m.pad = 0;
+      it.meta[static_cast<int64_t>(g) * SLICE_MAX + y] = m;
+    }
+    return n_out;
   }
   __syncthreads();
   if (tid == 0) {
@@ -614,6 +719,7 @@ __device__ __forceinline__ void select_wg(const SelectItem& it, HeadCtl* __restr
     c.leave_slot = sh.leave;
     (ctl + it.head0)[g] = c;
   }
+  return n_out;
 }
 
 template <int VPT, int MODE, int NB>
@@ -624,8 +730,87 @@ void prefill_select_kernel(SelectBatch<NB> batch) {
   const SelectItem& it = batch.item[blockIdx.z];
   // a batch launch covers its longest prompt's slices: shorter ones have none here
   if (MODE == SEL_SLICE && static_cast<int32_t>(blockIdx.y) >= it.n_slices) return;
-  select_wg<VPT, MODE>(it, batch.ctl, batch.s, batch.k, batch.W, static_cast<int>(blockIdx.x),
+  const int g = static_cast<int>(blockIdx.x);
+  const uint32_t* tau = (MODE != SEL_HEAD && batch.tau != nullptr)
+                            ? batch.tau + static_cast<int64_t>(blockIdx.z) * gridDim.x
+                            : nullptr;
+  if constexpr (MODE == SEL_LIST) {
+    if (tau != nullptr) {
+      // Fewer than kk of the head's entries reaching tau: the slices' keys
+      // may miss some of the top kk, so each slice keeps its own top kk
+      // (padded list) before the union is read.
+      const SliceMeta* mh = it.meta + static_cast<int64_t>(g) * SLICE_MAX;
+      int32_t n_ge = 0;
+      for (int j = 0; j < it.n_slices; ++j) n_ge += mh[j].n_ge;
+      if (n_ge < prefill_shape(it.P, batch.s, batch.k, batch.W).kk) {
+        for (int j = 0; j < it.n_slices; ++j) {
+          select_wg<VPT, SEL_SLICE>(it, batch.ctl, nullptr, batch.s, batch.k, batch.W, g, j, L);
+          __syncthreads();
+        }
+        tau = nullptr;
+      }
+    }
+  }
+  select_wg<VPT, MODE>(it, batch.ctl, tau, batch.s, batch.k, batch.W, g,
                        static_cast<int>(blockIdx.y), L);
+}
+
+// Sampled threshold of each KV head of two-level prompts, for the first
+// level (one workgroup per head).  The workgroup reads TAU_BLOCKS runs of
+// TAU_RUN consecutive candidates spread evenly over the head's range
+// (TAU_N = 4,096 codes, 4 per thread) and takes tau as the lower edge of the
+// 24-bit radix bin that holds their m-th largest code, m = n + 6 sqrt(n) + 16
+// with n = TAU_N * kk / C: the sample holds about n of the head's top kk, so
+// m exceeds that count by six standard deviations, and about m * C / TAU_N
+// entries of the head reach tau.  Nothing relies on the estimate: the
+// slices count the entries that reach tau and the second level checks that
+// at least kk do.  Two-level prompts have C > 32,768 candidates, so the runs
+// stay inside the range.
+constexpr int TAU_BLOCKS = 64, TAU_RUN = 64, TAU_N = TAU_BLOCKS * TAU_RUN;
+static_assert(TAU_N == 4 * SEL_THREADS, "four sampled codes per thread");
+
+template <int NB>
+__global__ __launch_bounds__(SEL_THREADS) void prefill_tau_kernel(SelectBatch<NB> batch) {
+  constexpr int NWAVE = SEL_THREADS / WAVE;
+  __shared__ __align__(16) uint32_t hist[NB0 + NB1];
+  __shared__ uint32_t s_lincl[SEL_THREADS];
+  __shared__ uint32_t s_wsum[NWAVE];
+  __shared__ uint32_t s_pick[3];
+  const SelectItem& it = batch.item[blockIdx.z];
+  const PrefillShape sh = prefill_shape(it.P, batch.s, batch.k, batch.W);
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t C = sh.c1 - sh.c0;
+  constexpr int TPR = TAU_RUN / 4;  // threads per run
+  const int64_t i0 = sh.c0 + static_cast<int64_t>(tid / TPR) * C / TAU_BLOCKS + (tid % TPR) * 4;
+  const float* src = it.scores + static_cast<int64_t>(g) * sh.P + i0;
+  float x[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = src[e];
+  for (int i = tid; i < NB0 + NB1; i += SEL_THREADS) hist[i] = 0u;
+  __syncthreads();
+  uint32_t code[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    code[e] = score_code(x[e]);
+    atomicAdd(&hist[code[e] >> SH0], 1u);
+  }
+  const float n = static_cast<float>(TAU_N) * static_cast<float>(sh.kk) / static_cast<float>(C);
+  const uint32_t m = min(static_cast<uint32_t>(ceilf(n + 6.f * sqrtf(n) + 16.f)),
+                         static_cast<uint32_t>(TAU_N));
+  __syncthreads();
+  block_find_bin<NB0>(hist, m, s_pick, s_wsum, s_lincl);
+  __syncthreads();
+  const uint32_t b0 = s_pick[0];
+  const uint32_t krem = m - s_pick[1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((code[e] >> SH0) == b0) atomicAdd(&hist[NB0 + ((code[e] >> SH1) & (NB1 - 1))], 1u);
+  __syncthreads();
+  block_find_bin<NB1>(hist + NB0, krem, s_pick, s_wsum, s_lincl);
+  __syncthreads();
+  if (tid == 0)
+    batch.tau[static_cast<int64_t>(blockIdx.z) * gridDim.x + g] = (b0 << SH0) | (s_pick[0] << SH1);
 }
 
 // Streaming select (SEL_HEAD, any prompt length): one workgroup per KV head
@@ -929,7 +1114,7 @@ SelectItem select_item(const PrefillItem& it, int32_t* sel, const PrefillWork& p
   si.scores = it.scores;
   si.sel = sel;
   si.slice_keys = pw.slice_keys;
-  si.slice_nan = pw.slice_nan;
+  si.meta = pw.slice_meta;
   si.head0 = it.head0;
   si.P = it.n_tokens;
   si.n_slices = 1;
@@ -952,6 +1137,7 @@ template <int NB>
 void fill_shared(SelectBatch<NB>& sb, GatherBatch<NB>& gb, const Geometry& geo,
                  const LayerView& all) {
   sb.ctl = all.ctl;
+  sb.tau = nullptr;
   sb.s = gb.dst.s = geo.n_sink;
   sb.k = gb.dst.k = geo.n_scored;
   sb.W = gb.dst.W = geo.n_recent;
@@ -1059,17 +1245,27 @@ hipError_t launch_two_level(const Geometry& geo, const LayerView& all,
     si.n_slices = lp.n_slices;
     si.slice_len = lp.slice_len;
     si.slice_keys = pw.slice_keys + i * slice_one;
-    si.slice_nan = pw.slice_nan + i * static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX;
+    si.meta = pw.slice_meta + i * static_cast<int64_t>(geo.n_kv_heads) * SLICE_MAX;
     max_slices = lp.n_slices > max_slices ? lp.n_slices : max_slices;
     gb.item[i] = gather_item(*its[i], sel);
+  }
+  const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads), 1u, static_cast<uint32_t>(m));
+  hipError_t e;
+  if (VPT == 16) {
+    // 16k slices filter by a sampled threshold.  The second level's
+    // fallback (each slice's own top k) runs on its 16 entries per thread,
+    // so 32k slices do not sample.
+    sb.tau = pw.slice_tau;
+    hipLaunchKernelGGL((prefill_tau_kernel<NB>), heads, dim3(SEL_THREADS), 0, stream, sb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const dim3 slices(static_cast<uint32_t>(geo.n_kv_heads), static_cast<uint32_t>(max_slices),
                     static_cast<uint32_t>(m));
   hipLaunchKernelGGL((prefill_select_kernel<VPT, SEL_SLICE, NB>), slices, dim3(SEL_THREADS), 0,
                      stream, sb);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 heads(static_cast<uint32_t>(geo.n_kv_heads), 1u, static_cast<uint32_t>(m));
   hipLaunchKernelGGL((prefill_select_kernel<16, SEL_LIST, NB>), heads, dim3(SEL_THREADS), 0,
                      stream, sb);
   e = hipGetLastError();

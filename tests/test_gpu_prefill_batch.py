@@ -27,12 +27,16 @@ def _gpu():
     torch.cuda.init()
 
 
-def _run(geo, n_layers, batch, prompts, steps, seed, kind="normal", check_oracle=True):
+def _run(geo, n_layers, batch, prompts, steps, seed, kind="normal", check_oracle=True,
+         tweak=None):
     """prompts: {(layer, seq): P}.  Fills one cache with a single batched call
     and another one prompt at a time, decodes `steps` steps on every layer
-    of both, and compares."""
+    of both, and compares.  tweak(P, stream) may edit a stream's scores."""
     streams = {key: Stream(geo, P + steps, seed + 97 * i, kind)
                for i, (key, P) in enumerate(sorted(prompts.items()))}
+    if tweak is not None:
+        for key, s in streams.items():
+            tweak(prompts[key], s)
     dev = {key: (to_dev_bf16(s.k[:, :prompts[key]]), to_dev_bf16(s.v[:, :prompts[key]]),
                  to_dev_f32(s.scores[:, :prompts[key]])) for key, s in streams.items()}
     log(f"batch prefill geo={geo} layers={n_layers} batch={batch} prompts={sorted(prompts.values())}")
@@ -153,3 +157,75 @@ def test_long_prompts_small_slice_buffer_and_streaming():
     _run(geo, 1, 18, prompts, 2, seed=29, check_oracle=False)
     geo = Geo(4, 1, 64, 4, 9000, 16)
     _run(geo, 1, 3, {(0, 0): 70000, (0, 1): 20000, (0, 2): 41000}, 2, seed=31)
+
+
+def _sampled_positions(geo, P):
+    """Candidates the sampled threshold of a two-level prompt reads: 64 runs of
+    64 consecutive candidates, run b starting floor(b * C / 64) into the
+    candidate range [s, P - W)."""
+    c0, C = geo.n_sink, P - geo.n_recent - geo.n_sink
+    return np.concatenate([c0 + (b * C) // 64 + np.arange(64) for b in range(64)])
+
+
+def test_sampled_threshold_reached_by_too_few():
+    """Head 0's sampled candidates score far above every other candidate, so
+    fewer than k candidates reach the sampled threshold: the slices' keys
+    would miss most of the top k, and every slice of that head must keep its
+    own top k instead.  Head 1 samples normally.  Against the oracle."""
+    geo = Geo(4, 2, 64, 4, 900, 32)
+
+    def boost(P, s):
+        s.scores[0, _sampled_positions(geo, P)] += 10.0
+
+    prompts = {(0, b): 33000 + 5000 * b for b in range(4)}
+    _run(geo, 1, 4, prompts, 3, seed=43, kind="uniform", tweak=boost)
+
+
+@pytest.mark.parametrize("kind", ["decreasing", "increasing"])
+def test_sampled_threshold_one_slice_holds_the_top(kind):
+    """Monotone scores put the whole top k in the first or the last slice:
+    that slice holds more entries at or above the sampled threshold than a
+    key list takes and keeps its own top k, while the other slices keep
+    none.  Against the oracle."""
+    geo = Geo(4, 2, 64, 4, 900, 32)
+    prompts = {(0, 0): 33001, (0, 1): 52000, (0, 2): 100000}
+    _run(geo, 1, 3, prompts, 3, seed=47, kind=kind)
+
+
+@pytest.mark.parametrize("kind", ["inf", "signed_zero_ties"])
+def test_sampled_threshold_at_special_codes(kind):
+    """Two-level prompts whose top k is all ties at +inf or 1.0 (a quarter of
+    the scores), with -inf, -0 and +0 below: the sampled threshold lands on
+    the tied code.  Against the oracle."""
+    geo = Geo(4, 2, 64, 4, 700, 32)
+    prompts = {(0, 0): 40000, (0, 1): 70000}
+    _run(geo, 1, 2, prompts, 3, seed=53, kind=kind)
+
+
+def test_nan_on_the_two_level_path():
+    """A NaN among a long prompt's candidates (one in a sampled run, one not)
+    sets the NaN flag, batched and one prompt at a time alike, and the kept
+    sets agree."""
+    geo = Geo(4, 2, 64, 4, 900, 32)
+    P = 60000
+    s = Stream(geo, P, 59)
+    sc = s.scores[:, :P].copy()
+    pos = _sampled_positions(geo, P)
+    sc[0, pos[1000]] = np.nan
+    sc[1, pos[2000] + 100] = np.nan
+    dev = (to_dev_bf16(s.k[:, :P]), to_dev_bf16(s.v[:, :P]), to_dev_f32(sc))
+    cb = make_cache(geo, n_layers=1, batch=2)
+    cb.prefill_compact_batch([(0, 0, *dev), (0, 1, *dev)])
+    cs = make_cache(geo)
+    cs.prefill_compact(0, 0, *dev)
+    torch.cuda.synchronize()
+    for st in (cb.state(0, 0), cb.state(0, 1), cs.state(0, 0)):
+        assert st.flags & abi.KVPOP_FLAG_NAN_SCORE
+        assert st.n == P - 1
+    ref = cs.state(0, 0)
+    for b in range(2):
+        st = cb.state(0, b)
+        for g in range(geo.n_kv_heads):
+            assert st.kept[g].tolist() == ref.kept[g].tolist(), (b, g)
+    cb.close()
+    cs.close()

@@ -62,6 +62,12 @@ CASES = [
      "signed_zero_ties", 0),
     ("dynamic_prunes", Geo(8, 2, 128, 4, 50, 16), [[120, 0], [300, 45], [80, 200]], 64,
      "normal", 9),
+    # more heads than the stream-order launch has workgroups (4 x 80 x 2 = 640)
+    ("many_heads_d64", Geo(4, 2, 64, 2, 40, 8),
+     [[int(x) for x in np.random.default_rng(l).integers(0, 120, 80)] for l in range(4)], 12,
+     "normal", 0),
+    # few heads with long slot ranges: every chunk its own workgroup, 25 partials per head
+    ("few_heads_long", Geo(8, 2, 128, 4, 1500, 64), [[3000], [1800]], 20, "normal", 0),
 ]
 
 

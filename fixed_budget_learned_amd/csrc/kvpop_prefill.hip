@@ -447,7 +447,14 @@ __device__ __forceinline__ int32_t select_wg(const SelectItem& it, HeadCtl* __re
   // those and are skipped (a uniform test); in the last row a lane past C
   // counts nothing.
   const int nrows = (C + SEL_THREADS - 1) / SEL_THREADS;
-  for (int i = tid; i < HTOT; i += SEL_THREADS) hist[i] = 0u;
+  static_assert(HTOT % 4 == 0, "histograms cleared in 16-byte pieces");
+  auto clear_hist = [&]() {
+    for (int i = tid; i < HTOT / 4; i += SEL_THREADS)
+      reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  };
+  // a sampled slice clears them only if it needs the radix passes
+  const bool sampled = MODE == SEL_SLICE && VPT == 16 && tau != nullptr;
+  if (!sampled) clear_hist();
   if (tid == 0) {
     s_nan = 0;
     s_minslot = -1;
@@ -626,6 +633,10 @@ __device__ __forceinline__ int32_t select_wg(const SelectItem& it, HeadCtl* __re
         // at most 16,384 entries: the count fits the low half
         n_ge = rank_table(reaches, [&](int) { return false; }) & 0xFFFFu;
         by_tau = n_ge <= static_cast<uint32_t>(ks);
+        if (!by_tau) {
+          clear_hist();
+          __syncthreads();
+        }
       }
     }
     if (by_tau) {

@@ -1,6 +1,10 @@
 """Build ``libkvpop.so`` in-tree with hipcc for gfx950.
 
-    python -m fixed_budget_learned_amd.build
+    python -m fixed_budget_learned_amd.build [--timeline]
+
+``--timeline`` builds ``libkvpop_timeline.so`` instead: the same library with
+the decode kernel's device-clock stamps compiled in (``-DKVPOP_TIMELINE``),
+read by ``python -m fixed_budget_learned_amd.timeline``.
 
 Every source is compiled every time (a few seconds per file); the objects go
 to ``_build/`` at the repository root and the library next to this file.
@@ -19,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkvpop.so")
+TIMELINE_LIB_PATH = os.path.join(PKG, "libkvpop_timeline.so")
 ARCH = "gfx950"
 
 SOURCES = ["kvpop_abi.cpp", "kvpop_prefill.hip", "kvpop_decode.hip", "kvpop_thresholds.hip",
@@ -56,24 +61,28 @@ def _run(cmd, verbose):
         print("\n".join(msgs), flush=True)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, timeline: bool = False) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = os.path.join(BUILD_DIR, "timeline") if timeline else BUILD_DIR
+    out = TIMELINE_LIB_PATH if timeline else LIB_PATH
+    extra = ["-DKVPOP_TIMELINE"] if timeline else []
+    os.makedirs(bdir, exist_ok=True)
     jobs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        jobs.append([hipcc] + COMMON_FLAGS + FILE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc] + COMMON_FLAGS + extra + FILE_FLAGS.get(src, []) + lang +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv[1:]))
+    print(build(verbose="-v" in sys.argv[1:], timeline="--timeline" in sys.argv[1:]))

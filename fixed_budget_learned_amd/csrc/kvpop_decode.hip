@@ -78,6 +78,29 @@ namespace kvpop {
 namespace {
 
 constexpr int MAX_SPLITS = 256;
+}  // namespace
+
+#ifdef KVPOP_TIMELINE
+// Timeline build only (-DKVPOP_TIMELINE): thread 0 of workgroup b records
+// the device clock (s_memrealtime, 100 MHz) at point i of the step in
+// timeline_stamps[b % TL_SLOTS][i]; kvpop_timeline_read copies them out.
+constexpr int TL_SLOTS = 4096, TL_POINTS = 8;
+__device__ uint64_t timeline_stamps[TL_SLOTS * TL_POINTS];
+#define TL_STAMP(i)                                                                   \
+  do {                                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    if (threadIdx.x == 0)                                                             \
+      timeline_stamps[(blockIdx.x % TL_SLOTS) * TL_POINTS + (i)] =                    \
+          __builtin_amdgcn_s_memrealtime();                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+  } while (0)
+#else
+#define TL_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
+
+namespace {
 
 // 16-byte non-temporal load (the K/V stream is read once per step).  On
 // batch 64 it raises the step from 5.9 to 6.6 TB/s; batch 1, whose layer
@@ -470,6 +493,7 @@ __device__ __forceinline__ void finish_head(const DecodeParams& p, int head, con
     if (lane == 0) fl.wmin[wid] = wm;
   }
   __syncthreads();
+  TL_STAMP(6);  // finisher: split factors and barrier
 
   // ---- accumulate this thread's columns over the splits
   const bool act = tid < NACT;
@@ -507,6 +531,10 @@ __device__ __forceinline__ void finish_head(const DecodeParams& p, int head, con
   write_ctl(p, head, dc, minkey, next_leave_slot(dc, ring_next, p.n_sink, W), tid == 0,
             mkey == minkey, static_cast<int32_t>(sraw));
   if (tid == 0) p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE] = 0u;
+#ifdef KVPOP_TIMELINE
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+  TL_STAMP(7);  // finisher done, its stores acknowledged
 }
 
 // One workgroup of 256 threads per (KV head, split).  K/V rows stream
@@ -541,6 +569,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wid = tid / WAVE;
+  TL_STAMP(0);
 
   // ---- workgroup -> (head, split); all splits of a head on one XCD when
   // the head count allows (workgroups are dealt to the 8 XCDs round robin),
@@ -743,6 +772,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
   }
 
+  TL_STAMP(1);  // wave 0's chunk loop done
   // ---- reduce the workgroup to one softmax state ---------------------------
   // Inside each wave: the row groups share m_run, so their accumulators add
   // plainly.  The transposing pair reductions leave lane l with NVF
@@ -792,6 +822,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     if (lane == 0) s_wmin[wid] = wm;
   }
   __syncthreads();
+  TL_STAMP(2);
 
   // ---- combine the waves: thread t owns columns [t * FPT, +FPT) ------------
   const uint64_t wg_minkey = min_u64(min_u64(s_wmin[0], s_wmin[1]), min_u64(s_wmin[2], s_wmin[3]));
@@ -888,6 +919,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     if (APART && split == 0 && tid == 0)
       __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(ring_next), r_min, 12, 0, 0);
   }
+  TL_STAMP(3);  // partial state stored (issued)
   if (APART) return;
 
   // ---- ticket: the last workgroup of the head finishes the step ------------
@@ -895,6 +927,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   // takes the ticket.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  TL_STAMP(4);  // every store of the workgroup acknowledged
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(
         &p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE], 1u, __ATOMIC_RELAXED,
@@ -902,6 +935,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     s_last = (prev == static_cast<uint32_t>(p.nsplit - 1)) ? 1 : 0;
   }
   __syncthreads();
+  TL_STAMP(5);  // ticket returned
   if (!s_last) return;
   finish_head<D, G, true>(p, head, dc, ring_next, s_fin);
 }
@@ -1001,3 +1035,21 @@ hipError_t launch_decode(const Geometry& geo, const LayerView& lv, const DecodeW
 }
 
 }  // namespace kvpop
+
+#ifdef KVPOP_TIMELINE
+// Timeline build only: copy the first n_slots workgroups' stamps
+// ([n_slots][8] device-clock ticks, 0 where a point was not reached) to
+// host memory, or zero them on the device.
+extern "C" __attribute__((visibility("default"))) int kvpop_timeline_read(uint64_t* host,
+                                                                         int n_slots) {
+  if (n_slots < 0 || n_slots > kvpop::TL_SLOTS) return -1;
+  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(kvpop::timeline_stamps),
+                                              size_t(n_slots) * kvpop::TL_POINTS * 8, 0,
+                                              hipMemcpyDeviceToHost));
+}
+extern "C" __attribute__((visibility("default"))) int kvpop_timeline_clear() {
+  static const uint64_t zero[kvpop::TL_SLOTS * kvpop::TL_POINTS] = {};
+  return static_cast<int>(hipMemcpyToSymbol(HIP_SYMBOL(kvpop::timeline_stamps), zero,
+                                            sizeof(zero), 0, hipMemcpyHostToDevice));
+}
+#endif

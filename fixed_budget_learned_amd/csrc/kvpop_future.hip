@@ -220,19 +220,37 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
           x[r] = (key <= my_q && key < T) ? x[r] : -INFINITY;
         }
       }
-      // the scale is positive: the largest scaled logit is the scaled maximum
-      float mx = -INFINITY;
+      // m is an anchor: the running maximum of the scaled logits when it last
+      // moved.  A tile adds 2^(c2 x - m) over its keys; when that passes
+      // 2^64 (some logit above m + 64) or no anchor is set yet, m moves to
+      // the running maximum and the tile is summed again.  The sum is the
+      // same up to rounding; most tiles skip the maximum.  The two lanes of
+      // a query (l and l ^ 32) hold the same m and part, so they branch
+      // together.
+      float part = 0.f;
+      if (m != -INFINITY) {
 #pragma unroll
-      for (int r = 0; r < 32; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * c2;
-      const float mnew = fmaxf(m, mx);
-      if (mnew != -INFINITY) {
-        float part = 0.f;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -mnew));
+        for (int r = 0; r < 32; ++r) part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -m));
         part += __shfl_xor(part, 32, WAVE);
-        ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
-        m = mnew;
+      }
+      if (m != -INFINITY && part <= 0x1p64f) {
+        ssum += part;
+      } else {
+        // the scale is positive: the largest scaled logit is the scaled maximum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) mx = fmaxf(mx, x[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * c2;
+        const float mnew = fmaxf(m, mx);
+        if (mnew != -INFINITY) {
+          part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 32; ++r)
+            part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -mnew));
+          part += __shfl_xor(part, 32, WAVE);
+          ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
+          m = mnew;
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -306,21 +324,29 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
       // every (query, key) pair of the tile counts when its first query is
       // at least W past this wave's last key and the tile ends before T
       const bool full = qrow0 >= jw + 31 + W && qrow0 + FT_TILE <= T && jw + 32 <= T;
-      const int32_t key0 = jw + 4 * (lane >> 5);
+      if (!full) {  // uniform: pairs that do not count get a logit of -inf (weight 0)
+        const int32_t key0 = jw + 4 * (lane >> 5);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int32_t qi = qrow0 + 32 * qb + (lane & 31);  // this lane's query
-        const float l2 = ltile[buf][32 * qb + (lane & 31)];
+        for (int qb = 0; qb < 2; ++qb) {
+          const int32_t qi = qrow0 + 32 * qb + (lane & 31);  // this lane's query
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f((qb == 0 ? acc0[r] : acc1[r]) * c2 - l2);
-          if (full) {
-            col[r] += p;
-          } else {
+          for (int r = 0; r < 16; ++r) {
             const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
-            col[r] += (qi < T && key < T && qi >= key + W) ? p : 0.f;
+            if (!(qi < T && key < T && qi >= key + W)) {
+              if (qb == 0)
+                acc0[r] = -INFINITY;
+              else
+                acc1[r] = -INFINITY;
+            }
           }
         }
+      }
+      // a multiply-add, an exp2 and an add per pair
+      const float l2a = ltile[buf][lane & 31], l2b = ltile[buf][32 + (lane & 31)];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        col[r] += __builtin_amdgcn_exp2f(acc0[r] * c2 - l2a);
+        col[r] += __builtin_amdgcn_exp2f(acc1[r] * c2 - l2b);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed

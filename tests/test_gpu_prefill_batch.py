@@ -229,3 +229,32 @@ def test_nan_on_the_two_level_path():
             assert st.kept[g].tolist() == ref.kept[g].tolist(), (b, g)
     cb.close()
     cs.close()
+
+
+def _random_long_cases(n, seed):
+    """Seeded long-prompt geometries: most on the sampled two-level path (k up to
+    what 16k slices allow), a few with larger k (32k slices or streaming)."""
+    rng = np.random.default_rng(seed)
+    kinds = ["uniform", "normal", "ties", "inf", "signed_zero_ties", "increasing", "decreasing"]
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        s = int(rng.choice([0, 1, 4]))
+        W = int(rng.choice([1, 16, 256]))
+        P = int(rng.integers(33000 + W + s, 140000))
+        C = P - W - s
+        ns16 = (C + 16383) // 16384
+        kmax = 16384 // ns16 - 64 if i % 4 else 6000
+        k = int(rng.integers(1, kmax))
+        cases.append((Geo(Hkv * G, Hkv, D, s, k, W), P, kinds[i % len(kinds)], 1000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("geo,P,kind,seed", _random_long_cases(14, 61),
+                         ids=[f"case{i}" for i in range(14)])
+def test_random_long_prompts_against_oracle(geo, P, kind, seed):
+    """Seeded random geometries and score kinds on long prompts, one prompt per
+    call and batched with a second prompt: kept sets against the oracle."""
+    _run(geo, 1, 2, {(0, 0): P, (0, 1): P // 2 + 1}, 2, seed=seed, kind=kind)

@@ -121,7 +121,6 @@ size_t decode_parts(const kvpop_config& c) {
 bool compute_layout(const kvpop_config& c, Layout* L) {
   const size_t budget = size_t(capacity_of(c));
   const size_t heads_all = size_t(c.n_layers) * c.batch * c.n_kv_heads;
-  const size_t heads = size_t(c.batch) * c.n_kv_heads;
   const size_t G = size_t(c.n_q_heads / c.n_kv_heads);
   choose_decode_shape(c, &L->nsplit, &L->rows_per_split, &L->threads, &L->rows_per_thread,
                       &L->finish_apart);
@@ -351,7 +350,6 @@ int kvpop_cache_create(const kvpop_config* cfg, void* device_arena, size_t arena
     c->owns = true;
   }
   const size_t heads_all = size_t(cfg->n_layers) * cfg->batch * cfg->n_kv_heads;
-  const size_t heads = size_t(cfg->batch) * cfg->n_kv_heads;
   hipError_t e = kvpop::launch_init_ctl(reinterpret_cast<kvpop::HeadCtl*>(c->base + L.ctl),
                                         int64_t(heads_all),
                                         reinterpret_cast<uint32_t*>(c->base + L.tickets),

@@ -251,7 +251,6 @@ __device__ __forceinline__ float xor4_add(float a, float b, bool hi) {
 // more than this many powers of two, so exponentials stay below 2^8 and the
 // accumulators are rescaled rarely.
 constexpr float RESCALE_SLACK = 8.f;
-constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
 
 // 2^x with the hardware instruction; no denormal range fix-up (results below
 // 2^-126 flush to zero, which the softmax weights tolerate).

@@ -53,6 +53,8 @@ constexpr int THR_ARR = 1024;      // entrants one chunk can hold
 constexpr int THR_VMAX = 4;        // candidates per thread
 constexpr int THR_ETARGET = 192;   // expected entrants per chunk
 constexpr int THR_BUCKET = 64;     // segment starts: largest bucket ranked by counting
+constexpr int THR_SAMPLE = 4096;   // segment starts: codes read for a sampled threshold
+constexpr int THR_SAMPLE_MIN = 16384;  // ... from prefixes of at least this many candidates
 
 // Segment plan of a prompt: candidate ranges [b[j], b[j+1]) for j < S.
 struct ThrPlan {
@@ -139,7 +141,107 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
   const int lane = tid & (WAVE - 1);
   const int32_t b = plan.b[j];                     // candidates [0, b), b >= k
   const float* __restrict__ sc = scores + static_cast<int64_t>(g) * P + s;
+  uint64_t* dst = ws + (static_cast<int64_t>(g) * plan.S + j) * k;
+  if (tid == 0) {
+    s_n = 0u;
+    s_cmax = 0u;
+    s_bmax = 0u;
+  }
 
+  // ---- long prefixes with a small kept fraction: a sampled threshold.  It
+  // is the lower edge of the 24-bit bin that holds the m-th largest of
+  // THR_SAMPLE codes read in 64 runs spread over the prefix, m = n + 4 sqrt(n)
+  // + 8 with n = THR_SAMPLE * k / b (about n of the sample are in the top
+  // k), so about m * b / THR_SAMPLE candidates reach it.  One pass keeps
+  // those (as keys) in LDS; when there are at least k of them and they fit,
+  // they hold the top k (every other key is below all of them), which the
+  // sort below places.  Otherwise the exact select runs as for any prefix.
+  uint32_t t = 0;     // every key of the sort is at or above code t
+  int32_t n = k;      // keys to sort; the top k of them are written
+  bool sampled = false;
+  const float nf = static_cast<float>(THR_SAMPLE) * static_cast<float>(k) / static_cast<float>(b);
+  const uint32_t m = min(static_cast<uint32_t>(ceilf(nf + 4.f * sqrtf(nf) + 8.f)),
+                         static_cast<uint32_t>(THR_SAMPLE));
+  // tried only where the expected survivors (m * b / THR_SAMPLE) fit the LDS
+  // key array with room to spare
+  if (b >= THR_SAMPLE_MIN &&
+      static_cast<int64_t>(m) * b <= static_cast<int64_t>(THR_KMAX) * THR_SAMPLE * 7 / 8) {
+    constexpr int TPR = THR_SAMPLE / 64 / 4;  // threads per run (4 codes each)
+    const int32_t i0 = static_cast<int32_t>(static_cast<int64_t>(tid / TPR) * b / 64) + (tid % TPR) * 4;
+    uint32_t code[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) code[e] = score_code(sc[i0 + e]);
+    uint32_t mrem = m, pre = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 20 : 8;
+      for (int i = tid; i < 4096; i += THR_THREADS) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (pass == 0 || (code[e] >> 20) == (pre >> 20)) atomicAdd(&hist[(code[e] >> shift) & 4095u], 1u);
+      __syncthreads();
+      uint32_t h[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = hist[4095 - 4 * tid - q];
+        sum += h[q];
+      }
+      uint32_t tot;
+      uint32_t ex = block_exclusive_scan_u32<THR_THREADS>(sum, scan_buf, &tot);
+      if (ex < mrem && mrem <= ex + sum) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (mrem <= ex + h[q]) {
+            s_bin = static_cast<uint32_t>(4095 - 4 * tid - q);
+            s_above = ex;
+            break;
+          }
+          ex += h[q];
+        }
+      }
+      __syncthreads();
+      mrem -= s_above;
+      pre |= s_bin << shift;
+    }
+    const uint32_t tau = pre;  // low 8 bits 0: codes in or above the bin
+    uint32_t cmax = 0;
+    stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
+      const bool keep = i < b && o >= tau;
+      const uint64_t msk = __ballot(keep);
+      if (msk != 0ull) {  // wavefront-uniform
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&s_n, static_cast<uint32_t>(__popcll(msk)));
+        base = __shfl(base, 0, WAVE);
+        if (keep) {
+          const uint32_t at = base + __builtin_amdgcn_mbcnt_hi(
+              static_cast<uint32_t>(msk >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(msk), 0u));
+          if (at < static_cast<uint32_t>(THR_KMAX)) keys[at] = make_key(o, s + i);
+          cmax = o > cmax ? o : cmax;
+        }
+      }
+    });
+#pragma unroll
+    for (int d = WAVE / 2; d >= 1; d >>= 1) {
+      const uint32_t y = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cmax), d, WAVE));
+      cmax = y > cmax ? y : cmax;
+    }
+    if (lane == 0) atomicMax(&s_cmax, cmax);
+    __syncthreads();
+    const uint32_t got = s_n;
+    if (got >= static_cast<uint32_t>(k) && got <= static_cast<uint32_t>(THR_KMAX)) {
+      sampled = true;
+      t = tau;
+      n = static_cast<int32_t>(got);
+    } else {
+      __syncthreads();  // every thread has read s_n
+      if (tid == 0) {
+        s_n = 0u;
+        s_cmax = 0u;
+      }
+    }
+  }
+
+  if (!sampled) {
   // ---- radix select of the k-th largest code: 12-, 12- and 8-bit digits.
   // The wide first digit (sign, exponent, 3 mantissa bits) spreads the codes
   // of real-valued scores over many bins; with 8 bits most fell into a few
@@ -182,7 +284,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     prefix |= s_bin << shift;
     mask |= static_cast<uint32_t>(nb - 1) << shift;
   }
-  const uint32_t t = prefix;               // the k-th largest code
+  t = prefix;                              // the k-th largest code
   const uint32_t drop = s_neq - krem;      // ties at t that lose (the oldest)
 
   // ---- the first kept tie, in position order: rank `drop` among ties ------
@@ -207,11 +309,6 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
       }
     }
   }
-  if (tid == 0) {
-    s_n = 0u;
-    s_cmax = 0u;
-    s_bmax = 0u;
-  }
   __syncthreads();
   const int32_t pcut = s_pcut;
 
@@ -232,7 +329,6 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
       }
     }
   });
-  uint64_t* dst = ws + (static_cast<int64_t>(g) * plan.S + j) * k;
   // the largest kept code: a wave maximum, then one LDS atomic per wave
 #pragma unroll
   for (int d = WAVE / 2; d >= 1; d >>= 1) {
@@ -240,6 +336,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     cmax = y > cmax ? y : cmax;
   }
   if (lane == 0) atomicMax(&s_cmax, cmax);
+  }  // exact select
 
   // ---- sort the k keys ascending.  Buckets: 4096 equal ranges of the
   // scores from the threshold's up to the largest kept one (of the codes,
@@ -263,7 +360,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     }
     return (o - t) >> sh;
   };
-  for (int32_t i = tid; i < k; i += THR_THREADS)
+  for (int32_t i = tid; i < n; i += THR_THREADS)
     atomicAdd(&hist[bucket(static_cast<uint32_t>(keys[i] >> 32))], 1u);
   __syncthreads();
   {
@@ -286,28 +383,31 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     atomicMax(&s_bmax, mx);
   }
   __syncthreads();
+  // the keys' ranks among all n; the top k (ranks n - k .. n - 1) are written
+  const int32_t skip = n - k;
   if (s_bmax <= static_cast<uint32_t>(THR_BUCKET)) {
-    for (int32_t i = tid; i < k; i += THR_THREADS) {
+    for (int32_t i = tid; i < n; i += THR_THREADS) {
       const uint64_t key = keys[i];
       keys2[atomicAdd(&cur[bucket(static_cast<uint32_t>(key >> 32))], 1u)] = key;
     }
     __syncthreads();
-    for (int32_t i = tid; i < k; i += THR_THREADS) {
+    for (int32_t i = tid; i < n; i += THR_THREADS) {
       const uint64_t key = keys2[i];
       const uint32_t d = bucket(static_cast<uint32_t>(key >> 32));
       const uint32_t lo = hist[d], hi = cur[d];  // the bucket, now filled
       uint32_t rank = 0;
       for (uint32_t x = lo; x < hi; ++x) rank += keys2[x] < key ? 1u : 0u;
-      dst[lo + rank] = key;
+      const int32_t at = static_cast<int32_t>(lo + rank) - skip;
+      if (at >= 0) dst[at] = key;
     }
     return;
   }
   int32_t p2 = 1;
-  while (p2 < k) p2 <<= 1;
-  for (int32_t i = k + tid; i < p2; i += THR_THREADS) keys[i] = ~0ull;  // sorts past the keys
+  while (p2 < n) p2 <<= 1;
+  for (int32_t i = n + tid; i < p2; i += THR_THREADS) keys[i] = ~0ull;  // sorts past the keys
   __syncthreads();
   bitonic_sort_lds(keys, p2);
-  for (int32_t i = tid; i < k; i += THR_THREADS) dst[i] = keys[i];
+  for (int32_t i = tid; i < k; i += THR_THREADS) dst[i] = keys[skip + i];
 }
 
 // #(x in a[0..n) with x < v), a sorted ascending

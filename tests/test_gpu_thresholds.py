@@ -66,6 +66,14 @@ CASES = [
     ("largest_k_32_segments", (1, 4, 4096, 64), 40000, "normal"),
     ("qwen3_8b_layer_4x", (8, 4, 3772, 256), 16384, "normal"),
     ("long_context_131k", (8, 4, 1788, 256), 131072, "normal"),
+    # segment starts over prefixes of 16k+ candidates with a small kept
+    # fraction keep the candidates at or above a sampled threshold; ties
+    # (a fifth of the scores share the top value) overflow that and take
+    # the exact select, monotone scores put the whole top k at one end
+    ("sampled_starts_ties", (2, 4, 700, 64), 60000, "ties"),
+    ("sampled_starts_increasing", (1, 4, 700, 16), 60000, "increasing"),
+    ("sampled_starts_decreasing", (1, 4, 700, 16), 60000, "decreasing"),
+    ("sampled_starts_qlog", (2, 0, 1500, 1), 90000, "qlog"),
 ]
 
 

@@ -581,7 +581,10 @@ def future_target_rate(w, reps: int):
     y = torch.empty((Hkv, T), dtype=torch.float32, device="cuda")
     cache = abi.KVpopCache(abi.make_config(1, 1, Hq, Hkv, D, w.n_sink, w.n_scored, W,
                                            max_positions=T))
-    cache.future_attention_target(q, k, work, y)
+    # untimed warm-up, about 50 ms of calls: the first ~35 ms run up to 10 %
+    # slower while the shader clock rises from idle
+    for _ in range(20):
+        cache.future_attention_target(q, k, work, y)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -965,7 +968,7 @@ def main():
         from fixed_budget_learned_amd.configs import (LONG_131K_8X, QWEN3_8B_36L_4X, TINY,
                                                       TP8_SHARE_4X)
         result["decode_cold_cache"] = decode_cold(w, 32)
-        result["future_attention_target"] = future_target_rate(w, 3)
+        result["future_attention_target"] = future_target_rate(w, 5)
         result["prefix_thresholds"] = [prefix_thresholds_rate(w, 5),
                                        prefix_thresholds_rate(LONG_131K_8X, 3)]
         result["configs"] = [layered_config(TINY, 512, 2),

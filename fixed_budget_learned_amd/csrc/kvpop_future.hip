@@ -9,9 +9,9 @@
 //
 // Two passes, FlashAttention-backward style, on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate), and a group sum:
-//   pass 1  per (query head, 128-query tile): S^T = K . Q^T over the causal
+//   pass 1  per (query head, 256-query tile): S^T = K . Q^T over the causal
 //           key tiles, online row log-sum-exp in the log2 domain -> lse[h][i].
-//   pass 2  per (query head, 128-key tile): for each 64-query tile with
+//   pass 2  per (query head, 256-key tile): for each 64-query tile with
 //           queries >= key + W, P = 2^(c S - lse), summed over the queries
 //           -> part[h][j].
 //   sum     y[g][j] = sum of part[h][j] over the group's heads, in head order.
@@ -20,12 +20,17 @@
 // the fixed-order group sum keeps the result deterministic.
 // Both passes launch the largest tiles (most work) first: the grid's x is the
 // head, its y the tile.
+// Each wave keeps 64 rows of the stationary operand in registers (queries in
+// pass 1, keys in pass 2) as two 32-row MFMA operands, and every 32-row
+// operand it reads from the LDS tile feeds two MFMAs.  With 32 rows per wave
+// the LDS reads bound both passes (one read per MFMA, 1 KB per 32 cycles of
+// matrix core per SIMD); 64 rows halve them for 148 and 160 registers, 3
+// waves per SIMD instead of 4 (measured on the 16,384-token layer shape:
+// 2.22-2.27 -> 2.07-2.12 ms per call).
 // Tiles reach LDS in two ways.  Pass 1 stages its key tiles through
 // registers into padded LDS rows.  Pass 2 loads its query tiles (and their
-// log-sum-exps) straight from global memory into LDS, XOR-swizzled: that
-// frees the 16 staging registers and lets 4 waves share a SIMD instead of 3
-// (measured on the 16,384-token layer shape: 1.58 -> 1.42 ms).  Pass 1 already
-// runs 4 waves per SIMD and was slower with the direct loads (1.25 -> 1.35 ms).
+// log-sum-exps) straight from global memory into LDS, XOR-swizzled, which
+// needs no staging registers.  Pass 1 was slower with the direct loads.
 // S^T puts keys on the MFMA rows and queries on its columns: a lane holds 16
 // keys of one query, so the row reductions of pass 1 are in-lane plus one
 // swap of wave halves, and pass 2 sums columns in-lane until one final
@@ -75,7 +80,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int FT_THREADS = 256;   // 4 waves
-constexpr int FT_ROWS = 128;      // queries (pass 1) or keys (pass 2) per workgroup
+constexpr int FT_WROWS = 64;      // queries (pass 1) or keys (pass 2) per wave, in registers
+constexpr int FT_ROWS = FT_WROWS * FT_THREADS / WAVE;  // ... per workgroup
 constexpr int FT_TILE = 64;       // keys (pass 1) or queries (pass 2) per LDS tile
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -158,6 +164,8 @@ __device__ __forceinline__ void settle(u32x4_t (&op)[N]) {
 }
 
 // ---- pass 1: log2-domain log-sum-exp of every query row --------------------
+// A wave holds 64 queries as two register operands, so every 32-key operand
+// it reads from LDS feeds two MFMAs (one per query block).
 template <int D>
 __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int32_t T, int32_t Hq,
@@ -173,84 +181,87 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const uint16_t* qh = q + static_cast<int64_t>(h) * T * D;
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
-  const int32_t iw = i0 + 32 * wid;          // this wave's first query
-  const int32_t my_q = iw + (lane & 31);     // this lane's query (column)
-  u32x4_t qreg[D / 16];
-  load_operand_rows<D>(qh, iw, T, qreg);
+  const int32_t iw = i0 + FT_WROWS * wid;    // this wave's first query
+  const int32_t my_q = iw + (lane & 31);     // this lane's queries: my_q and my_q + 32
+  u32x4_t qreg[2][D / 16];
+  load_operand_rows<D>(qh, iw, T, qreg[0]);
+  load_operand_rows<D>(qh, iw + 32, T, qreg[1]);
   __builtin_amdgcn_sched_barrier(0);
   const int32_t ilast = min(i0 + FT_ROWS, T) - 1;
   const int ntile = ilast / FT_TILE + 1;      // key tiles 0 .. ilast/64
   TileLoader<D> ld;
   ld.load(kg, 0, T);
   ld.store(ktile[0]);
-  settle(qreg);
+  settle(qreg[0]);
+  settle(qreg[1]);
   __syncthreads();
-  float m = -INFINITY, ssum = 0.f;
+  // Per query: m is an anchor, the running maximum of the scaled logits when
+  // it last moved.  A key block adds 2^(c2 x - m) over its keys; when that
+  // passes 2^64 (some logit above m + 64) or no anchor is set yet, m moves to
+  // the running maximum and the block is summed again.  The sum is the same
+  // up to rounding; most blocks skip the maximum.  The two lanes of a query
+  // (l and l ^ 32) hold the same m and part, so they branch together.
+  float m[2] = {-INFINITY, -INFINITY}, ssum[2] = {0.f, 0.f};
+  auto add_block = [&](const f32x16_t& x, float& mq, float& sq) {
+    float part = 0.f;
+    if (mq != -INFINITY) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -mq));
+      part += __shfl_xor(part, 32, WAVE);
+    }
+    if (mq != -INFINITY && part <= 0x1p64f) {
+      sq += part;
+    } else {
+      // the scale is positive: the largest scaled logit is the scaled maximum
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * c2;
+      const float mnew = fmaxf(mq, mx);
+      if (mnew != -INFINITY) {
+        part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -mnew));
+        part += __shfl_xor(part, 32, WAVE);
+        sq = sq * __builtin_amdgcn_exp2f(mq - mnew) + part;
+        mq = mnew;
+      }
+    }
+  };
   for (int t = 0; t < ntile; ++t) {
     if (t + 1 < ntile) ld.load(kg, (t + 1) * FT_TILE, T);
     // keep the next tile's LDS stores after this tile's math, so that its
     // loads stay in flight meanwhile
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* kt = ktile[t & 1];
-    if (iw <= ilast && t * FT_TILE <= iw + 31) {  // the wave has unmasked work
-      // both 32-key blocks of the tile as two independent MFMA chains
-      f32x16_t acc0 = {}, acc1 = {};
-      {
-        const uint16_t* a0 = kt + (lane & 31) * (D + 8) + 8 * (lane >> 5);
-        const uint16_t* a1 = a0 + 32 * (D + 8);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int32_t kf = t * FT_TILE + 32 * kb;  // the key block's first key
+      if (iw <= ilast && kf <= iw + FT_WROWS - 1) {  // some pair of the block is causal
+        // the key operand read once per k-step, for both query blocks
+        f32x16_t acc0 = {}, acc1 = {};
+        const uint16_t* a = kt + (32 * kb + (lane & 31)) * (D + 8) + 8 * (lane >> 5);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4_t av0 = *reinterpret_cast<const u32x4_t*>(a0 + 16 * ks);
-          const u32x4_t av1 = *reinterpret_cast<const u32x4_t*>(a1 + 16 * ks);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av0), as_bf16x8(qreg[ks]),
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(a + 16 * ks);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(qreg[0][ks]),
                                                          acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av1), as_bf16x8(qreg[ks]),
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(qreg[1][ks]),
                                                          acc1, 0, 0, 0);
         }
-      }
-      float x[32];
+        // keys of the block past the wave's first query need the causal mask
+        if (kf + 31 > iw || kf + 32 > T) {
+          const int32_t key0 = kf + 4 * (lane >> 5);
 #pragma unroll
-      for (int r = 0; r < 32; ++r) x[r] = r < 16 ? acc0[r] : acc1[r - 16];
-      // keys of the tile past this wave's first query need the causal mask
-      if (t * FT_TILE + FT_TILE - 1 > iw || t * FT_TILE + FT_TILE > T) {
-        const int32_t key0 = t * FT_TILE + 4 * (lane >> 5);
-#pragma unroll
-        for (int r = 0; r < 32; ++r) {
-          const int32_t key = key0 + 32 * (r >> 4) + 8 * ((r & 15) >> 2) + (r & 3);
-          x[r] = (key <= my_q && key < T) ? x[r] : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
+            acc0[r] = (key <= my_q && key < T) ? acc0[r] : -INFINITY;
+            acc1[r] = (key <= my_q + 32 && key < T) ? acc1[r] : -INFINITY;
+          }
         }
-      }
-      // m is an anchor: the running maximum of the scaled logits when it last
-      // moved.  A tile adds 2^(c2 x - m) over its keys; when that passes
-      // 2^64 (some logit above m + 64) or no anchor is set yet, m moves to
-      // the running maximum and the tile is summed again.  The sum is the
-      // same up to rounding; most tiles skip the maximum.  The two lanes of
-      // a query (l and l ^ 32) hold the same m and part, so they branch
-      // together.
-      float part = 0.f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int r = 0; r < 32; ++r) part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -m));
-        part += __shfl_xor(part, 32, WAVE);
-      }
-      if (m != -INFINITY && part <= 0x1p64f) {
-        ssum += part;
-      } else {
-        // the scale is positive: the largest scaled logit is the scaled maximum
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) mx = fmaxf(mx, x[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * c2;
-        const float mnew = fmaxf(m, mx);
-        if (mnew != -INFINITY) {
-          part = 0.f;
-#pragma unroll
-          for (int r = 0; r < 32; ++r)
-            part += __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c2, -mnew));
-          part += __shfl_xor(part, 32, WAVE);
-          ssum = ssum * __builtin_amdgcn_exp2f(m - mnew) + part;
-          m = mnew;
-        }
+        add_block(acc0, m[0], ssum[0]);
+        add_block(acc1, m[1], ssum[1]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -259,10 +270,16 @@ __global__ __launch_bounds__(FT_THREADS) void future_lse_kernel(
     }
     __syncthreads();
   }
-  if (lane < 32 && my_q < T) lse[static_cast<int64_t>(h) * T + my_q] = m + __log2f(ssum);
+  if (lane < 32) {
+    float* lh = lse + static_cast<int64_t>(h) * T;
+    if (my_q < T) lh[my_q] = m[0] + __log2f(ssum[0]);
+    if (my_q + 32 < T) lh[my_q + 32] = m[1] + __log2f(ssum[1]);
+  }
 }
 
 // ---- pass 2: column sums of the probabilities of queries past the window --
+// A wave holds 64 keys as two register operands, so every 32-query operand
+// it reads from LDS feeds two MFMAs (one per key block).
 template <int D>
 __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
@@ -275,14 +292,15 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const uint16_t* kg = k + static_cast<int64_t>(g) * T * D;
-  const int32_t jw = j0 + 32 * wid;          // this wave's first key
-  u32x4_t kreg[D / 16];
-  load_operand_rows<D>(kg, jw, T, kreg);
+  const int32_t jw = j0 + FT_WROWS * wid;    // this wave's first key
+  u32x4_t kreg[2][D / 16];
+  load_operand_rows<D>(kg, jw, T, kreg[0]);
+  load_operand_rows<D>(kg, jw + 32, T, kreg[1]);
   __builtin_amdgcn_sched_barrier(0);
-  // this lane's 16 keys: jw + 8*(r/4) + 4*(lane/32) + r%4
-  float col[16];
+  // this lane's 32 keys: jw + 32*b + 8*(r/4) + 4*(lane/32) + r%4
+  float col[2][16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) col[r] = 0.f;
+  for (int r = 0; r < 16; ++r) col[0][r] = col[1][r] = 0.f;
   const int32_t qfirst = j0 + W;              // first query any key of the tile counts
   const int t0 = qfirst / FT_TILE;
   const int nsteps = (qfirst < T) ? (T - 1) / FT_TILE + 1 - t0 : 0;  // query tiles
@@ -298,55 +316,55 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
           (__attribute__((address_space(3))) void*)(ltile[b]), 4, 0, 0);
   };
   if (nsteps > 0) fetch(0, 0);
-  settle(kreg);
+  settle(kreg[0]);
+  settle(kreg[1]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     if (step + 1 < nsteps) fetch(step + 1, buf ^ 1);
-    const int32_t qrow0 = (t0 + step) * FT_TILE;
-    if (jw < T && qrow0 + FT_TILE - 1 >= jw + W) {  // some query of the tile counts
-      // both 32-query blocks of the tile as two independent MFMA chains
-      f32x16_t acc0 = {}, acc1 = {};
-      {
-        const char* qb8 = reinterpret_cast<const char*>(qtile[buf]);
+    const char* qb8 = reinterpret_cast<const char*>(qtile[buf]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int32_t qs = (t0 + step) * FT_TILE + 32 * qb;  // the query block's first query
+      if (jw < T && qs + 31 >= jw + W) {  // some query of the block counts (uniform)
+        // the query operand read once per k-step, for both key blocks
+        f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const int cch = 2 * ks + (lane >> 5);
-          const u32x4_t bv0 = *reinterpret_cast<const u32x4_t*>(qb8 + TileDma<D>::at(lane & 31, cch));
-          const u32x4_t bv1 = *reinterpret_cast<const u32x4_t*>(qb8 + TileDma<D>::at(32 + (lane & 31), cch));
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(bv0),
+          const u32x4_t bv =
+              *reinterpret_cast<const u32x4_t*>(qb8 + TileDma<D>::at(32 * qb + (lane & 31), cch));
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[0][ks]), as_bf16x8(bv),
                                                          acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(bv1),
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[1][ks]), as_bf16x8(bv),
                                                          acc1, 0, 0, 0);
         }
-      }
-      // every (query, key) pair of the tile counts when its first query is
-      // at least W past this wave's last key and the tile ends before T
-      const bool full = qrow0 >= jw + 31 + W && qrow0 + FT_TILE <= T && jw + 32 <= T;
-      if (!full) {  // uniform: pairs that do not count get a logit of -inf (weight 0)
-        const int32_t key0 = jw + 4 * (lane >> 5);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int32_t qi = qrow0 + 32 * qb + (lane & 31);  // this lane's query
+        // every (query, key) pair of the block counts when its first query is
+        // at least W past the wave's last key and both lie before T
+        const bool full = qs >= jw + FT_WROWS - 1 + W && qs + 32 <= T && jw + FT_WROWS <= T;
+        if (!full) {  // uniform: pairs that do not count get a logit of -inf (weight 0)
+          // the lane's query qi and keys key0 + o (o = 8*(r/4) + r%4, and
+          // o + 32 for the second block): a pair counts when qi < T,
+          // o < T - key0 and o <= qi - key0 - W
+          const int32_t qi = qs + (lane & 31);
+          const int32_t key0 = jw + 4 * (lane >> 5);
+          const int32_t d = qi < T ? qi - key0 - W : -1;
+          const int32_t e = min(T - key0 - 1, d);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int32_t key = key0 + 8 * (r >> 2) + (r & 3);
-            if (!(qi < T && key < T && qi >= key + W)) {
-              if (qb == 0)
-                acc0[r] = -INFINITY;
-              else
-                acc1[r] = -INFINITY;
-            }
+            const int o = 8 * (r >> 2) + (r & 3);
+            if (o > e) acc0[r] = -INFINITY;
+            if (o + 32 > e) acc1[r] = -INFINITY;
           }
         }
-      }
-      // a multiply-add, an exp2 and an add per pair
-      const float l2a = ltile[buf][lane & 31], l2b = ltile[buf][32 + (lane & 31)];
+        // a multiply-add, an exp2 and an add per pair
+        const float l2 = ltile[buf][32 * qb + (lane & 31)];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        col[r] += __builtin_amdgcn_exp2f(acc0[r] * c2 - l2a);
-        col[r] += __builtin_amdgcn_exp2f(acc1[r] * c2 - l2b);
+        for (int r = 0; r < 16; ++r) {
+          col[0][r] += __builtin_amdgcn_exp2f(acc0[r] * c2 - l2);
+          col[1][r] += __builtin_amdgcn_exp2f(acc1[r] * c2 - l2);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
@@ -354,20 +372,26 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
   }
   // every key's sum is spread over the 32 query lanes of its wave half
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float v = col[r];
-    v += __shfl_xor(v, 1, WAVE);
-    v += __shfl_xor(v, 2, WAVE);
-    v += __shfl_xor(v, 4, WAVE);
-    v += __shfl_xor(v, 8, WAVE);
-    v += __shfl_xor(v, 16, WAVE);
-    col[r] = v;
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = col[b][r];
+      v += __shfl_xor(v, 1, WAVE);
+      v += __shfl_xor(v, 2, WAVE);
+      v += __shfl_xor(v, 4, WAVE);
+      v += __shfl_xor(v, 8, WAVE);
+      v += __shfl_xor(v, 16, WAVE);
+      col[b][r] = v;
+    }
   }
   if ((lane & 31) == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int32_t key = jw + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
-      if (key < T) part[static_cast<int64_t>(h) * T + key] = col[r];
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t key = jw + 32 * b + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
+        if (key < T) part[static_cast<int64_t>(h) * T + key] = col[b][r];
+      }
     }
   }
 }

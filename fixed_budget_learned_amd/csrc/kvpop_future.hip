@@ -95,11 +95,20 @@ struct TileLoader {
   static constexpr int PER_THREAD = FT_TILE * PIECES / FT_THREADS;
   u32x4_t buf[PER_THREAD];
   __device__ __forceinline__ void load(const uint16_t* src, int32_t row0, int32_t nrows) {
+    if (row0 + FT_TILE <= nrows) {  // uniform: one base, per-lane offsets that stay fixed
+      const uint16_t* base = src + static_cast<int64_t>(row0) * D;
 #pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      const int p = threadIdx.x + u * FT_THREADS;
-      const int32_t r = min(row0 + p / PIECES, nrows - 1);
-      buf[u] = reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(r) * D)[p % PIECES];
+      for (int u = 0; u < PER_THREAD; ++u) {
+        const int p = threadIdx.x + u * FT_THREADS;
+        buf[u] = *reinterpret_cast<const u32x4_t*>(base + (p / PIECES) * D + (p % PIECES) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER_THREAD; ++u) {
+        const int p = threadIdx.x + u * FT_THREADS;
+        const int32_t r = min(row0 + p / PIECES, nrows - 1);
+        buf[u] = reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(r) * D)[p % PIECES];
+      }
     }
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
@@ -117,24 +126,38 @@ struct TileLoader {
 // together by a 16-byte LDS read (8 rows, one chunk) hit distinct banks.  A
 // wave instruction fills 1 KB: lane i writes position i of it, so it loads
 // the global chunk that belongs there.  Rows past `nrows` read the last row.
+// `wid` is the wave index, uniform.
 template <int D>
 struct TileDma {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int RPI = 1024 / (D * 2);        // rows per wave instruction
   static constexpr int INST = FT_TILE / RPI / (FT_THREADS / WAVE);  // per wave
   __device__ __forceinline__ static void issue(const uint16_t* src, int32_t row0, int32_t nrows,
-                                               uint16_t* lds) {
+                                               uint16_t* lds, int wid) {
     const int lane = threadIdx.x & (WAVE - 1);
-    const int wid = threadIdx.x / WAVE;
+    if (row0 + FT_TILE <= nrows) {  // uniform: one base, per-lane offsets that stay fixed
+      const uint16_t* base = src + static_cast<int64_t>(row0) * D;
 #pragma unroll
-    for (int u = 0; u < INST; ++u) {
-      const int blk = u * (FT_THREADS / WAVE) + wid;  // 1 KB block of the tile
-      const int r = blk * RPI + lane / CPR;           // tile row of this lane
-      const int c = (lane % CPR) ^ (r % CPR);         // global chunk it must fetch
-      const int32_t gr = min(row0 + r, nrows - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src + static_cast<int64_t>(gr) * D + c * 8),
-          (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+      for (int u = 0; u < INST; ++u) {
+        const int blk = u * (FT_THREADS / WAVE) + wid;  // 1 KB block of the tile
+        const int r = blk * RPI + lane / CPR;           // tile row of this lane
+        const int c = (lane % CPR) ^ (r % CPR);         // global chunk it must fetch
+        const uint32_t off = static_cast<uint32_t>((r * D + c * 8) * 2);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(base) + off),
+            (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < INST; ++u) {
+        const int blk = u * (FT_THREADS / WAVE) + wid;
+        const int r = blk * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ (r % CPR);
+        const int32_t gr = min(row0 + r, nrows - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(src + static_cast<int64_t>(gr) * D + c * 8),
+            (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+      }
     }
   }
   // byte offset of (row, chunk) in the tile
@@ -309,10 +332,12 @@ __global__ __launch_bounds__(FT_THREADS) void future_colsum_kernel(
   // the query tile and its 64 log-sum-exps, straight into LDS
   auto fetch = [&](int step, int b) {
     const int32_t qrow0 = (t0 + step) * FT_TILE;
-    TileDma<D>::issue(qh, qrow0, T, qtile[b]);
+    TileDma<D>::issue(qh, qrow0, T, qtile[b], wid);
     if (wid == 0)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(lh + min(qrow0 + lane, T - 1)),
+          (const __attribute__((address_space(1))) void*)(qrow0 + FT_TILE <= T
+                                                              ? lh + qrow0 + lane
+                                                              : lh + min(qrow0 + lane, T - 1)),
           (__attribute__((address_space(3))) void*)(ltile[b]), 4, 0, 0);
   };
   if (nsteps > 0) fetch(0, 0);

@@ -59,10 +59,15 @@ bool config_valid(const kvpop_config* c) {
 // workgroups of 256 threads, each thread holding 2 rows per pass.  With 256
 // or more heads (batched serving) each head is one workgroup: the step needs
 // no cross-workgroup merge at all.  With fewer heads the splits fill the
-// 256 compute units once (one workgroup per unit).  Every split keeps at
-// least 128 slots: at batch 1, twice the splits of half the slots (two
-// workgroups per unit) measured slower, since the workgroups start later and
-// the merge has twice the partials.
+// 256 compute units at most once (one workgroup per unit), with at most 32
+// splits per head and at least 64 slots per split.  Measured at batch 1:
+//   * 4,032 slots, 8 KV heads: 32 splits of 128 slots 8.3 us; 64 splits of
+//     64 slots (two workgroups per unit) 10.3 us;
+//   * 2,048 slots, 8 KV heads: 32 splits of 64 slots (one pass of the
+//     workgroup) 7.5 us; 16 or 20 splits of 128 slots 8.3 us;
+//   * 4,032 slots, one KV head: 32 splits 8.2 us, 48 splits 9.3 us, 64
+//     splits 8.7 us: beyond 32 the finishing workgroup's merge of the
+//     partials costs more than the shorter splits save.
 //
 // Split heads are merged by the last split's workgroup, in the same launch,
 // unless the configuration asks for the second launch: with each head's
@@ -84,8 +89,8 @@ int64_t decode_splits_for(const kvpop_config& c, int64_t heads, bool layers) {
   const int64_t budget = capacity_of(c);
   int64_t ns = c.decode_splits;
   if (ns == 0) {
-    ns = layers ? (1440 + heads - 1) / heads : 256 / heads;
-    ns = std::min<int64_t>(ns, (budget + 127) / 128);
+    ns = layers ? (1440 + heads - 1) / heads : std::min<int64_t>(256 / heads, 32);
+    ns = std::min<int64_t>(ns, (budget + 63) / 64);
     ns = std::min<int64_t>(ns, kvpop::decode_max_splits());
     ns = std::max<int64_t>(ns, 1);
   }

@@ -747,18 +747,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
   };
 
-  // Chunks.  A split of at most two chunks (batch 1) requests both at once
-  // and computes them in order, so no load is left in flight after the
-  // last one.  Longer splits ping-pong: the next chunk's loads are issued
+  // Chunks.  A split of one chunk loads nothing more; a split of two
+  // (batch 1) requests both at once and computes them in order, so no load
+  // is left in flight after the last one.  Longer splits ping-pong: the next chunk's loads are issued
   // before the current one is computed (and after the last, whose loads
   // read slot 0), so the load count never depends on the path taken and
   // the compiler's wait for the current chunk counts exactly the loads
   // issued after it.
   const int32_t nch = hi > lo ? (hi - lo + CHUNK - 1) / CHUNK : 0;
-  if (nch <= 2) {
+  if (nch == 2) {
     load_chunk(kB, vB, keyB, lo + CHUNK);
+    compute_chunk(kA, vA, keyA, lo);
+    compute_chunk(kB, vB, keyB, lo + CHUNK);
+  } else if (nch < 2) {  // one chunk (or none): nothing more to load
     if (nch > 0) compute_chunk(kA, vA, keyA, lo);
-    if (nch > 1) compute_chunk(kB, vB, keyB, lo + CHUNK);
   } else {
     for (int32_t base = lo; base < hi;) {
       load_chunk(kB, vB, keyB, base + CHUNK);

@@ -69,6 +69,14 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise KVpopLibraryMissing(
             f"{LIB_PATH} is missing; build it with `python -m fixed_budget_learned_amd.build`")
+    # torch ships its own HIP runtime.  Loaded first, it is the one the
+    # library binds to; loaded after the library, a second runtime comes up
+    # whose device memory and streams the library cannot use (cache creation
+    # then fails with a HIP error).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.kvpop_cache_required_bytes.argtypes = [ctypes.POINTER(Config)]

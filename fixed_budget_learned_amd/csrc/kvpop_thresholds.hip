@@ -12,8 +12,12 @@
 // candidates before it (for the first segment: the first k): a radix select
 // over the prefix (12-, 12- and 8-bit digits of the score code, ties at the
 // threshold code resolved by position, the newest kept), a gather of the k
-// keys and a sort in LDS.  The second launch runs one workgroup per
-// (segment, head) from that set.
+// keys and a sort in LDS.  Long prefixes with a small kept fraction are
+// sampled first (two more launches ahead of it): a threshold from 4,096
+// sampled codes, then many workgroups keep the candidates that reach it;
+// when at least k and at most THR_KMAX do, they hold the top k and the sort
+// takes them instead of the select.  The last launch runs one workgroup per
+// (segment, head) from the starts.
 //
 // Within a segment a 1024-thread workgroup sweeps the candidates in chunks,
 // keeping the current top-k keys sorted ascending in LDS (R, k <= THR_KMAX;
@@ -54,12 +58,29 @@ constexpr int THR_VMAX = 4;        // candidates per thread
 constexpr int THR_ETARGET = 192;   // expected entrants per chunk
 constexpr int THR_BUCKET = 64;     // segment starts: largest bucket ranked by counting
 constexpr int THR_SAMPLE = 4096;   // segment starts: codes read for a sampled threshold
-constexpr int THR_SAMPLE_MIN = 16384;  // ... from prefixes of at least this many candidates
+static_assert(THR_SAMPLE <= THR_KMAX, "a prefix read whole fits the key list");
+constexpr int THR_FCHUNK = 8 * THR_THREADS;   // sampled starts: candidates per filter workgroup
 
-// Segment plan of a prompt: candidate ranges [b[j], b[j+1]) for j < S.
+// Segment plan of a prompt: candidate ranges [b[j], b[j+1]) for j < S, and
+// for each segment start the rank m of its sampled threshold (0: the start
+// takes the exact select).
 struct ThrPlan {
   int32_t S;
   int32_t b[THR_SEG_MAX + 1];
+  uint32_t m[THR_SEG_MAX];
+};
+
+// The filter launch's work: (start, chunk) pairs of the sampled starts.
+constexpr int THR_FPAIRS = 512;
+struct ThrFilterWork {
+  int32_t n;
+  uint16_t j[THR_FPAIRS], c[THR_FPAIRS];
+};
+
+// A sampled segment start: its threshold, the keys that reach it (counted
+// by the filter workgroups, stored up to THR_KMAX) and their largest code.
+struct ThrMeta {
+  uint32_t tau, count, cmax, pad;
 };
 
 // Ascending bitonic sort of a[0, p2) in LDS (p2 a power of two, at most
@@ -121,12 +142,164 @@ __device__ __forceinline__ void stream_scores(const float* __restrict__ sc, int3
   }
 }
 
+// Sampled segment starts, first launch: the threshold of each (start j,
+// head g) with plan.m[j] != 0 is the lower edge of the 24-bit bin that holds
+// the m-th largest of THR_SAMPLE codes read in 64 runs spread over the
+// prefix [0, b[j]) (all of it when b <= THR_SAMPLE).  With m = n + 4 sqrt(n)
+// + 8, n = THR_SAMPLE * k / b (about n of the sample are in the top k),
+// about m * b / THR_SAMPLE candidates reach it; a prefix read whole takes
+// m = k.  The launch also clears the start's count and largest code for
+// the filter launch.  Grid (S, Hkv).
+__global__ __launch_bounds__(THR_THREADS) void thresholds_tau_kernel(
+    const float* __restrict__ scores, int32_t P, int32_t s, ThrPlan plan,
+    ThrMeta* __restrict__ meta) {
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t scan_buf[THR_THREADS / WAVE + 1];
+  __shared__ uint32_t s_bin, s_above;
+  const int j = blockIdx.x;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint32_t m = plan.m[j];
+  ThrMeta* mt = meta + static_cast<int64_t>(g) * plan.S + j;
+  if (m == 0) return;
+  const int32_t b = plan.b[j];
+  const float* __restrict__ sc = scores + static_cast<int64_t>(g) * P + s;
+  // a prefix of at most THR_SAMPLE candidates is read whole (the host then
+  // asks for m = k: the bin of the k-th largest code); a longer one in runs
+  // that do not overlap
+  const bool whole = b <= THR_SAMPLE;
+  constexpr int TPR = THR_SAMPLE / 64 / 4;  // threads per run (4 codes each)
+  const int32_t i0 = whole ? tid * 4
+                           : static_cast<int32_t>(static_cast<int64_t>(tid / TPR) * b / 64) +
+                                 (tid % TPR) * 4;
+  uint32_t code[4];
+  bool valid[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    valid[e] = i0 + e < b;
+    code[e] = valid[e] ? score_code(sc[i0 + e]) : 0u;
+  }
+  uint32_t mrem = m, pre = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 20 : 8;
+    for (int i = tid; i < 4096; i += THR_THREADS) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (valid[e] && (pass == 0 || (code[e] >> 20) == (pre >> 20)))
+        atomicAdd(&hist[(code[e] >> shift) & 4095u], 1u);
+    __syncthreads();
+    uint32_t h[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[q] = hist[4095 - 4 * tid - q];
+      sum += h[q];
+    }
+    uint32_t tot;
+    uint32_t ex = block_exclusive_scan_u32<THR_THREADS>(sum, scan_buf, &tot);
+    if (ex < mrem && mrem <= ex + sum) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (mrem <= ex + h[q]) {
+          s_bin = static_cast<uint32_t>(4095 - 4 * tid - q);
+          s_above = ex;
+          break;
+        }
+        ex += h[q];
+      }
+    }
+    __syncthreads();
+    mrem -= s_above;
+    pre |= s_bin << shift;
+  }
+  if (tid == 0) *mt = ThrMeta{pre, 0u, 0u, 0u};  // low 8 bits 0: codes in or above the bin
+}
+
+// Sampled segment starts, second launch: every workgroup streams
+// THR_FCHUNK candidates of one start's prefix, gathers the keys whose code
+// reaches the start's threshold in LDS, then reserves room in the start's
+// list with one atomic and copies them there (stores past THR_KMAX are
+// dropped: the count still tells), and raises the start's largest code.
+// Spreading each prefix over many workgroups matters: one workgroup
+// streamed a 114k-candidate prefix in 26-30 us, bound by the loads one
+// compute unit keeps in flight.  One global atomic per wavefront instead of
+// per workgroup serialised on the start's counter (2x slower overall), and
+// so do chunks much smaller than 8,192 candidates (131,072 tokens: 70, 74
+// and 93 us per call at 8,192, 4,096 and 2,048; 72 and 79 us at 16,384 and
+// 32,768).
+// Grid (pairs, Hkv): one workgroup per (start, chunk) pair and head.
+__global__ __launch_bounds__(THR_THREADS) void thresholds_filter_kernel(
+    const float* __restrict__ scores, int32_t P, int32_t s, ThrPlan plan, ThrFilterWork fw,
+    ThrMeta* __restrict__ meta, uint64_t* __restrict__ lists) {
+  __shared__ uint64_t lk[THR_KMAX];
+  __shared__ uint32_t s_cnt, s_cmax, s_base;
+  const int j = fw.j[blockIdx.x];
+  const int c = fw.c[blockIdx.x];
+  const int g = blockIdx.y;
+  const int32_t b = plan.b[j];
+  const int32_t lo = c * THR_FCHUNK;
+  const int32_t hi = min(b, lo + THR_FCHUNK);
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  ThrMeta* mt = meta + static_cast<int64_t>(g) * plan.S + j;
+  uint64_t* list = lists + (static_cast<int64_t>(g) * plan.S + j) * THR_KMAX;
+  const uint32_t tau = mt->tau;
+  const float* __restrict__ sc = scores + static_cast<int64_t>(g) * P + s;
+  constexpr int U = THR_FCHUNK / THR_THREADS;
+  float x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) x[u] = sc[min(lo + u * THR_THREADS + tid, hi - 1)];
+  if (tid == 0) {
+    s_cnt = 0u;
+    s_cmax = 0u;
+  }
+  __syncthreads();
+  uint32_t cmax = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t i = lo + u * THR_THREADS + tid;
+    const uint32_t o = score_code(x[u]);
+    const bool keep = i < hi && o >= tau;
+    const uint64_t msk = __ballot(keep);
+    if (msk != 0ull) {  // wavefront-uniform
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s_cnt, static_cast<uint32_t>(__popcll(msk)));
+      base = __shfl(base, 0, WAVE);
+      if (keep) {
+        const uint32_t at = base + __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(msk >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(msk), 0u));
+        if (at < static_cast<uint32_t>(THR_KMAX)) lk[at] = make_key(o, s + i);
+        cmax = o > cmax ? o : cmax;
+      }
+    }
+  }
+#pragma unroll
+  for (int d = WAVE / 2; d >= 1; d >>= 1) {
+    const uint32_t y = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cmax), d, WAVE));
+    cmax = y > cmax ? y : cmax;
+  }
+  if (lane == 0 && cmax != 0u) atomicMax(&s_cmax, cmax);
+  __syncthreads();
+  const uint32_t n = s_cnt;
+  if (n == 0u) return;  // uniform
+  if (tid == 0) {
+    s_base = atomicAdd(&mt->count, n);
+    atomicMax(&mt->cmax, s_cmax);
+  }
+  __syncthreads();
+  const uint32_t base = s_base;
+  const uint32_t nl = min(n, static_cast<uint32_t>(THR_KMAX));
+  for (uint32_t i = tid; i < nl; i += THR_THREADS)
+    if (base + i < static_cast<uint32_t>(THR_KMAX)) list[base + i] = lk[i];
+}
+
 // The exact top-k keys (ascending) of the first b[j] candidates of head g
 // (b[0] = k: the first k), the start of segment j, into
 // ws[(g * S + j) * k ...].  Grid (S, Hkv).
 __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     const float* __restrict__ scores, int32_t P, int32_t s, int32_t k, ThrPlan plan,
-    uint64_t* __restrict__ ws) {
+    uint64_t* __restrict__ ws, const ThrMeta* __restrict__ meta,
+    const uint64_t* __restrict__ lists) {
   constexpr int NWAVE = THR_THREADS / WAVE;
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t cur[4096];
@@ -148,96 +321,22 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     s_bmax = 0u;
   }
 
-  // ---- long prefixes with a small kept fraction: a sampled threshold.  It
-  // is the lower edge of the 24-bit bin that holds the m-th largest of
-  // THR_SAMPLE codes read in 64 runs spread over the prefix, m = n + 4 sqrt(n)
-  // + 8 with n = THR_SAMPLE * k / b (about n of the sample are in the top
-  // k), so about m * b / THR_SAMPLE candidates reach it.  One pass keeps
-  // those (as keys) in LDS; when there are at least k of them and they fit,
-  // they hold the top k (every other key is below all of them), which the
-  // sort below places.  Otherwise the exact select runs as for any prefix.
+  // ---- a sampled start: when at least k keys reach its threshold and they
+  // fit, they hold the top k (every other key is below all of them), which
+  // the sort below places.  Otherwise the exact select runs.
   uint32_t t = 0;     // every key of the sort is at or above code t
   int32_t n = k;      // keys to sort; the top k of them are written
   bool sampled = false;
-  const float nf = static_cast<float>(THR_SAMPLE) * static_cast<float>(k) / static_cast<float>(b);
-  const uint32_t m = min(static_cast<uint32_t>(ceilf(nf + 4.f * sqrtf(nf) + 8.f)),
-                         static_cast<uint32_t>(THR_SAMPLE));
-  // tried only where the expected survivors (m * b / THR_SAMPLE) fit the LDS
-  // key array with room to spare
-  if (b >= THR_SAMPLE_MIN &&
-      static_cast<int64_t>(m) * b <= static_cast<int64_t>(THR_KMAX) * THR_SAMPLE * 7 / 8) {
-    constexpr int TPR = THR_SAMPLE / 64 / 4;  // threads per run (4 codes each)
-    const int32_t i0 = static_cast<int32_t>(static_cast<int64_t>(tid / TPR) * b / 64) + (tid % TPR) * 4;
-    uint32_t code[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) code[e] = score_code(sc[i0 + e]);
-    uint32_t mrem = m, pre = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 20 : 8;
-      for (int i = tid; i < 4096; i += THR_THREADS) hist[i] = 0u;
+  if (meta != nullptr && plan.m[j] != 0) {
+    const ThrMeta mt = meta[g * plan.S + j];
+    if (mt.count >= static_cast<uint32_t>(k) && mt.count <= static_cast<uint32_t>(THR_KMAX)) {
+      const uint64_t* list = lists + (static_cast<int64_t>(g) * plan.S + j) * THR_KMAX;
+      for (int32_t i = tid; i < static_cast<int32_t>(mt.count); i += THR_THREADS) keys[i] = list[i];
+      if (tid == 0) s_cmax = mt.cmax;
       __syncthreads();
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (pass == 0 || (code[e] >> 20) == (pre >> 20)) atomicAdd(&hist[(code[e] >> shift) & 4095u], 1u);
-      __syncthreads();
-      uint32_t h[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        h[q] = hist[4095 - 4 * tid - q];
-        sum += h[q];
-      }
-      uint32_t tot;
-      uint32_t ex = block_exclusive_scan_u32<THR_THREADS>(sum, scan_buf, &tot);
-      if (ex < mrem && mrem <= ex + sum) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (mrem <= ex + h[q]) {
-            s_bin = static_cast<uint32_t>(4095 - 4 * tid - q);
-            s_above = ex;
-            break;
-          }
-          ex += h[q];
-        }
-      }
-      __syncthreads();
-      mrem -= s_above;
-      pre |= s_bin << shift;
-    }
-    const uint32_t tau = pre;  // low 8 bits 0: codes in or above the bin
-    uint32_t cmax = 0;
-    stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
-      const bool keep = i < b && o >= tau;
-      const uint64_t msk = __ballot(keep);
-      if (msk != 0ull) {  // wavefront-uniform
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&s_n, static_cast<uint32_t>(__popcll(msk)));
-        base = __shfl(base, 0, WAVE);
-        if (keep) {
-          const uint32_t at = base + __builtin_amdgcn_mbcnt_hi(
-              static_cast<uint32_t>(msk >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(msk), 0u));
-          if (at < static_cast<uint32_t>(THR_KMAX)) keys[at] = make_key(o, s + i);
-          cmax = o > cmax ? o : cmax;
-        }
-      }
-    });
-#pragma unroll
-    for (int d = WAVE / 2; d >= 1; d >>= 1) {
-      const uint32_t y = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cmax), d, WAVE));
-      cmax = y > cmax ? y : cmax;
-    }
-    if (lane == 0) atomicMax(&s_cmax, cmax);
-    __syncthreads();
-    const uint32_t got = s_n;
-    if (got >= static_cast<uint32_t>(k) && got <= static_cast<uint32_t>(THR_KMAX)) {
       sampled = true;
-      t = tau;
-      n = static_cast<int32_t>(got);
-    } else {
-      __syncthreads();  // every thread has read s_n
-      if (tid == 0) {
-        s_n = 0u;
-        s_cmax = 0u;
-      }
+      t = mt.tau;
+      n = static_cast<int32_t>(mt.count);
     }
   }
 
@@ -682,10 +781,63 @@ hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const
   }
   plan.b[plan.S] = C;
   for (int j = plan.S + 1; j <= THR_SEG_MAX; ++j) plan.b[j] = C;
+  for (int j = 0; j < THR_SEG_MAX; ++j) plan.m[j] = 0u;
   if (plan.S > 1) {
-    hipLaunchKernelGGL(thresholds_segment_start_kernel,
-                       dim3(static_cast<uint32_t>(plan.S), static_cast<uint32_t>(geo.n_kv_heads)),
-                       dim3(THR_THREADS), 0, stream, scores, n_tokens, geo.n_sink, k, plan, ws);
+    // Sampled starts: prefixes whose expected survivors (m * b / THR_SAMPLE,
+    // or at most b for a prefix read whole) fit THR_KMAX with room to spare,
+    // when the workspace also holds the starts' lists and records (after the
+    // S * Hkv * k start keys) and the filter's pair table has room.  Only
+    // when every start qualifies: otherwise the starts that take the exact
+    // select set the launch's length and the two extra launches only add to
+    // it (16,384-token prompt at k = 3,772: 63 against 53 us per call).
+    const int64_t SH = static_cast<int64_t>(plan.S) * geo.n_kv_heads;
+    uint64_t* lists = ws + SH * k;
+    ThrMeta* meta = reinterpret_cast<ThrMeta*>(lists + SH * THR_KMAX);
+    const bool room = ws_keys >= SH * (k + THR_KMAX + 2);
+    ThrFilterWork fw;
+    fw.n = 0;
+    for (int j = 0; j < plan.S && room; ++j) {
+      const int32_t b = plan.b[j];
+      // a whole prefix (b <= THR_SAMPLE) is its own sample: m = k, and at most
+      // b <= THR_KMAX keys can reach the threshold
+      const double nf = static_cast<double>(THR_SAMPLE) * k / b;
+      const int64_t m = b <= THR_SAMPLE
+                            ? k
+                            : std::min<int64_t>(
+                                  static_cast<int64_t>(std::ceil(nf + 4.0 * std::sqrt(nf) + 8.0)),
+                                  THR_SAMPLE);
+      const int32_t chunks = (b + THR_FCHUNK - 1) / THR_FCHUNK;
+      const bool fits = b <= THR_SAMPLE ||
+                        m * b <= static_cast<int64_t>(THR_KMAX) * THR_SAMPLE * 7 / 8;
+      if (!fits || fw.n + chunks > THR_FPAIRS) {
+        fw.n = 0;
+        break;
+      }
+      plan.m[j] = static_cast<uint32_t>(m);
+      for (int32_t q = 0; q < chunks; ++q) {
+        fw.j[fw.n] = static_cast<uint16_t>(j);
+        fw.c[fw.n] = static_cast<uint16_t>(q);
+        ++fw.n;
+      }
+    }
+    if (fw.n == 0)
+      for (int j = 0; j < THR_SEG_MAX; ++j) plan.m[j] = 0u;
+    const dim3 starts(static_cast<uint32_t>(plan.S), static_cast<uint32_t>(geo.n_kv_heads));
+    if (fw.n > 0) {
+      hipLaunchKernelGGL(thresholds_tau_kernel, starts, dim3(THR_THREADS), 0, stream, scores,
+                         n_tokens, geo.n_sink, plan, meta);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(thresholds_filter_kernel,
+                         dim3(static_cast<uint32_t>(fw.n), static_cast<uint32_t>(geo.n_kv_heads)),
+                         dim3(THR_THREADS), 0, stream, scores, n_tokens, geo.n_sink, plan, fw, meta,
+                         lists);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(thresholds_segment_start_kernel, starts, dim3(THR_THREADS), 0, stream,
+                       scores, n_tokens, geo.n_sink, k, plan, ws,
+                       fw.n > 0 ? meta : static_cast<ThrMeta*>(nullptr), lists);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -55,7 +55,7 @@ namespace {
 constexpr int THR_THREADS = 1024;
 constexpr int THR_ARR = 1024;      // entrants one chunk can hold
 constexpr int THR_VMAX = 4;        // candidates per thread
-constexpr int THR_ETARGET = 192;   // expected entrants per chunk
+constexpr int THR_ETARGET = 256;   // expected entrants per chunk
 constexpr int THR_BUCKET = 64;     // segment starts: largest bucket ranked by counting
 constexpr int THR_SAMPLE = 4096;   // segment starts: codes read for a sampled threshold
 static_assert(THR_SAMPLE <= THR_KMAX, "a prefix read whole fits the key list");

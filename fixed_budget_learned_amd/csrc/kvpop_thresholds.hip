@@ -128,8 +128,9 @@ __device__ __forceinline__ void bitonic_sort_lds(uint64_t* a, int32_t p2) {
 }
 
 // f(i, code) for every candidate i in [0, n) of sc, coalesced, U loads per
-// thread in flight.  Every thread runs the same number of rounds; f is
-// called for i < n only.
+// thread in flight.  Every thread runs the same number of rounds, so f is
+// also called past the end (i >= n, with the last candidate's code): it
+// must test i < n itself.
 template <int U, typename F>
 __device__ __forceinline__ void stream_scores(const float* __restrict__ sc, int32_t n, F&& f) {
   for (int32_t i0 = threadIdx.x; i0 - static_cast<int32_t>(threadIdx.x) < n;
@@ -340,7 +341,25 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     }
   }
 
+  // the prefix's codes in registers when one round of 16 per thread holds
+  // them (the radix passes and the gather then read no memory), in the
+  // order stream_scores<16> visits them
+  constexpr int RC = 16;
+  const bool in_regs = b <= RC * THR_THREADS;
+  uint32_t rcode[RC];
+  auto codes = [&](auto&& f) {
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < RC; ++u) f(tid + u * THR_THREADS, rcode[u]);
+    } else {
+      stream_scores<RC>(sc, b, f);
+    }
+  };
   if (!sampled) {
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < RC; ++u) rcode[u] = score_code(sc[min(tid + u * THR_THREADS, b - 1)]);
+  }
   // ---- radix select of the k-th largest code: 12-, 12- and 8-bit digits.
   // The wide first digit (sign, exponent, 3 mantissa bits) spreads the codes
   // of real-valued scores over many bins; with 8 bits most fell into a few
@@ -351,7 +370,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
     const int shift = shifts[pass], nb = nbins[pass];
     for (int i = tid; i < nb; i += THR_THREADS) hist[i] = 0u;
     __syncthreads();
-    stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
+    codes([&](int32_t i, uint32_t o) {
       if (i < b && (o & mask) == prefix)
         atomicAdd(&hist[(o >> shift) & static_cast<uint32_t>(nb - 1)], 1u);
     });
@@ -413,7 +432,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_segment_start_kernel(
 
   // ---- gather the k keys that reach the k-th largest key ------------------
   uint32_t cmax = 0;  // this thread's largest kept code
-  stream_scores<16>(sc, b, [&](int32_t i, uint32_t o) {
+  codes([&](int32_t i, uint32_t o) {
     const bool keep = i < b && (o > t || (o == t && i >= pcut));
     const uint64_t m = __ballot(keep);
     if (m != 0ull) {  // wavefront-uniform; most rounds keep nothing

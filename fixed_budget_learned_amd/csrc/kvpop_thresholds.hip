@@ -59,7 +59,8 @@ constexpr int THR_ETARGET = 256;   // expected entrants per chunk
 constexpr int THR_BUCKET = 64;     // segment starts: largest bucket ranked by counting
 constexpr int THR_SAMPLE = 4096;   // segment starts: codes read for a sampled threshold
 static_assert(THR_SAMPLE <= THR_KMAX, "a prefix read whole fits the key list");
-constexpr int THR_FCHUNK = 8 * THR_THREADS;   // sampled starts: candidates per filter workgroup
+constexpr int THR_FTHREADS = 512;     // sampled starts: threads per filter workgroup
+constexpr int THR_FCHUNK = 8 * 1024;   // ... and candidates per filter workgroup
 
 // Segment plan of a prompt: candidate ranges [b[j], b[j+1]) for j < S, and
 // for each segment start the rank m of its sampled threshold (0: the start
@@ -227,9 +228,10 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_tau_kernel(
 // per workgroup serialised on the start's counter (2x slower overall), and
 // so do chunks much smaller than 8,192 candidates (131,072 tokens: 70, 74
 // and 93 us per call at 8,192, 4,096 and 2,048; 72 and 79 us at 16,384 and
-// 32,768).
+// 32,768).  512 threads per workgroup: 69.3 us, against 70.4 with 1,024 and
+// 70.7 with 256.
 // Grid (pairs, Hkv): one workgroup per (start, chunk) pair and head.
-__global__ __launch_bounds__(THR_THREADS) void thresholds_filter_kernel(
+__global__ __launch_bounds__(THR_FTHREADS) void thresholds_filter_kernel(
     const float* __restrict__ scores, int32_t P, int32_t s, ThrPlan plan, ThrFilterWork fw,
     ThrMeta* __restrict__ meta, uint64_t* __restrict__ lists) {
   __shared__ uint64_t lk[THR_KMAX];
@@ -246,10 +248,10 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_filter_kernel(
   uint64_t* list = lists + (static_cast<int64_t>(g) * plan.S + j) * THR_KMAX;
   const uint32_t tau = mt->tau;
   const float* __restrict__ sc = scores + static_cast<int64_t>(g) * P + s;
-  constexpr int U = THR_FCHUNK / THR_THREADS;
+  constexpr int U = THR_FCHUNK / THR_FTHREADS;
   float x[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) x[u] = sc[min(lo + u * THR_THREADS + tid, hi - 1)];
+  for (int u = 0; u < U; ++u) x[u] = sc[min(lo + u * THR_FTHREADS + tid, hi - 1)];
   if (tid == 0) {
     s_cnt = 0u;
     s_cmax = 0u;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_filter_kernel(
   uint32_t cmax = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int32_t i = lo + u * THR_THREADS + tid;
+    const int32_t i = lo + u * THR_FTHREADS + tid;
     const uint32_t o = score_code(x[u]);
     const bool keep = i < hi && o >= tau;
     const uint64_t msk = __ballot(keep);
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(THR_THREADS) void thresholds_filter_kernel(
   __syncthreads();
   const uint32_t base = s_base;
   const uint32_t nl = min(n, static_cast<uint32_t>(THR_KMAX));
-  for (uint32_t i = tid; i < nl; i += THR_THREADS)
+  for (uint32_t i = tid; i < nl; i += THR_FTHREADS)
     if (base + i < static_cast<uint32_t>(THR_KMAX)) list[base + i] = lk[i];
 }
 
@@ -849,7 +851,7 @@ hipError_t launch_prefix_thresholds(const Geometry& geo, int32_t n_tokens, const
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(thresholds_filter_kernel,
                          dim3(static_cast<uint32_t>(fw.n), static_cast<uint32_t>(geo.n_kv_heads)),
-                         dim3(THR_THREADS), 0, stream, scores, n_tokens, geo.n_sink, plan, fw, meta,
+                         dim3(THR_FTHREADS), 0, stream, scores, n_tokens, geo.n_sink, plan, fw, meta,
                          lists);
       e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -346,30 +346,42 @@ __device__ __forceinline__ void write_slot_update(const DecodeParams& p, int hea
   }
 }
 
-// The control block after the step.  Thread 0 writes every field but
-// minslot; minslot is written by the thread that holds the least important
-// key (-1 by thread 0 when no scored token is held).
-__device__ __forceinline__ void write_ctl(const DecodeParams& p, int head, const Decision& dc,
-                                          uint64_t minkey, int32_t leave_next, bool zero_thread,
-                                          bool holds_min, int32_t minslot) {
-  HeadCtl* c = p.ctl + head;
-  if (zero_thread) {
-    c->n = dc.n;
-    c->count = dc.count_new;
-    c->nscored = dc.nscored_new;
-    c->minkey = minkey;
-    c->flags = dc.flags;
-    c->leave_slot = leave_next;
-    if (minkey == KEY_NONE) c->minslot = -1;
-  }
-  if (holds_min && minkey != KEY_NONE) c->minslot = minslot;
-}
+// The fields of the control block that the step's decision fixes (all but
+// the least important key and its slot, which need every split's minimum).
+struct CtlUpdate {
+  int32_t n, count, nscored, flags, leave_slot;
+};
 
 // Slot of the next token to leave the window, for the new control block.
 __device__ __forceinline__ int32_t next_leave_slot(const Decision& dc, int32_t ring_next,
                                                    int32_t n_sink, int32_t W) {
   // with a one-token window the next leaving token is the one just added
   return (dc.n + 1 - W < n_sink) ? -1 : (W == 1 ? dc.newslot : ring_next);
+}
+
+__device__ __forceinline__ CtlUpdate make_update(const Decision& dc, int32_t ring_next,
+                                                 int32_t n_sink, int32_t W) {
+  return CtlUpdate{dc.n, dc.count_new, dc.nscored_new, dc.flags,
+                   next_leave_slot(dc, ring_next, n_sink, W)};
+}
+
+// The control block after the step.  Thread 0 writes every field but
+// minslot; minslot is written by the thread that holds the least important
+// key (-1 by thread 0 when no scored token is held).
+__device__ __forceinline__ void write_ctl(const DecodeParams& p, int head, const CtlUpdate& u,
+                                          uint64_t minkey, bool zero_thread, bool holds_min,
+                                          int32_t minslot) {
+  HeadCtl* c = p.ctl + head;
+  if (zero_thread) {
+    c->n = u.n;
+    c->count = u.count;
+    c->nscored = u.nscored;
+    c->minkey = minkey;
+    c->flags = u.flags;
+    c->leave_slot = u.leave_slot;
+    if (minkey == KEY_NONE) c->minslot = -1;
+  }
+  if (holds_min && minkey != KEY_NONE) c->minslot = minslot;
 }
 
 // Window ring entry of the token that leaves at the next step (read by the
@@ -396,10 +408,12 @@ struct FinishLds {
 // before the first wait; loads past the last split fall outside the buffer
 // descriptors' ranges and read 0, so no load needs a branch.  The splits'
 // (max, sum) pairs are turned into per-split factors by one wavefront per
-// query head.
-template <int D, int G, bool COHERENT>
-__device__ __forceinline__ void finish_head(const DecodeParams& p, int head, const Decision& dc,
-                                            int32_t ring_next, FinishLds& fl) {
+// query head.  get_update() yields the step's control-block fields; it is
+// called only after every load has been issued, so a merge that reads them
+// from memory waits for them together with the partials.
+template <int D, int G, bool COHERENT, class GetUpdate>
+__device__ __forceinline__ void finish_head(const DecodeParams& p, int head,
+                                            GetUpdate get_update, FinishLds& fl) {
   constexpr int NT = 256;
   constexpr int NWAVE = NT / WAVE;
   constexpr int GD = G * D;
@@ -414,7 +428,6 @@ __device__ __forceinline__ void finish_head(const DecodeParams& p, int head, con
   const int wid = tid / WAVE;
   const int ns = p.nsplit;
   const int64_t p0 = static_cast<int64_t>(head) * ns;
-  const int32_t W = p.n_recent;
 
   const __amdgpu_buffer_rsrc_t r_acc = __builtin_amdgcn_make_buffer_rsrc(
       p.part_acc + p0 * GD, 0, ns * GD * 4, BUF_RSRC_WORD3);
@@ -527,8 +540,7 @@ __device__ __forceinline__ void finish_head(const DecodeParams& p, int head, con
     }
   }
   const uint64_t minkey = min_u64(min_u64(fl.wmin[0], fl.wmin[1]), min_u64(fl.wmin[2], fl.wmin[3]));
-  write_ctl(p, head, dc, minkey, next_leave_slot(dc, ring_next, p.n_sink, W), tid == 0,
-            mkey == minkey, static_cast<int32_t>(sraw));
+  write_ctl(p, head, get_update(), minkey, tid == 0, mkey == minkey, static_cast<int32_t>(sraw));
   if (tid == 0) p.tickets[static_cast<int64_t>(head) * TICKET_STRIDE] = 0u;
 #ifdef KVPOP_TIMELINE
   __builtin_amdgcn_s_waitcnt(0);
@@ -877,8 +889,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
       }
     }
-    write_ctl(p, head, dc, wg_minkey, next_leave_slot(dc, ring_next, p.n_sink, W), tid == 0,
-              holds_min, msl);
+    write_ctl(p, head, make_update(dc, ring_next, p.n_sink, W), wg_minkey, tid == 0, holds_min,
+              msl);
     return;
   }
 
@@ -915,10 +927,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           0, CP);
     if (holds_min && wg_minkey != KEY_NONE)
       __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(msl), r_min, 8, 0, CP);
-    // the second launch reads the next leaving token's slot here instead of
-    // a ring lookup that would wait for the control block
-    if (APART && split == 0 && tid == 0)
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(ring_next), r_min, 12, 0, 0);
+    // the second launch takes the step's control-block fields from here, so
+    // its loads need neither the control block nor a decision of their own
+    if (APART && split == 0 && tid == 0) {
+      const CtlUpdate u = make_update(dc, ring_next, p.n_sink, W);
+      const __amdgpu_buffer_rsrc_t r_u = __builtin_amdgcn_make_buffer_rsrc(
+          p.tickets + static_cast<int64_t>(head) * TICKET_STRIDE + UPDATE_WORD, 0, 32,
+          BUF_RSRC_WORD3);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4_t{static_cast<uint32_t>(u.n), static_cast<uint32_t>(u.count),
+                  static_cast<uint32_t>(u.nscored), static_cast<uint32_t>(u.flags)},
+          r_u, 0, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(u.leave_slot), r_u, 16, 0, 0);
+    }
   }
   TL_STAMP(3);  // partial state stored (issued)
   if (APART) return;
@@ -938,22 +959,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   __syncthreads();
   TL_STAMP(5);  // ticket returned
   if (!s_last) return;
-  finish_head<D, G, true>(p, head, dc, ring_next, s_fin);
+  finish_head<D, G, true>(p, head, [&] { return make_update(dc, ring_next, p.n_sink, W); },
+                          s_fin);
 }
 
 // Second launch of a step with several splits: one workgroup per KV head
 // merges the splits' partial results into the output and writes the control
 // block.  The launch boundary orders it after every access of the first
-// launch, so no ticket is needed.
+// launch, so no ticket is needed.  The control-block fields come from split
+// 0's record in the head's ticket block; they are loaded with the partials,
+// so the merge waits for one round of loads.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   __shared__ __align__(16) FinishLds s_fin;
   const int head = blockIdx.x;
-  const HeadCtl c = p.ctl[head];
-  const float sg = p.score_leaving[head];
-  const int32_t ring_next = p.part_min[static_cast<int64_t>(head) * p.nsplit].pad;
-  const Decision dc = decide(c, sg, p.n_sink, p.n_scored, p.n_recent);
-  finish_head<D, G, false>(p, head, dc, ring_next, s_fin);
+  const __amdgpu_buffer_rsrc_t r_u = __builtin_amdgcn_make_buffer_rsrc(
+      p.tickets + static_cast<int64_t>(head) * TICKET_STRIDE + UPDATE_WORD, 0, 32,
+      BUF_RSRC_WORD3);
+  const u32x4_t u4 = __builtin_amdgcn_raw_buffer_load_b128(r_u, 0, 0, 0);
+  const uint32_t u5 = __builtin_amdgcn_raw_buffer_load_b32(r_u, 16, 0, 0);
+  finish_head<D, G, false>(
+      p, head,
+      [&] {
+        return CtlUpdate{static_cast<int32_t>(__builtin_amdgcn_readfirstlane(u4.x)),
+                         static_cast<int32_t>(__builtin_amdgcn_readfirstlane(u4.y)),
+                         static_cast<int32_t>(__builtin_amdgcn_readfirstlane(u4.z)),
+                         static_cast<int32_t>(__builtin_amdgcn_readfirstlane(u4.w)),
+                         static_cast<int32_t>(__builtin_amdgcn_readfirstlane(u5))};
+      },
+      s_fin);
 }
 
 template <int D, int G>

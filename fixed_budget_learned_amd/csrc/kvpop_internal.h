@@ -28,9 +28,8 @@ struct HeadCtl {
 };
 static_assert(sizeof(HeadCtl) == 32, "HeadCtl layout");
 
-// Partial minimum of one split of a head's slot range.  pad: in split 0's
-// record, the slot of the next token to leave the window (for a
-// second-launch merge).
+// Partial minimum of one split of a head's slot range (pad: unused, keeps
+// the record at 16 bytes).
 struct MinPart {
   uint64_t key;
   int32_t slot;
@@ -61,14 +60,19 @@ struct Geometry {
 
 // Each head's split ticket sits alone in a 256-byte block: atomics on one
 // cache line serialise in L2, so heads sharing a line would queue together.
+// Words UPDATE_WORD .. UPDATE_WORD + 4 of the block carry, from split 0 to a
+// second-launch merge, the control-block fields the step's decision fixes
+// (n, count, nscored, flags, leave_slot).
 constexpr int TICKET_STRIDE = 64;
+constexpr int UPDATE_WORD = 8;
 
 // Decode workspace, shared by every layer (calls are stream-ordered).
 struct DecodeWork {
   float* part_acc;     // [heads][nsplit][G*D] unnormalised accumulators
   float* part_ml;      // [heads][nsplit][G][2]  (running max in log2 units, sum)
   MinPart* part_min;   // [heads][nsplit]  least important key of the split and its slot
-  uint32_t* tickets;   // [B*Hkv][TICKET_STRIDE], element 0 used; zero between calls
+  uint32_t* tickets;   // [B*Hkv][TICKET_STRIDE]: element 0 the ticket, zero between calls;
+                       // elements UPDATE_WORD.. split 0's control-block fields
   int32_t nsplit;
   int32_t rows_per_split;
   int32_t threads;     // workgroup size of the decode kernel (256)

@@ -281,35 +281,28 @@ struct Decision {
   uint64_t keyt;        // its key
 };
 
+// Written with selects rather than branches: the leaving token's score is
+// then needed on every path, so its load is issued beside the control
+// block's instead of after it (a branch would take it into the scoring case
+// and make two dependent round trips of the two loads).
 __device__ __forceinline__ Decision decide(const HeadCtl& c, float sg, int32_t n_sink,
                                            int32_t n_scored, int32_t W) {
   Decision d;
   d.n = c.n + 1;
   const int32_t t = d.n - W;
-  d.newslot = c.count;
-  d.count_new = c.count;
-  d.nscored_new = c.nscored;
-  d.st = -1;
-  d.admitted = false;
-  d.keyt = KEY_NONE;
-  d.flags = c.flags;
-  if (t < n_sink) {
-    d.count_new = c.count + 1;                   // sink, or window still filling
-  } else {
-    d.st = c.leave_slot;
-    if (score_is_nan(sg)) d.flags |= 1;
-    d.keyt = make_key(score_code(sg), t);
-    if (c.nscored < n_scored) {                  // free scored slot
-      d.admitted = true;
-      d.count_new = c.count + 1;
-      d.nscored_new = c.nscored + 1;
-    } else if (d.keyt > c.minkey) {              // replaces the least important
-      d.admitted = true;
-      d.newslot = c.minslot;
-    } else {                                     // dropped for good
-      d.newslot = d.st;
-    }
-  }
+  const bool scoring = t >= n_sink;              // else: sink, or window still filling
+  const uint64_t key = make_key(score_code(sg), t);
+  const bool free_slot = c.nscored < n_scored;   // a scored slot is free
+  const bool replace = !free_slot && key > c.minkey;  // replaces the least important
+  d.st = scoring ? c.leave_slot : -1;
+  d.flags = c.flags | ((scoring && score_is_nan(sg)) ? 1 : 0);
+  d.keyt = scoring ? key : KEY_NONE;
+  d.admitted = scoring && (free_slot || replace);
+  d.count_new = c.count + ((!scoring || free_slot) ? 1 : 0);
+  d.nscored_new = c.nscored + ((scoring && free_slot) ? 1 : 0);
+  // the new token takes the next free slot, the evicted token's slot, or
+  // (dropped for good) the leaving token's own slot
+  d.newslot = (!scoring || free_slot) ? c.count : (replace ? c.minslot : c.leave_slot);
   return d;
 }
 
